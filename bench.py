@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD chunk scan on one MI355X.
+
+One step = one ssd_chunk_scan_fwd call over the Mamba-2 2.7B-layer workload
+(B=4, L=4096, H=80, P=64, N=128, G=1, chunk 256, bf16 x/Bm/Cm/y, fp32 dt/A/D
+and states, random initial state).  Inputs are resident in HBM before the
+timed region; three input/output sets are rotated so that no step finds the
+previous step's data in the 256 MB Infinity Cache.  The decode step
+(ssd_step, B=256, H=80, P=64, N=128) is timed the same way and reported in
+its own object.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
+
+
+def scan_algorithmic(w):
+    """Bytes every input read once + outputs written once; flops of the block
+    decomposition (causal halves of the quadratic terms)."""
+    B, L, H, P, N, G, Q = w.B, w.L, w.H, w.P, w.N, w.G, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    nc = -(-L // Q)
+    byts = (2 * B * L * H * P * e          # x in, y out
+            + B * L * H * 4                # dt
+            + 2 * B * L * G * N * e        # Bm, Cm
+            + 2 * H * 4                    # A, D
+            + (B * H * P * N * 4 if w.init else 0)   # initial state
+            + B * H * P * N * 4)           # final state
+    tri = Q * (Q + 1) // 2
+    flops = (2 * B * nc * G * tri * N      # Cm Bm^T, causal
+             + 2 * B * nc * H * tri * P    # masked product with x
+             + 2 * B * L * H * P * N       # block states
+             + 2 * B * L * H * P * N       # state -> output
+             + 2 * B * nc * H * P * N      # state pass
+             + 2 * B * L * H * P)          # D skip
+    return byts, flops
+
+
+def step_algorithmic(B, H, P, N, G, e=2):
+    byts = (2 * B * H * P * N * 4          # state read + write
+            + 2 * B * H * P * e            # x in, y out
+            + B * H * 4                    # dt
+            + 2 * B * G * N * e            # Bm, Cm
+            + 2 * H * 4)
+    return byts
+
+
+def make_device_sets(w, nsets, device):
+    import torch
+    import ssd_inputs as si
+    sets = []
+    for k in range(nsets):
+        d = si.make_scan_inputs(w.B, w.L, w.H, w.P, w.N, w.G, dtype=w.dtype, init=w.init,
+                                seed=w.seed + 100 * k)
+        td = {}
+        for name, v in d.items():
+            if v is None:
+                td[name] = None
+            elif name in ("x", "Bm", "Cm"):
+                td[name] = torch.from_numpy(v).to(device=device, dtype=torch.bfloat16)
+            else:
+                td[name] = torch.from_numpy(v).to(device=device, dtype=torch.float32)
+        td["y"] = torch.empty_like(td["x"])
+        td["final"] = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device=device)
+        sets.append(td)
+    return sets
+
+
+def time_scan(w, steps, warmup, device):
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    sets = make_device_sets(w, 3, device)
+    nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, torch.bfloat16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+    def run(k):
+        s = sets[k % len(sets)]
+        ssd.ssd_chunk_scan_fwd(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], s["D"], s["init"], w.chunk,
+                               y=s["y"], final_state=s["final"], workspace_tensor=ws)
+
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize(device)
+    # per-launch events on the stream the library launches on (the current stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize(device)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        starts[k].record()
+        run(k)
+        ends[k].record()
+    torch.cuda.synchronize(device)
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms
+    ssd.ssd_chunk_scan_workspace_check(ws, w.B, w.L, w.H, w.P, w.G, w.N, w.chunk)
+    return wall, per
+
+
+def time_step(B, H, P, N, G, steps, warmup, device):
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    import ssd_inputs as si
+    st = torch.from_numpy(si.make_step_state(B, H, P, N, seed=si.SEED_BASE + 4)).to(device)
+    ins = []
+    for t in range(4):
+        s = si.make_step_inputs(B, H, P, N, G, step=t, dtype="bf16", seed=si.SEED_BASE + 4)
+        ins.append({k: torch.from_numpy(v).to(device, dtype=torch.bfloat16 if k in ("x", "Bm", "Cm")
+                                               else torch.float32) for k, v in s.items()})
+    ys = [torch.empty_like(i["x"]) for i in ins]
+    for k in range(warmup):
+        i = ins[k % 4]
+        ssd.ssd_step(st, i["x"], i["dt"], i["A"], i["Bm"], i["Cm"], i["D"], y=ys[k % 4])
+    torch.cuda.synchronize(device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        i = ins[k % 4]
+        starts[k].record()
+        ssd.ssd_step(st, i["x"], i["dt"], i["A"], i["Bm"], i["Cm"], i["D"], y=ys[k % 4])
+        ends[k].record()
+    torch.cuda.synchronize(device)
+    return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload: whole
+    sequences of a few (batch, head) pairs, scaled to tokens/s of the full
+    layer (a token is all H heads of one position)."""
+    import numpy as np
+    import oracle
+    import ssd_inputs as si
+    threads = oracle.num_threads()
+    d = si.make_scan_inputs(1, w.L, w.H, w.P, w.N, w.G, dtype=w.dtype, init=w.init, seed=w.seed)
+    f = si.as_f64(d)
+    pairs = max(1, threads)
+    t0 = time.perf_counter()
+    oracle.recurrence(f["x"], f["dt"], f["A"], f["Bm"], f["Cm"], f["D"], f["init"],
+                      bh=list(range(min(pairs, w.H))))
+    probe = time.perf_counter() - t0
+    # grow the sample toward the budget, in whole rounds of `threads` pairs
+    rounds = max(1, min(int(budget_s / max(probe, 1e-3)), max(1, w.H // max(1, pairs))))
+    n = min(w.H, pairs * rounds)
+    t0 = time.perf_counter()
+    oracle.recurrence(f["x"], f["dt"], f["A"], f["Bm"], f["Cm"], f["D"], f["init"], bh=list(range(n)))
+    el = time.perf_counter() - t0
+    token_heads_per_s = n * w.L / el
+    return {"value": token_heads_per_s / w.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 token-by-token recurrence over {n} of the {w.B * w.H} (batch, head) "
+                      f"sequences of L={w.L} ({el:.1f} s); tokens/s = sequences*L/s / H"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the scan has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssd_inputs as si
+    device = torch.device("cuda:0")
+    w = si.WORKLOADS["m2_2p7b"]
+    wall, per = time_scan(w, args.steps, args.warmup, device)
+    ms_step = wall * 1000.0 / args.steps
+    kern_ms = sum(per) / len(per)
+    byts, flops = scan_algorithmic(w)
+    achieved = byts / (kern_ms * 1e-3) / 1e9
+    tokens = w.B * w.L
+    out = {
+        "metric": "SSD chunk-scan fwd tokens/s at Mamba-2 2.7B layer shape; % of roofline",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mamba2_2.7b_layer_ssd_chunk_scan", "batch": w.B, "seq_len": w.L,
+                   "heads": w.H, "head_dim": w.P, "state": w.N, "groups": w.G, "chunk": w.chunk,
+                   "init_state": True, "parallelism": "single_gpu"},
+        "kernel_ms": {"mean": kern_ms, "median": per[len(per) // 2], "p10": per[len(per) // 10],
+                      "p90": per[(9 * len(per)) // 10]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": byts, "algorithmic_flops": flops,
+                     "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_decode:
+        B, H, P, N, G = 256, 80, 64, 128, 1
+        sp = time_step(B, H, P, N, G, max(20, args.steps // 2), 5, device)
+        smean = sum(sp) / len(sp)
+        sb = step_algorithmic(B, H, P, N, G)
+        out["decode"] = {"workload": "mamba2_2.7b_layer_ssd_step", "batch": B, "heads": H,
+                         "head_dim": P, "state": N, "us_per_step": smean * 1000.0,
+                         "tokens_per_s": B / (smean * 1e-3),
+                         "roofline": {"bound": "hbm", "achieved": sb / (smean * 1e-3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "algorithmic_bytes": sb}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * libssd -- the Mamba-2 SSD (structured state space duality) scan on AMD
+ * Instinct MI355X (gfx950), behind a plain C ABI.
+ *
+ * The operation.  For every batch b and head h (group g = h / (H / G)), with a
+ * state S of P x N numbers per (b, h), starting from init_state (zero when
+ * absent):
+ *
+ *   alpha_t = exp(dt[b,t,h] * A[h])
+ *   S      <- alpha_t * S + dt[b,t,h] * x[b,t,h,:] (outer) Bm[b,t,g,:]
+ *   y[b,t,h,p] = sum_n S[p,n] * Cm[b,t,g,n] + D[h] * x[b,t,h,p]
+ *
+ * and final_state is S after the last token.  This is the selective SSM
+ * recurrence h_t = A_t h_{t-1} + B_t x_t, y_t = C_t^T h_t with a scalar decay
+ * A_t = a_t I (the "Mamba-2" note, sections "writing the SSM as a matrix" and
+ * "reducing A to a number"), the decay discretised as exp(dt A) ("Mamba"
+ * reading notes, section 2.2) and the input term as dt B, with multi-head
+ * inputs sharing B and C within a group ("Mamba-2" note, section "Mamba-2
+ * block", item 2) and a D skip connection.
+ *
+ * ssd_chunk_scan_fwd evaluates it in blocks of chunk_size tokens, the
+ * two-way split of the "Mamba-2" note (section "taking each path half way")
+ * and of the "Mamba-2 model walkthrough" (sections 6.1-6.2): a quadratic,
+ * attention-like product inside each block, (Cm Bm^T masked by the segment-sum
+ * decay) times dt x, plus states passed from block to block.  The result does
+ * not depend on chunk_size except through rounding.  ssd_step applies the
+ * recurrence to one token.
+ *
+ * Conventions shared by every call:
+ *
+ *  - Memory.  Every tensor argument is a DEVICE pointer to dense, row-major
+ *    memory in the shape stated, owned by the caller.  The library allocates
+ *    nothing and keeps no state between calls.  Every pointer must be 16-byte
+ *    aligned, else SSD_ERR_INVALID_ARG.
+ *  - Types.  dt, A, D and all states are float32.  x, Bm, Cm and y are
+ *    float32 (SSD_DTYPE_F32) or bfloat16 (SSD_DTYPE_BF16).  Arithmetic
+ *    accumulates in float32; products inside a block may use bfloat16 operands
+ *    in SSD_DTYPE_BF16 mode.
+ *  - Execution.  Calls validate their arguments on the host, enqueue kernels
+ *    on `stream` (0 = the null stream) and return without waiting.  Argument
+ *    errors are returned before anything is enqueued.  A launch error is
+ *    returned as SSD_ERR_HIP.  No exception crosses the ABI.
+ *  - Values.  Inputs are not inspected.  The method assumes A <= 0 and dt >= 0
+ *    (the decay lies in [0, 1]); other values are computed as written and may
+ *    overflow.
+ *  - Support.  P in {16, 32, 64, 128}; N in {16, 32, 64, 128, 256};
+ *    chunk_size in {64, 128, 256}; H % G == 0; B, L >= 0 (L need not be a
+ *    multiple of chunk_size).  Other shapes return SSD_ERR_UNSUPPORTED.
+ */
+#ifndef LIBSSD_H
+#define LIBSSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, H % G != 0 */
+    SSD_ERR_UNSUPPORTED = 2,   /* shape, chunk size, dtype or algorithm not supported */
+    SSD_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+    SSD_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} ssd_status;
+
+typedef enum {
+    SSD_DTYPE_F32 = 0,
+    SSD_DTYPE_BF16 = 1
+} ssd_dtype;
+
+/* Which kernel sequence evaluates the chunk scan.  All give the same result
+ * up to rounding.  SSD_ALGO_AUTO picks by shape and dtype. */
+typedef enum {
+    SSD_ALGO_AUTO = 0,
+    SSD_ALGO_REFERENCE = 1,   /* float32 vector arithmetic, three kernels, every supported shape */
+    SSD_ALGO_STAGED = 2,      /* bf16 matrix cores: block states, state pass, block outputs */
+    SSD_ALGO_FUSED = 3        /* bf16 matrix cores, one pass: states handed from block to block */
+} ssd_algo;
+
+/* Human-readable name of a status code (static storage). */
+const char *ssd_status_string(ssd_status status);
+
+/* Library version string (static storage). */
+const char *ssd_version(void);
+
+/*
+ * Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (with
+ * SSD_ALGO_AUTO; every algorithm fits in it).  Returns 0 when the shape is
+ * not supported.  The workspace holds per-block states (scratch) and the
+ * hand-off flags and counters of SSD_ALGO_FUSED.  It must be ZERO-FILLED once
+ * before its first use; every call leaves the flags and counters at zero when
+ * its kernels finish, so one workspace serves any sequence of calls.  Calls
+ * sharing a workspace must be ordered on one stream (they would race
+ * otherwise).
+ */
+size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                     int64_t N, int64_t chunk_size, ssd_dtype dtype);
+
+/*
+ * Chunked SSD scan, forward.
+ *
+ *   x            [B, L, H, P]   dtype        inputs
+ *   dt           [B, L, H]      float32      step sizes (>= 0)
+ *   A            [H]            float32      per-head decay rate (<= 0)
+ *   Bm           [B, L, G, N]   dtype        input projections ("B")
+ *   Cm           [B, L, G, N]   dtype        output projections ("C")
+ *   D            [H]            float32      skip weights
+ *   init_state   [B, H, P, N]   float32      state before token 0, or NULL for zeros
+ *   y            [B, L, H, P]   dtype        output (written); must not alias an input
+ *   final_state  [B, H, P, N]   float32      state after token L-1, or NULL to skip;
+ *                                            may alias init_state
+ *   workspace    device memory of at least ssd_chunk_scan_workspace_size(...) bytes
+ *
+ * Errors: SSD_ERR_INVALID_ARG for a null required pointer, a misaligned
+ * pointer or a negative size; SSD_ERR_UNSUPPORTED outside the support matrix;
+ * SSD_ERR_WORKSPACE when the workspace is NULL or too small; SSD_ERR_HIP when a
+ * launch fails.  L == 0 or B == 0 copies init_state (or zeros) to final_state.
+ */
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
+                              const void *Bm, const void *Cm, const float *D,
+                              const float *init_state, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes,
+                              int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                              int64_t chunk_size, ssd_dtype dtype, hipStream_t stream);
+
+/*
+ * As ssd_chunk_scan_fwd, with the kernel sequence chosen by the caller.  An
+ * algorithm that does not cover the shape or dtype returns
+ * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16 and
+ * P == 64).
+ */
+ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A,
+                                   const void *Bm, const void *Cm, const float *D,
+                                   const float *init_state, void *y, float *final_state,
+                                   void *workspace, size_t workspace_bytes,
+                                   int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                   int64_t N, int64_t chunk_size, ssd_dtype dtype,
+                                   ssd_algo algo, hipStream_t stream);
+
+/*
+ * Diagnostic: waits for `stream`, then reports whether a block-to-block
+ * hand-off of SSD_ALGO_FUSED in this workspace ever gave up waiting (a bounded
+ * wait that is never expected to expire; when it does, outputs of that call
+ * are wrong).  Returns SSD_OK when none did, SSD_ERR_HIP when one did or a
+ * HIP call failed; clears the indicator.  Same shape arguments as the scan.
+ */
+ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes,
+                                          int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                          int64_t N, int64_t chunk_size, hipStream_t stream);
+
+/*
+ * One recurrent decode step: the update above for a single token, in place.
+ *
+ *   state  [B, H, P, N]  float32  read and overwritten with the updated state
+ *   x      [B, H, P]     dtype
+ *   dt     [B, H]        float32
+ *   A      [H]           float32
+ *   Bm     [B, G, N]     dtype
+ *   Cm     [B, G, N]     dtype
+ *   D      [H]           float32
+ *   y      [B, H, P]     dtype    y = Cm . (updated state) + D x
+ *
+ * This is the recurrent path of the "Mamba-2" note (four-token section): it
+ * carries only the fixed-size state from token to token.  Errors as for
+ * ssd_chunk_scan_fwd; B == 0 is a no-op.
+ */
+ssd_status ssd_step(float *state, const void *x, const float *dt, const float *A,
+                    const void *Bm, const void *Cm, const float *D, void *y,
+                    int64_t B, int64_t H, int64_t P, int64_t G, int64_t N,
+                    ssd_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_H */

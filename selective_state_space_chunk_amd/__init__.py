@@ -1,0 +1,212 @@
+"""libssd -- the Mamba-2 SSD chunk scan and decode step on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/libssd.h``.  It only
+marshals arguments: every step of the scan runs in the HIP kernels of
+``libssd.so``.  PyTorch supplies device memory and the current stream.  There
+is no fallback: if the library is not built, importing the binding's entry
+points raises.
+
+Entry points (same names as the C ABI):
+
+* ``ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, D, init_state=None, chunk_size=256)``
+  -> ``(y, final_state)``
+* ``ssd_step(state, x, dt, A, Bm, Cm, D)`` -> ``y`` (``state`` updated in place)
+* ``ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libssd.so")
+
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
+ALGOS = {"auto": 0, "reference": 1, "staged": 2, "fused": 3}
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    """A libssd call returned a status other than SSD_OK."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssd.so (built in-tree by ``build.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libssd.so not found at {LIB_PATH}; build it first with "
+            "`python -m selective_state_space_chunk_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    lib.ssd_version.restype = ctypes.c_char_p
+    lib.ssd_chunk_scan_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_workspace_size.restype = sz
+    scan_args = [vp] * 10 + [sz] + [i64] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_fwd.argtypes = scan_args + [vp]
+    lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_algo.argtypes = scan_args + [ctypes.c_int, vp]
+    lib.ssd_chunk_scan_fwd_algo.restype = ctypes.c_int
+    lib.ssd_chunk_scan_workspace_check.argtypes = [vp, sz] + [i64] * 7 + [vp]
+    lib.ssd_chunk_scan_workspace_check.restype = ctypes.c_int
+    lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
+    lib.ssd_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != SSD_OK:
+        raise SSDError(status, f"{what}: {status_string(status)}")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SSD_DTYPE_F32
+    if t == torch.bfloat16:
+        return SSD_DTYPE_BF16
+    raise TypeError(f"x, Bm, Cm must be float32 or bfloat16, got {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device, stream=None):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def ssd_chunk_scan_workspace_size(B: int, L: int, H: int, P: int, G: int, N: int,
+                                  chunk_size: int, dtype: torch.dtype) -> int:
+    return int(load_library().ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size,
+                                                            _dtype_code(dtype)))
+
+
+_workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zero-filled device workspace of at least ``nbytes``, cached per device
+    (calls leave its flags zeroed, so it is reused across calls on one stream)."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), 0)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, D: torch.Tensor, init_state: Optional[torch.Tensor] = None,
+                       chunk_size: int = 256, *, y: Optional[torch.Tensor] = None,
+                       final_state: Optional[torch.Tensor] = None, return_final: bool = True,
+                       workspace_tensor: Optional[torch.Tensor] = None, algo: str = "auto",
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked SSD scan.  Shapes: x [B,L,H,P], dt [B,L,H] f32, A [H] f32,
+    Bm/Cm [B,L,G,N], D [H] f32, init_state [B,H,P,N] f32 or None.
+    Returns (y [B,L,H,P], final_state [B,H,P,N] f32 or None)."""
+    lib = load_library()
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    _need(x, "x", x.dtype, (Bsz, L, H, P), dev)
+    _need(dt, "dt", torch.float32, (Bsz, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(Bm, "Bm", x.dtype, (Bsz, L, G, N), dev)
+    _need(Cm, "Cm", x.dtype, (Bsz, L, G, N), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (Bsz, H, P, N), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, (Bsz, L, H, P), dev)
+    if final_state is None and return_final:
+        final_state = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (Bsz, H, P, N), dev)
+    code = _dtype_code(x.dtype)
+    need = int(lib.ssd_chunk_scan_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
+    if workspace_tensor is None:
+        workspace_tensor = workspace(need, dev) if need > 0 else None
+    ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}")
+    st = lib.ssd_chunk_scan_fwd_algo(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y),
+        _ptr(final_state), _ptr(workspace_tensor), ws_bytes, Bsz, L, H, P, G, N, chunk_size, code,
+        ALGOS[algo], _stream_handle(dev, stream))
+    _check(st, "ssd_chunk_scan_fwd")
+    return y, final_state
+
+
+def ssd_chunk_scan_workspace_check(workspace_tensor: torch.Tensor, B: int, L: int, H: int, P: int,
+                                   G: int, N: int, chunk_size: int, stream=None) -> None:
+    """Raise if a block-to-block hand-off in this workspace ever gave up waiting."""
+    lib = load_library()
+    nbytes = workspace_tensor.numel() * workspace_tensor.element_size()
+    st = lib.ssd_chunk_scan_workspace_check(_ptr(workspace_tensor), nbytes, B, L, H, P, G, N,
+                                            chunk_size, _stream_handle(workspace_tensor.device, stream))
+    _check(st, "ssd_chunk_scan_workspace_check")
+
+
+def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+             Bm: torch.Tensor, Cm: torch.Tensor, D: torch.Tensor, *,
+             y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode token.  state [B,H,P,N] f32 (updated in place), x [B,H,P],
+    dt [B,H] f32, A [H] f32, Bm/Cm [B,G,N], D [H] f32.  Returns y [B,H,P]."""
+    lib = load_library()
+    Bsz, H, P, N = state.shape
+    G = Bm.shape[1]
+    dev = state.device
+    _need(state, "state", torch.float32, (Bsz, H, P, N), dev)
+    _need(x, "x", x.dtype, (Bsz, H, P), dev)
+    _need(dt, "dt", torch.float32, (Bsz, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(Bm, "Bm", x.dtype, (Bsz, G, N), dev)
+    _need(Cm, "Cm", x.dtype, (Bsz, G, N), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, (Bsz, H, P), dev)
+    st = lib.ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(y),
+                      Bsz, H, P, G, N, _dtype_code(x.dtype), _stream_handle(dev, stream))
+    _check(st, "ssd_step")
+    return y
+
+
+def version() -> str:
+    return load_library().ssd_version().decode()

@@ -1,0 +1,225 @@
+// C ABI of libssd: argument validation, workspace carve-up and dispatch.
+// Declarations and the contract of every entry point are in include/libssd.h.
+#include "libssd.h"
+#include "common.h"
+
+#include <hip/hip_runtime.h>
+
+namespace ssd {
+hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws);
+hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws);
+bool mfma_supported(int64_t P, int64_t N, int64_t Q);
+size_t fused_max_chains();
+}
+
+namespace {
+
+using namespace ssd;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool shape_supported(int64_t P, int64_t N, int64_t Q) {
+    return pow2_in(P, 16, 128) && pow2_in(N, 16, 256) && pow2_in(Q, 64, 256);
+}
+
+struct Layout {
+    size_t states, decay, flags, counters, ring, total;
+};
+
+// Byte offsets of each workspace region.  Sizes are in elements of 4 bytes.
+Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q) {
+    Layout l{};
+    const int64_t nc = (L + Q - 1) / Q;
+    size_t off = 0;
+    l.states = off;   off = align_up(off + (size_t)(B * nc * H * P * N) * sizeof(float));
+    l.decay = off;    off = align_up(off + (size_t)(B * H * nc) * sizeof(float));
+    l.flags = off;    off = align_up(off + (size_t)(B * H) * sizeof(unsigned));
+    l.counters = off; off = align_up(off + 4 * sizeof(unsigned));
+    l.ring = off;     off = align_up(off + (size_t)(B * H * 2 * P * N) * sizeof(float));
+    l.total = off;
+    return l;
+}
+
+Workspace carve(void *base, const Layout &l) {
+    char *p = (char *)base;
+    Workspace w;
+    w.states = (float *)(p + l.states);
+    w.decay = (float *)(p + l.decay);
+    w.flags = (unsigned *)(p + l.flags);
+    w.counters = (unsigned *)(p + l.counters);
+    w.ring = (float *)(p + l.ring);
+    return w;
+}
+
+__global__ void fill_or_copy(float *__restrict__ dst, const float *__restrict__ src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+ssd_status common_checks(const void *x, const float *dt, const float *A, const void *Bm,
+                         const void *Cm, const float *D, const void *y, int64_t B, int64_t L,
+                         int64_t H, int64_t P, int64_t G, int64_t N, ssd_dtype dtype,
+                         bool need_data) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0) return SSD_ERR_INVALID_ARG;
+    if (H % G != 0) return SSD_ERR_INVALID_ARG;
+    if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (need_data) {
+        if (!x || !dt || !A || !Bm || !Cm || !D || !y) return SSD_ERR_INVALID_ARG;
+    }
+    const void *ptrs[] = {x, dt, A, Bm, Cm, D, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_INVALID_ARG;
+    return SSD_OK;
+}
+
+ssd_status scan_impl(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
+                     const float *D, const float *init, void *y, float *final_state,
+                     void *workspace, size_t workspace_bytes, int64_t B, int64_t L, int64_t H,
+                     int64_t P, int64_t G, int64_t N, int64_t Q, ssd_dtype dtype, ssd_algo algo,
+                     hipStream_t stream) {
+    const bool has_work = B > 0 && L > 0;
+    ssd_status st = common_checks(x, dt, A, Bm, Cm, D, y, B, L, H, P, G, N, dtype, has_work);
+    if (st != SSD_OK) return st;
+    if ((init && !aligned16(init)) || (final_state && !aligned16(final_state)))
+        return SSD_ERR_INVALID_ARG;
+    if (Q <= 0) return SSD_ERR_INVALID_ARG;
+    if (!shape_supported(P, N, Q)) return SSD_ERR_UNSUPPORTED;
+    if (B > 65535 || H > 65535 || B * H > 65535) return SSD_ERR_UNSUPPORTED;
+    if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
+        algo != SSD_ALGO_FUSED)
+        return SSD_ERR_UNSUPPORTED;
+    const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
+    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED) && !mfma_ok) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_FUSED && ((size_t)(B * H) > fused_max_chains() ||
+                                   B * H * ((L + Q - 1) / Q) > 0x7fffffff))
+        return SSD_ERR_UNSUPPORTED;
+
+    const Layout l = layout(B, L, H, P, N, Q);
+    if (has_work) {
+        if (!workspace || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
+    }
+
+    if (!has_work) {
+        // nothing to scan: the final state is the initial state (or zeros)
+        if (final_state && B > 0) {
+            const int64_t n = B * H * P * N;
+            if (init != final_state)
+                fill_or_copy<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(final_state, init, n);
+        }
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+
+    ScanArgs a{x, dt, A, Bm, Cm, D, init, y, final_state, B, L, H, P, G, N, Q,
+               dtype == SSD_DTYPE_BF16 ? 1 : 0, stream};
+    const Workspace ws = carve(workspace, l);
+
+    if (algo == SSD_ALGO_AUTO) {
+        if (!mfma_ok) {
+            algo = SSD_ALGO_REFERENCE;
+        } else {
+            const int64_t nc = (L + Q - 1) / Q;
+            // one pass while chains of blocks are short and many; staged otherwise
+            algo = (nc <= 64 && (size_t)(B * H) <= fused_max_chains() && B * H >= 64 &&
+                    B * H * nc <= 0x7fffffff)
+                       ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
+        }
+    }
+    hipError_t e;
+    switch (algo) {
+        case SSD_ALGO_REFERENCE: e = launch_reference_scan(a, ws); break;
+        case SSD_ALGO_STAGED: e = launch_staged_scan(a, ws); break;
+        case SSD_ALGO_FUSED: e = launch_fused_scan(a, ws); break;
+        default: return SSD_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_INVALID_ARG: return "SSD_ERR_INVALID_ARG: invalid argument";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape, chunk size, dtype or algorithm not supported";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime or launch failure";
+    }
+    return "unknown ssd_status";
+}
+
+const char *ssd_version(void) { return "libssd 0.1 (gfx950)"; }
+
+size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                     int64_t N, int64_t chunk_size, ssd_dtype dtype) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0) return 0;
+    if (H % G != 0 || !shape_supported(P, N, chunk_size)) return 0;
+    if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return 0;
+    return layout(B, L, H, P, N, chunk_size).total;
+}
+
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *Bm,
+                              const void *Cm, const float *D, const float *init_state, void *y,
+                              float *final_state, void *workspace, size_t workspace_bytes,
+                              int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                              int64_t chunk_size, ssd_dtype dtype, hipStream_t stream) {
+    return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes,
+                     B, L, H, P, G, N, chunk_size, dtype, SSD_ALGO_AUTO, stream);
+}
+
+ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A, const void *Bm,
+                                   const void *Cm, const float *D, const float *init_state, void *y,
+                                   float *final_state, void *workspace, size_t workspace_bytes,
+                                   int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                                   int64_t chunk_size, ssd_dtype dtype, ssd_algo algo,
+                                   hipStream_t stream) {
+    return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes,
+                     B, L, H, P, G, N, chunk_size, dtype, algo, stream);
+}
+
+ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes, int64_t B,
+                                          int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                                          int64_t chunk_size, hipStream_t stream) {
+    if (!workspace || B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0)
+        return SSD_ERR_INVALID_ARG;
+    const Layout l = layout(B, L, H, P, N, chunk_size);
+    if (workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
+    unsigned *ctr = (unsigned *)((char *)workspace + l.counters);
+    unsigned host[4] = {0, 0, 0, 0};
+    if (hipStreamSynchronize(stream) != hipSuccess) return SSD_ERR_HIP;
+    if (hipMemcpy(host, ctr, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess) return SSD_ERR_HIP;
+    if (host[2] != 0) {
+        const unsigned zero = 0;
+        if (hipMemcpy(ctr + 2, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SSD_ERR_HIP;
+        return SSD_ERR_HIP;
+    }
+    return SSD_OK;
+}
+
+ssd_status ssd_step(float *state, const void *x, const float *dt, const float *A, const void *Bm,
+                    const void *Cm, const float *D, void *y, int64_t B, int64_t H, int64_t P,
+                    int64_t G, int64_t N, ssd_dtype dtype, hipStream_t stream) {
+    ssd_status st = common_checks(x, dt, A, Bm, Cm, D, y, B, 1, H, P, G, N, dtype, B > 0);
+    if (st != SSD_OK) return st;
+    if (B > 0 && !state) return SSD_ERR_INVALID_ARG;
+    if (state && !aligned16(state)) return SSD_ERR_INVALID_ARG;
+    if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 256)) return SSD_ERR_UNSUPPORTED;
+    if (B * H > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (B == 0) return SSD_OK;
+    const hipError_t e = launch_step(state, x, dt, A, Bm, Cm, D, y, B, H, P, G, N,
+                                     dtype == SSD_DTYPE_BF16 ? 1 : 0, stream);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// One recurrent decode step (the recurrent path of the "Mamba-2" note,
+// four-token section): for each (b, h),
+//   alpha = exp(dt A_h);  S <- alpha S + dt x (outer) Bm;  y = S Cm + D x.
+//
+// The state dominates the traffic: P*N float32 read and written once per
+// token, against P + 2N + a few inputs.  The kernel is a coalesced stream over
+// the state: one workgroup per (b, h), each row of N floats read as N/4
+// float4 lanes, all of a thread's rows loaded before any is written so that
+// every load is in flight at once; the row's dot product with Cm is reduced
+// across its lanes with shuffles.  Loads and stores of the state bypass
+// cache allocation (non-temporal): nothing re-reads it within the step.
+#include "common.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kThreads = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <class T, int P, int N>
+__global__ __launch_bounds__(kThreads) void step_kernel(
+    float *__restrict__ state, const T *__restrict__ x, const float *__restrict__ dt,
+    const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
+    const float *__restrict__ D, T *__restrict__ y, int H, int G) {
+    constexpr int LPR = N / 4;                 // lanes per state row (4..64, power of two)
+    constexpr int ROWS = kThreads / LPR;       // rows covered per pass
+    constexpr int ITERS = (P + ROWS - 1) / ROWS;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int g = h / (H / G);
+    const int lane = threadIdx.x & (LPR - 1);
+    const int row0 = threadIdx.x / LPR;
+
+    const float dtv = dt[bh];
+    const float alpha = expf(dtv * A[h]);
+    const float Dh = D[h];
+    float bv[4], cv[4];
+    const T *bp = Bm + ((int64_t)b * G + g) * N + lane * 4;
+    const T *cp = Cm + ((int64_t)b * G + g) * N + lane * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { bv[k] = to_f32(bp[k]); cv[k] = to_f32(cp[k]); }
+
+    f32x4 *sp = reinterpret_cast<f32x4 *>(state + bh * (int64_t)(P * N));
+    f32x4 s[ITERS];
+    float xv[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int p = row0 + it * ROWS;
+        if (p < P) {
+            s[it] = __builtin_nontemporal_load(sp + p * LPR + lane);
+            xv[it] = to_f32(x[bh * P + p]);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int p = row0 + it * ROWS;
+        if (p < P) {
+            const float u = dtv * xv[it];
+            f32x4 v = s[it];
+            v.x = alpha * v.x + u * bv[0];
+            v.y = alpha * v.y + u * bv[1];
+            v.z = alpha * v.z + u * bv[2];
+            v.w = alpha * v.w + u * bv[3];
+            __builtin_nontemporal_store(v, sp + p * LPR + lane);
+            float part = v.x * cv[0] + v.y * cv[1] + v.z * cv[2] + v.w * cv[3];
+#pragma unroll
+            for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+            if (lane == 0) y[bh * P + p] = from_f32<T>(part + Dh * xv[it]);
+        }
+    }
+}
+
+template <class T, int P>
+hipError_t launch_n(float *state, const void *x, const float *dt, const float *A, const void *Bm,
+                    const void *Cm, const float *D, void *y, int64_t B, int64_t H, int64_t G,
+                    int64_t N, hipStream_t stream) {
+    const dim3 grid((unsigned)(B * H));
+#define SSD_STEP_N(NN)                                                                      \
+    case NN:                                                                                \
+        step_kernel<T, P, NN><<<grid, kThreads, 0, stream>>>(                               \
+            state, (const T *)x, dt, A, (const T *)Bm, (const T *)Cm, D, (T *)y, (int)H, (int)G); \
+        break;
+    switch (N) {
+        SSD_STEP_N(16) SSD_STEP_N(32) SSD_STEP_N(64) SSD_STEP_N(128) SSD_STEP_N(256)
+        default: return hipErrorInvalidValue;
+    }
+#undef SSD_STEP_N
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_p(float *state, const void *x, const float *dt, const float *A, const void *Bm,
+                    const void *Cm, const float *D, void *y, int64_t B, int64_t H, int64_t P,
+                    int64_t G, int64_t N, hipStream_t stream) {
+    switch (P) {
+        case 16: return launch_n<T, 16>(state, x, dt, A, Bm, Cm, D, y, B, H, G, N, stream);
+        case 32: return launch_n<T, 32>(state, x, dt, A, Bm, Cm, D, y, B, H, G, N, stream);
+        case 64: return launch_n<T, 64>(state, x, dt, A, Bm, Cm, D, y, B, H, G, N, stream);
+        case 128: return launch_n<T, 128>(state, x, dt, A, Bm, Cm, D, y, B, H, G, N, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_step(float *state, const void *x, const float *dt, const float *A,
+                       const void *Bm, const void *Cm, const float *D, void *y,
+                       int64_t B, int64_t H, int64_t P, int64_t G, int64_t N, int bf16,
+                       hipStream_t stream) {
+    return bf16 ? launch_p<ssd::bf16>(state, x, dt, A, Bm, Cm, D, y, B, H, P, G, N, stream)
+                : launch_p<float>(state, x, dt, A, Bm, Cm, D, y, B, H, P, G, N, stream);
+}
+
+}  // namespace ssd

@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/libssd.h declares, sizes workspaces, and rejects bad arguments before
+anything reaches the GPU.  No call here launches a kernel: every call either
+is a pure host query or returns an error status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import selective_state_space_chunk_amd as ssd
+    if not os.path.exists(ssd.LIB_PATH):
+        from selective_state_space_chunk_amd import build
+        build.build()
+    return ssd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
+              "ssd_status_string", "ssd_chunk_scan_fwd_algo", "ssd_version",
+              "ssd_chunk_scan_workspace_check"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import selective_state_space_chunk_amd as ssd
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings_and_version(lib):
+    import selective_state_space_chunk_amd as ssd
+    for code in range(5):
+        assert ssd.status_string(code).startswith("SSD_")
+    assert "gfx950" in ssd.version()
+
+
+B, L, H, P, G, N, Q = 4, 4096, 80, 64, 1, 128, 256
+
+
+def test_workspace_size(lib):
+    ws = lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 1)
+    nc = L // Q
+    assert ws >= B * nc * H * P * N * 4 + B * H * 2 * P * N * 4
+    # ragged L rounds the block count up
+    assert lib.ssd_chunk_scan_workspace_size(B, L + 1, H, P, G, N, Q, 1) > ws
+    # unsupported shapes report 0
+    for bad in [(B, L, H, 48, G, N, Q), (B, L, H, P, G, 512, Q), (B, L, H, P, G, N, 32),
+                (B, L, H, P, 3, N, Q), (-1, L, H, P, G, N, Q)]:
+        assert lib.ssd_chunk_scan_workspace_size(*bad, 1) == 0
+    assert lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 7) == 0
+
+
+def fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def scan_call(lib, *, x=0x10000, dt=0x20000, A=0x30000, Bm=0x40000, Cm=0x50000, D=0x60000,
+              init=None, y=0x70000, fin=None, ws=0x80000, ws_bytes=None, shape=(B, L, H, P, G, N, Q),
+              dtype=1, algo=0):
+    b, l, h, p, g, n, q = shape
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.ssd_chunk_scan_fwd_algo(fake(x) if x else None, fake(dt) if dt else None,
+                                       fake(A) if A else None, fake(Bm) if Bm else None,
+                                       fake(Cm) if Cm else None, fake(D) if D else None,
+                                       fake(init) if init else None, fake(y) if y else None,
+                                       fake(fin) if fin else None, fake(ws) if ws else None,
+                                       ws_bytes, b, l, h, p, g, n, q, dtype, algo, None)
+
+
+def test_scan_rejects_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+    assert scan_call(lib, x=0) == ssd.SSD_ERR_INVALID_ARG            # null input
+    assert scan_call(lib, y=0) == ssd.SSD_ERR_INVALID_ARG            # null output
+    assert scan_call(lib, Bm=0x40008) == ssd.SSD_ERR_INVALID_ARG     # misaligned
+    assert scan_call(lib, init=0x90004) == ssd.SSD_ERR_INVALID_ARG   # misaligned init
+    assert scan_call(lib, shape=(B, -1, H, P, G, N, Q)) == ssd.SSD_ERR_INVALID_ARG
+    assert scan_call(lib, shape=(B, L, H, P, 3, N, Q)) == ssd.SSD_ERR_INVALID_ARG   # H % G
+    assert scan_call(lib, shape=(B, L, H, P, G, N, 0)) == ssd.SSD_ERR_INVALID_ARG
+    assert scan_call(lib, shape=(B, L, H, 48, G, N, Q)) == ssd.SSD_ERR_UNSUPPORTED
+    assert scan_call(lib, shape=(B, L, H, P, G, 512, Q)) == ssd.SSD_ERR_UNSUPPORTED
+    assert scan_call(lib, shape=(B, L, H, P, G, N, 32)) == ssd.SSD_ERR_UNSUPPORTED
+    assert scan_call(lib, dtype=5) == ssd.SSD_ERR_UNSUPPORTED
+    assert scan_call(lib, algo=9) == ssd.SSD_ERR_UNSUPPORTED
+    # matrix-core algorithms need bf16 and P = 64
+    assert scan_call(lib, dtype=0, algo=3) == ssd.SSD_ERR_UNSUPPORTED
+    assert scan_call(lib, shape=(B, L, H, 32, G, N, Q), algo=2) == ssd.SSD_ERR_UNSUPPORTED
+    # workspace missing or too small
+    assert scan_call(lib, ws=0) == ssd.SSD_ERR_WORKSPACE
+    need = lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 1)
+    assert scan_call(lib, ws_bytes=need - 1) == ssd.SSD_ERR_WORKSPACE
+
+
+def test_step_rejects_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+
+    def call(state=0x1000, x=0x2000, shape=(256, 80, 64, 1, 128), dtype=1):
+        b, h, p, g, n = shape
+        return lib.ssd_step(fake(state) if state else None, fake(x) if x else None, fake(0x3000),
+                            fake(0x4000), fake(0x5000), fake(0x6000), fake(0x7000), fake(0x8000),
+                            b, h, p, g, n, dtype, None)
+    assert call(state=0) == ssd.SSD_ERR_INVALID_ARG
+    assert call(x=0) == ssd.SSD_ERR_INVALID_ARG
+    assert call(state=0x1004) == ssd.SSD_ERR_INVALID_ARG
+    assert call(shape=(256, 80, 64, 3, 128)) == ssd.SSD_ERR_INVALID_ARG
+    assert call(shape=(256, 80, 64, 1, 512)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(shape=(256, 80, 48, 1, 128)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(dtype=3) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(shape=(0, 80, 64, 1, 128)) == ssd.SSD_OK                 # empty batch: no-op
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch):
+    import selective_state_space_chunk_amd as ssd
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        ssd.load_library()
