@@ -45,7 +45,8 @@
  *    overflow.
  *  - Support.  P in {16, 32, 64, 128}; N in {16, 32, 64, 128, 256};
  *    chunk_size in {64, 128, 256}; H % G == 0; B, L >= 0 (L need not be a
- *    multiple of chunk_size).  Other shapes return SSD_ERR_UNSUPPORTED.
+ *    multiple of chunk_size); B * H <= 65535 for the chunk scan.  Other shapes
+ *    return SSD_ERR_UNSUPPORTED.
  */
 #ifndef LIBSSD_H
 #define LIBSSD_H
@@ -129,8 +130,8 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
 /*
  * As ssd_chunk_scan_fwd, with the kernel sequence chosen by the caller.  An
  * algorithm that does not cover the shape or dtype returns
- * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16 and
- * P == 64).
+ * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16,
+ * P == 64 and N in {64, 128, 256}).
  */
 ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A,
                                    const void *Bm, const void *Cm, const float *D,

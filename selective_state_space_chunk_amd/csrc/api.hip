@@ -10,6 +10,7 @@ hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws);
 hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws);
 bool mfma_supported(int64_t P, int64_t N, int64_t Q);
 size_t fused_max_chains();
+size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
 }
 
 namespace {
@@ -31,19 +32,25 @@ bool shape_supported(int64_t P, int64_t N, int64_t Q) {
 }
 
 struct Layout {
-    size_t states, decay, flags, counters, ring, total;
+    size_t states, decay, flags, counters, ring, gram, total;
 };
 
-// Byte offsets of each workspace region.  Sizes are in elements of 4 bytes.
-Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q) {
+// Most (batch, head) chains the hand-off flags cover; scans are limited to it.
+constexpr int64_t kMaxChains = 65535;
+
+// Byte offsets of each workspace region.  The counters and flags sit at the
+// same offsets for every shape, ahead of all scratch, so that they are never
+// overwritten by another call's scratch and stay zero between calls.
+Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t Q) {
     Layout l{};
     const int64_t nc = (L + Q - 1) / Q;
     size_t off = 0;
+    l.counters = off; off = align_up(off + 4 * sizeof(unsigned));
+    l.flags = off;    off = align_up(off + (size_t)kMaxChains * sizeof(unsigned));
     l.states = off;   off = align_up(off + (size_t)(B * nc * H * P * N) * sizeof(float));
     l.decay = off;    off = align_up(off + (size_t)(B * H * nc) * sizeof(float));
-    l.flags = off;    off = align_up(off + (size_t)(B * H) * sizeof(unsigned));
-    l.counters = off; off = align_up(off + 4 * sizeof(unsigned));
     l.ring = off;     off = align_up(off + (size_t)(B * H * 2 * P * N) * sizeof(float));
+    l.gram = off;     off = align_up(off + gram_bytes(B, L, G, Q));
     l.total = off;
     return l;
 }
@@ -56,6 +63,7 @@ Workspace carve(void *base, const Layout &l) {
     w.flags = (unsigned *)(p + l.flags);
     w.counters = (unsigned *)(p + l.counters);
     w.ring = (float *)(p + l.ring);
+    w.gram = (void *)(p + l.gram);
     return w;
 }
 
@@ -92,7 +100,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         return SSD_ERR_INVALID_ARG;
     if (Q <= 0) return SSD_ERR_INVALID_ARG;
     if (!shape_supported(P, N, Q)) return SSD_ERR_UNSUPPORTED;
-    if (B > 65535 || H > 65535 || B * H > 65535) return SSD_ERR_UNSUPPORTED;
+    if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
         algo != SSD_ALGO_FUSED)
@@ -103,7 +111,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
                                    B * H * ((L + Q - 1) / Q) > 0x7fffffff))
         return SSD_ERR_UNSUPPORTED;
 
-    const Layout l = layout(B, L, H, P, N, Q);
+    const Layout l = layout(B, L, H, P, G, N, Q);
     if (has_work) {
         if (!workspace || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
@@ -166,7 +174,7 @@ size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
     if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0) return 0;
     if (H % G != 0 || !shape_supported(P, N, chunk_size)) return 0;
     if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return 0;
-    return layout(B, L, H, P, N, chunk_size).total;
+    return layout(B, L, H, P, G, N, chunk_size).total;
 }
 
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *Bm,
@@ -193,7 +201,7 @@ ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_byte
                                           int64_t chunk_size, hipStream_t stream) {
     if (!workspace || B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0)
         return SSD_ERR_INVALID_ARG;
-    const Layout l = layout(B, L, H, P, N, chunk_size);
+    const Layout l = layout(B, L, H, P, G, N, chunk_size);
     if (workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
     unsigned *ctr = (unsigned *)((char *)workspace + l.counters);
     unsigned host[4] = {0, 0, 0, 0};

@@ -75,6 +75,7 @@ struct Workspace {
     unsigned *flags;    // hand-off flags of the one-pass algorithm
     unsigned *counters; // ticket and completion counters of the one-pass algorithm
     float *ring;        // [B*H, 2, P, N] states handed from block to block
+    void *gram;         // [B*G, nsb, 64, 64] bf16 Cm.Bm^T of every 64-token block
 };
 
 hipError_t launch_reference_scan(const ScanArgs &a, const Workspace &ws);

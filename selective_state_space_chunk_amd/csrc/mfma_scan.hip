@@ -11,7 +11,7 @@
 //
 //   per sub-block, with Lambda the in-block inclusive prefix sum of dt*A,
 //   s the first token of the sub-block and e its last:
-//     G^T[j][i]  = Bm_j . Cm_i                        (causal 16x16 tiles only)
+//     G[i][j]    = Cm_i . Bm_j                 (gram kernel, once per group)
 //     M[i][j]    = G[i][j] exp(Lambda_i - Lambda_j) dt_j    for j <= i, else 0
 //     y_i        = exp(Lambda_i - Lambda_{s-1}) Cm_i . H  +  sum_j M[i][j] x_j
 //                  + D x_i
@@ -26,6 +26,12 @@
 // from LDS in the same (permuted) k order.  The masked decay matrix M goes
 // through LDS because all four waves need all of it.
 //
+// Memory latency is hidden inside the workgroup: the block's x (the only
+// input streamed from HBM per head) is loaded into registers when the
+// workgroup starts, and the Bm, Cm and G of the next sub-block are loaded
+// into registers while the current one computes (Bm, Cm and G are shared by
+// all heads of a group and mostly hit in L2).
+//
 // Three modes share this code:
 //   kState   the state each block produces from zero (its "chunk state") and
 //            its total decay, written to the workspace;
@@ -38,7 +44,7 @@
 //            the predecessor of ticket t holds ticket t - (B*H) and has
 //            already started: waiting on it always ends.  States are handed
 //            over through a two-slot ring per (b, h) and a flag counting the
-//            blocks published; both stay in cache.
+//            blocks published.
 #include "common.h"
 
 namespace ssd {
@@ -57,15 +63,16 @@ enum Mode { kState = 0, kOutput = 1, kFused = 2 };
 
 template <int N, int Q>
 struct Smem {
-    static constexpr int RS = N + 8;      // row stride (elements) of [64][N] tiles: +16 bytes
+    static constexpr int RS = N + 8;      // row stride (elements) of Cs: +16 bytes
     static constexpr int TS = kSub + 8;   // row stride of [*][64] tiles
     __bf16 Cs[kSub * RS];                 // Cm of the sub-block, [i][n]
-    __bf16 Bs[kSub * RS];                 // Bm of the sub-block, [j][n]
     __bf16 BwT[N * TS];                   // weighted Bm, transposed: [n][j] = w_j Bm_j[n]
     __bf16 xT[kP * TS];                   // x transposed: [p][j]
     __bf16 Mm[kSub * TS];                 // masked decay matrix: [i][j]
     float lam[Q];                         // inclusive prefix of dt*A in the block
     float dts[Q];                         // dt in the block (0 past the end)
+    float wsub[Q];                        // exp(lam[e] - lam[j]) dt_j, e = end of j's sub-block
+    float rdec[Q];                        // exp(lam[i] - lam[s - 1]), s = start of i's sub-block
     unsigned ticket;
 };
 
@@ -81,77 +88,181 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-struct Dims {
-    int64_t L, H, G;
-    int nc;
+// causal 16x16 tile k (0..9) of a 64x64 block -> (row tile it, column tile jt), jt <= it
+__device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
+    it = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+    jt = k - (it * (it + 1)) / 2;
+}
+
+// ---------------------------------------------------------------------------
+// Gram kernel: G[i][j] = Cm_i . Bm_j for every 64-token block and group, the
+// causal 16x16 tiles only (the others are never read), bf16, row-major [i][j].
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(kThreads) void gram_kernel(const __bf16 *__restrict__ Bm,
+                                                        const __bf16 *__restrict__ Cm,
+                                                        __bf16 *__restrict__ gram, int64_t L,
+                                                        int64_t G, int64_t nsb) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int64_t sbg = blockIdx.x, bg = blockIdx.y;
+    const int64_t b = bg / G, g = bg % G;
+    const int64_t t_base = sbg * kSub;
+    __bf16 *out = gram + (bg * nsb + sbg) * (int64_t)(kSub * kSub);
+    for (int k = wave; k < 10; k += 4) {
+        int it, jt;
+        tile_of(k, it, jt);
+        const int64_t tj = t_base + 16 * jt + lrow, ti = t_base + 16 * it + lrow;
+        const __bf16 *brow = Bm + ((b * L + tj) * G + g) * N;
+        const __bf16 *crow = Cm + ((b * L + ti) * G + g) * N;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks) {
+            const int n0 = 32 * ks + 8 * lgrp;
+            bf16x8 ab = {}, bc = {};
+            if (tj < L) ab = *reinterpret_cast<const bf16x8 *>(brow + n0);
+            if (ti < L) bc = *reinterpret_cast<const bf16x8 *>(crow + n0);
+            acc = mfma(ab, bc, acc);          // rows j, column i
+        }
+        const int i = 16 * it + lrow;
+        uint2 pk;
+        pk.x = pack2(acc[0], acc[1]);
+        pk.y = pack2(acc[2], acc[3]);
+        *reinterpret_cast<uint2 *>(out + i * kSub + 16 * jt + 4 * lgrp) = pk;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-thread registers holding one sub-block's Bm, Cm and G until staged.
+// ---------------------------------------------------------------------------
+template <int N>
+struct SubRegs {
+    uint4 b[2 * (N / 64)];   // Bm: N/64 units of (token pair, 8 columns)
+    uint4 c[N / 32];         // Cm: row pieces of 8 columns
+    uint2 g[3];              // G: this wave's causal tiles, 4 values per lane
 };
 
-// Stage one sub-block into LDS.  Tokens past the valid count q are zeros.
-//   xT[p][j]  always;  BwT[n][j] = w_j Bm_j[n] always (w_j = exp(lam_e - lam_j) dt_j);
-//   Cs, Bs (row copies) only when FULL.
-template <int N, int Q, bool FULL>
-__device__ __forceinline__ void stage_sub_block(Smem<N, Q> &sm, const __bf16 *__restrict__ x,
-                                                const __bf16 *__restrict__ Bm,
-                                                const __bf16 *__restrict__ Cm, const Dims &d,
-                                                int64_t b, int64_t h, int64_t g, int64_t t0,
-                                                int s, int q) {
-    using S = Smem<N, Q>;
-    const int tid = threadIdx.x;
-    const int e = s + kSub - 1;
-    const float lam_e = sm.lam[e];
-    // x: thread -> token pair tp (tokens 2tp, 2tp+1 of the sub-block), 8 columns 8pg..8pg+7
-    {
-        const int tp = tid & 31, pg = tid >> 5;
-        const int j0 = 2 * tp;
-        uint4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-        if (s + j0 < q)
-            v0 = *reinterpret_cast<const uint4 *>(x + ((((int64_t)b * d.L + t0 + s + j0) * d.H + h) * kP + 8 * pg));
-        if (s + j0 + 1 < q)
-            v1 = *reinterpret_cast<const uint4 *>(x + ((((int64_t)b * d.L + t0 + s + j0 + 1) * d.H + h) * kP + 8 * pg));
-        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+struct Ctx {
+    const __bf16 *x, *Bm, *Cm, *gram;
+    int64_t b, h, g, t0, L, H, G, nsb;
+    int q;
+};
+
+template <int N>
+__device__ __forceinline__ void load_sub(SubRegs<N> &r, const Ctx &cx, int s, bool with_b, bool with_cg) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lrow = lane & 15, lgrp = lane >> 4;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = (a0[k] & 0xffffu) | (a1[k] << 16);          // column 2k
-            const uint32_t hi = (a0[k] >> 16) | (a1[k] & 0xffff0000u);      // column 2k+1
-            *reinterpret_cast<uint32_t *>(&sm.xT[(8 * pg + 2 * k) * S::TS + j0]) = lo;
-            *reinterpret_cast<uint32_t *>(&sm.xT[(8 * pg + 2 * k + 1) * S::TS + j0]) = hi;
+    for (int k = 0; k < N / 64 && with_b; ++k) {
+        const int u = tid + k * kThreads;
+        const int tp = u & 31, cg = u >> 5;
+        const int j0 = s + 2 * tp;
+        const __bf16 *p0 = cx.Bm + (((cx.b * cx.L + cx.t0 + j0) * cx.G + cx.g) * N + 8 * cg);
+        r.b[2 * k] = j0 < cx.q ? *reinterpret_cast<const uint4 *>(p0) : uint4{0, 0, 0, 0};
+        r.b[2 * k + 1] = j0 + 1 < cx.q ? *reinterpret_cast<const uint4 *>(p0 + cx.G * N) : uint4{0, 0, 0, 0};
+    }
+    if (with_cg) {
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const int u = tid + k * kThreads;
+            const int j = u / (N / 8), cg = u % (N / 8);
+            r.c[k] = s + j < cx.q
+                         ? *reinterpret_cast<const uint4 *>(cx.Cm + (((cx.b * cx.L + cx.t0 + s + j) * cx.G + cx.g) * N + 8 * cg))
+                         : uint4{0, 0, 0, 0};
+        }
+        const int64_t sbg = (cx.t0 + s) / kSub;
+        const __bf16 *gb = cx.gram + ((cx.b * cx.G + cx.g) * cx.nsb + sbg) * (int64_t)(kSub * kSub);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int k = wave + 4 * m;
+            if (k < 10) {
+                int it, jt;
+                tile_of(k, it, jt);
+                r.g[m] = *reinterpret_cast<const uint2 *>(gb + (16 * it + lrow) * kSub + 16 * jt + 4 * lgrp);
+            }
         }
     }
-    // Bm: units of (token pair, 8 columns); N/8 column groups x 32 pairs
-    constexpr int kGroups = N / 8;
-    constexpr int kUnits = kGroups * 32;
+}
+
+// x of the whole block into registers: per sub-block, tokens 2tp, 2tp+1 and
+// columns 8pg..8pg+7 (tp = tid & 31, pg = tid >> 5).
+template <int NSB>
+__device__ __forceinline__ void load_x(uint4 (&xr)[2 * NSB], const Ctx &cx) {
+    const int tid = threadIdx.x, tp = tid & 31, pg = tid >> 5;
 #pragma unroll
-    for (int u = tid; u < kUnits; u += kThreads) {
-        const int tp = u & 31, cg = u >> 5;
-        const int j0 = 2 * tp;
-        uint4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-        if (s + j0 < q)
-            v0 = *reinterpret_cast<const uint4 *>(Bm + ((((int64_t)b * d.L + t0 + s + j0) * d.G + g) * N + 8 * cg));
-        if (s + j0 + 1 < q)
-            v1 = *reinterpret_cast<const uint4 *>(Bm + ((((int64_t)b * d.L + t0 + s + j0 + 1) * d.G + g) * N + 8 * cg));
-        if (FULL) {
-            *reinterpret_cast<uint4 *>(&sm.Bs[j0 * S::RS + 8 * cg]) = v0;
-            *reinterpret_cast<uint4 *>(&sm.Bs[(j0 + 1) * S::RS + 8 * cg]) = v1;
-        }
-        const float w0 = __expf(lam_e - sm.lam[s + j0]) * sm.dts[s + j0];
-        const float w1 = __expf(lam_e - sm.lam[s + j0 + 1]) * sm.dts[s + j0 + 1];
-        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+    for (int sb = 0; sb < NSB; ++sb) {
+        const int j0 = sb * kSub + 2 * tp;
+        const __bf16 *p0 = cx.x + (((cx.b * cx.L + cx.t0 + j0) * cx.H + cx.h) * kP + 8 * pg);
+        xr[2 * sb] = j0 < cx.q ? *reinterpret_cast<const uint4 *>(p0) : uint4{0, 0, 0, 0};
+        xr[2 * sb + 1] = j0 + 1 < cx.q ? *reinterpret_cast<const uint4 *>(p0 + cx.H * kP) : uint4{0, 0, 0, 0};
+    }
+}
+
+// Stage sub-block s: xT always; BwT when WITH_B; Cs and the masked matrix Mm when FULL.
+template <int N, int Q, bool WITH_B, bool FULL>
+__device__ __forceinline__ void stage(Smem<N, Q> &sm, const SubRegs<N> &r, uint4 x0, uint4 x1, int s) {
+    using S = Smem<N, Q>;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    {
+        const int tp = tid & 31, pg = tid >> 5, j0 = 2 * tp;
+        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            *reinterpret_cast<uint32_t *>(&sm.BwT[(8 * cg + 2 * k) * S::TS + j0]) =
-                pack2(w0 * lo_bf16(a0[k]), w1 * lo_bf16(a1[k]));
-            *reinterpret_cast<uint32_t *>(&sm.BwT[(8 * cg + 2 * k + 1) * S::TS + j0]) =
-                pack2(w0 * hi_bf16(a0[k]), w1 * hi_bf16(a1[k]));
+            *reinterpret_cast<uint32_t *>(&sm.xT[(8 * pg + 2 * k) * S::TS + j0]) = (a0[k] & 0xffffu) | (a1[k] << 16);
+            *reinterpret_cast<uint32_t *>(&sm.xT[(8 * pg + 2 * k + 1) * S::TS + j0]) = (a0[k] >> 16) | (a1[k] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < N / 64 && WITH_B; ++k) {
+        const int u = tid + k * kThreads;
+        const int tp = u & 31, cg = u >> 5, j0 = 2 * tp;
+        const float w0 = sm.wsub[s + j0], w1 = sm.wsub[s + j0 + 1];
+        const uint4 v0 = r.b[2 * k], v1 = r.b[2 * k + 1];
+        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            *reinterpret_cast<uint32_t *>(&sm.BwT[(8 * cg + 2 * m) * S::TS + j0]) =
+                pack2(w0 * lo_bf16(a0[m]), w1 * lo_bf16(a1[m]));
+            *reinterpret_cast<uint32_t *>(&sm.BwT[(8 * cg + 2 * m + 1) * S::TS + j0]) =
+                pack2(w0 * hi_bf16(a0[m]), w1 * hi_bf16(a1[m]));
         }
     }
     if (FULL) {
-        // Cm: plain row copies, 16 bytes per thread per step
-        for (int u = tid; u < kSub * kGroups; u += kThreads) {
-            const int j = u / kGroups, cg = u % kGroups;
-            uint4 v = {0, 0, 0, 0};
-            if (s + j < q)
-                v = *reinterpret_cast<const uint4 *>(Cm + ((((int64_t)b * d.L + t0 + s + j) * d.G + g) * N + 8 * cg));
-            *reinterpret_cast<uint4 *>(&sm.Cs[j * S::RS + 8 * cg]) = v;
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const int u = tid + k * kThreads;
+            const int j = u / (N / 8), cg = u % (N / 8);
+            *reinterpret_cast<uint4 *>(&sm.Cs[j * S::RS + 8 * cg]) = r.c[k];
+        }
+        // masked decay matrix from this wave's G tiles
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int k = wave + 4 * m;
+            if (k < 10) {
+                int it, jt;
+                tile_of(k, it, jt);
+                const int i = 16 * it + lrow;
+                const float li = sm.lam[s + i];
+                const uint32_t gw[2] = {r.g[m].x, r.g[m].y};
+                float mv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * jt + 4 * lgrp + e;
+                    const float gv = (e & 1) ? hi_bf16(gw[e >> 1]) : lo_bf16(gw[e >> 1]);
+                    mv[e] = j <= i ? gv * __expf(li - sm.lam[s + j]) * sm.dts[s + j] : 0.f;
+                }
+                uint2 pk;
+                pk.x = pack2(mv[0], mv[1]);
+                pk.y = pack2(mv[2], mv[3]);
+                *reinterpret_cast<uint2 *>(&sm.Mm[i * S::TS + 16 * jt + 4 * lgrp]) = pk;
+            }
+        }
+        if (wave >= 2) {
+            // tiles above the diagonal that the apply step reads: (0,1), (2,3)
+            const int it = wave == 2 ? 0 : 2;
+            *reinterpret_cast<uint2 *>(&sm.Mm[(16 * it + lrow) * S::TS + 16 * (it + 1) + 4 * lgrp]) =
+                uint2{0u, 0u};
         }
     }
 }
@@ -179,8 +290,8 @@ __device__ __forceinline__ void scale_state(f32x4 (&Hacc)[N / 16], float f) {
     for (int t = 0; t < N / 16; ++t) Hacc[t] *= f;
 }
 
-// Load / store the state of one (b, h) ([P][N] float32, row-major) in the
-// accumulator layout: lane holds p = 16*wave + lrow, n = 16t + 4*lgrp + 0..3.
+// A state of one (b, h) is [P][N] float32, row-major.  In the accumulator
+// layout a lane holds p = 16*wave + lrow, n = 16t + 4*lgrp + 0..3.
 template <int N>
 __device__ __forceinline__ void load_state(f32x4 (&Hacc)[N / 16], const float *src, int wave,
                                            int lrow, int lgrp) {
@@ -198,17 +309,20 @@ __device__ __forceinline__ void store_state(const f32x4 (&Hacc)[N / 16], float *
 }
 
 template <int N, int Q, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_mfma(
+__global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     const __bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm, const float *__restrict__ D,
     const float *init, __bf16 *__restrict__ y, float *final_state, float *states,
-    float *decay, unsigned *flags, unsigned *counters, float *ring, int64_t Bsz, int64_t L,
-    int64_t H, int64_t G) {
+    float *decay, unsigned *flags, unsigned *counters, float *ring, const __bf16 *gram,
+    int64_t Bsz, int64_t L, int64_t H, int64_t G) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     using S = Smem<N, Q>;
     S &sm = *reinterpret_cast<S *>(smem_raw);
     constexpr int NT = N / 16;
     constexpr int NSB = Q / kSub;
+    // One pass keeps bf16 snapshots of the block-local state at every
+    // sub-block boundary, so its output pass needs no state recurrence.
+    constexpr bool kSnap = MODE == kFused;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -233,28 +347,77 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
         c = blockIdx.x;
         chain = blockIdx.y;
     }
-    const int64_t b = chain / H, h = chain % H, g = h / (H / G);
-    const int64_t t0 = c * Q;
-    const int q = (int)((L - t0) < Q ? (L - t0) : Q);
-    const Dims d{L, H, G, nc};
+    Ctx cx;
+    cx.x = x; cx.Bm = Bm; cx.Cm = Cm; cx.gram = gram;
+    cx.b = chain / H; cx.h = chain % H; cx.g = cx.h / (H / G);
+    cx.t0 = c * Q; cx.L = L; cx.H = H; cx.G = G; cx.nsb = (int64_t)nc * (Q / kSub);
+    cx.q = (int)((L - cx.t0) < Q ? (L - cx.t0) : Q);
+    const int q = cx.q;
 
-    block_prefix(dt + (b * L + t0) * H + h, H, q, Q, A[h], sm.lam, sm.dts);
+    // issue every load the block starts with: dt, the block's x, the first sub-block
+    const float dtv = tid < q ? dt[(cx.b * L + cx.t0 + tid) * H + cx.h] : 0.f;
+    uint4 xr[2 * NSB];
+    load_x<NSB>(xr, cx);
+    SubRegs<N> r;
+    load_sub<N>(r, cx, 0, MODE != kOutput || !kSnap, MODE == kOutput);
+
+    // in-block prefix sums of dt*A (first wave), then per-token weights and decays
+    if (tid < Q) sm.dts[tid] = dtv;
+    __syncthreads();
+    if (wave == 0) {
+        const float Ah = A[cx.h];
+        float carry = 0.f;
+#pragma unroll
+        for (int base = 0; base < Q; base += 64) {
+            float v = sm.dts[base + lane] * Ah;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(v, off);
+                if (lane >= off) v += o;
+            }
+            v += carry;
+            sm.lam[base + lane] = v;
+            carry = __shfl(v, 63);
+        }
+    }
+    __syncthreads();
+    if (tid < Q) {
+        const int s0 = tid & ~(kSub - 1);
+        const float lj = sm.lam[tid];
+        const float before = s0 == 0 ? 0.f : sm.lam[s0 - 1];
+        sm.wsub[tid] = __expf(sm.lam[s0 + kSub - 1] - lj) * sm.dts[tid];
+        sm.rdec[tid] = __expf(lj - before);
+    }
+    __syncthreads();
 
     f32x4 Hacc[NT];
-    const int64_t state_off = ((b * nc + c) * H + h) * (int64_t)(kP * N);
+    uint32_t Ts[NSB > 1 ? NSB - 1 : 1][2 * NT];   // bf16 snapshots (one pass only)
+    const int64_t state_off = ((cx.b * nc + c) * H + cx.h) * (int64_t)(kP * N);
 
     if (MODE == kState || MODE == kFused) {
         // the block's own state, from zero
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             const int s = sb * kSub;
             if (s >= q) break;
-            stage_sub_block<N, Q, false>(sm, x, Bm, Cm, d, b, h, g, t0, s, q);
+            stage<N, Q, true, false>(sm, r, xr[2 * sb], xr[2 * sb + 1], s);
+            if (sb + 1 < NSB && s + kSub < q)
+                load_sub<N>(r, cx, s + kSub, true, false);
+            else if (MODE == kFused)
+                load_sub<N>(r, cx, 0, false, true);   // first sub-block of the output pass
             __syncthreads();
             const float before = s == 0 ? 0.f : sm.lam[s - 1];
             scale_state<N>(Hacc, __expf(sm.lam[s + kSub - 1] - before));
             state_update<N, Q>(Hacc, sm, wave, lrow, lgrp);
+            if (kSnap && sb + 1 < NSB) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    Ts[sb][2 * t] = pack2(Hacc[t][0], Hacc[t][1]);
+                    Ts[sb][2 * t + 1] = pack2(Hacc[t][2], Hacc[t][3]);
+                }
+            }
             __syncthreads();
         }
         const float gamma = __expf(sm.lam[Q - 1]);
@@ -263,7 +426,8 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
             if (tid == 0) decay[chain * nc + c] = gamma;
             return;
         }
-        // take the entering state H_c, publish H_{c+1} = gamma H_c + S_c
+        // take the entering state H_c, hand on H_{c+1} = gamma H_c + S_c
+        const int64_t lane_off = (int64_t)(16 * wave + lrow) * N + 4 * lgrp;   // floats
         f32x4 Hin[NT];
         if (c == 0) {
             if (init) {
@@ -275,31 +439,40 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
         } else {
             if (tid == 0) {
                 unsigned spins = 0;
-                while (__hip_atomic_load(&flags[chain], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+                while (__hip_atomic_load(&flags[chain], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                        (unsigned)c) {
-                    __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_s_sleep(1);
                     if (++spins > kSpinLimit) {       // never expected: record and go on
                         atomicOr(&counters[2], 1u);
                         break;
                     }
                 }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            load_state<N>(Hin, ring + (chain * 2 + (c & 1)) * (int64_t)(kP * N), wave, lrow, lgrp);
+            // device-coherent 16-byte loads (sc1): the state was written by another CU
+            const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+                ring + (chain * 2 + (c & 1)) * (int64_t)(kP * N), 0, kP * N * 4, 0x00020000);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                Hin[t] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)((lane_off + 16 * t) * 4), 0, 16);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hacc[t] = gamma * Hin[t] + Hacc[t];
         if (c + 1 < nc) {
-            store_state<N>(Hacc, ring + (chain * 2 + ((c + 1) & 1)) * (int64_t)(kP * N), wave, lrow, lgrp);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+                ring + (chain * 2 + ((c + 1) & 1)) * (int64_t)(kP * N), 0, kP * N * 4, 0x00020000);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                __builtin_amdgcn_raw_buffer_store_b128(Hacc[t], dst, (int)((lane_off + 16 * t) * 4), 0, 16);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's hand-off stores done
             __syncthreads();
             if (tid == 0)
                 __hip_atomic_store(&flags[chain], (unsigned)(c + 1), __ATOMIC_RELEASE,
                                    __HIP_MEMORY_SCOPE_AGENT);
         } else {
             if (final_state) store_state<N>(Hacc, final_state + chain * (int64_t)(kP * N), wave, lrow, lgrp);
-            if (tid == 0) flags[chain] = 0u;      // last user of this chain's flag
+            if (tid == 0) flags[chain] = 0u;      // last user of this chain's flag: leave it zero
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hacc[t] = Hin[t];
@@ -308,57 +481,34 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
     }
 
     // outputs of the block from the entering state
-    const float Dh = D[h];
+    const float Dh = D[cx.h];
+#pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
         const int s = sb * kSub;
         if (s >= q) break;
-        stage_sub_block<N, Q, true>(sm, x, Bm, Cm, d, b, h, g, t0, s, q);
+        stage<N, Q, !kSnap, true>(sm, r, xr[2 * sb], xr[2 * sb + 1], s);
+        if (sb + 1 < NSB && s + kSub < q) load_sub<N>(r, cx, s + kSub, !kSnap, true);
         __syncthreads();
-        const float before = s == 0 ? 0.f : sm.lam[s - 1];
 
-        // masked decay matrix: causal 16x16 tiles (it >= jt), 10 of them, round-robin over waves
-        for (int k = wave; k < 10; k += 4) {
-            const int it = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
-            const int jt = k - (it * (it + 1)) / 2;
-            f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < N / 32; ++ks) {
-                const int n0 = 32 * ks + 8 * lgrp;
-                const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(&sm.Bs[(16 * jt + lrow) * S::RS + n0]);
-                const bf16x8 bc = *reinterpret_cast<const bf16x8 *>(&sm.Cs[(16 * it + lrow) * S::RS + n0]);
-                gacc = mfma(ab, bc, gacc);
-            }
-            const int i = 16 * it + lrow;                 // column of G^T: output token
-            const float li = sm.lam[s + i];
-            float m[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * jt + 4 * lgrp + r;     // row of G^T: input token
-                m[r] = j <= i ? gacc[r] * __expf(li - sm.lam[s + j]) * sm.dts[s + j] : 0.f;
-            }
-            uint2 pk;
-            pk.x = pack2(m[0], m[1]);
-            pk.y = pack2(m[2], m[3]);
-            *reinterpret_cast<uint2 *>(&sm.Mm[i * S::TS + 16 * jt + 4 * lgrp]) = pk;
-        }
-        if (wave >= 2) {
-            // zero tiles above the diagonal that the apply step reads: (0,1), (2,3)
-            const int it = wave == 2 ? 0 : 2;
-            *reinterpret_cast<uint2 *>(&sm.Mm[(16 * it + lrow) * S::TS + 16 * (it + 1) + 4 * lgrp]) =
-                uint2{0u, 0u};
-        }
-
-        // inter-block part: Y^T[p][i] = sum_n H[p][n] Cm_i[n], then the row decay
+        // inter-block part: Y^T[p][i] = sum_n H[p][n] Cm_i[n], with H the state
+        // entering the sub-block, then the row decay exp(lam_i - lam_{s-1})
+        const float eb = kSnap ? (s == 0 ? 1.f : __expf(sm.lam[s - 1])) : 1.f;
         f32x4 Y[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) Y[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) {
+            f32x4 h0 = Hacc[2 * ks], h1 = Hacc[2 * ks + 1];
+            if (kSnap && sb > 0) {
+                const uint32_t *tw = &Ts[sb > 0 ? sb - 1 : 0][4 * ks];
+                h0 = eb * h0 + f32x4{lo_bf16(tw[0]), hi_bf16(tw[0]), lo_bf16(tw[1]), hi_bf16(tw[1])};
+                h1 = eb * h1 + f32x4{lo_bf16(tw[2]), hi_bf16(tw[2]), lo_bf16(tw[3]), hi_bf16(tw[3])};
+            }
             bf16x8 ah;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                ah[r] = (__bf16)Hacc[2 * ks][r];
-                ah[4 + r] = (__bf16)Hacc[2 * ks + 1][r];
+            for (int e = 0; e < 4; ++e) {
+                ah[e] = (__bf16)h0[e];
+                ah[4 + e] = (__bf16)h1[e];
             }
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -370,8 +520,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
             }
         }
 #pragma unroll
-        for (int it = 0; it < 4; ++it) Y[it] *= __expf(sm.lam[s + 16 * it + lrow] - before);
-        __syncthreads();   // Mm complete
+        for (int it = 0; it < 4; ++it) Y[it] *= sm.rdec[s + 16 * it + lrow];
 
         // intra-block part: Y^T[p][i] += sum_j x_j[p] M[i][j] (causal k-steps only)
 #pragma unroll
@@ -385,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
                 Y[it] = mfma(ax, bm, Y[it]);
             }
         }
-        // skip term and store: lane holds p = 16*wave + 4*lgrp + r, token i = 16*it + lrow
+        // skip term and store: lane holds p = 16*wave + 4*lgrp + e, token i = 16*it + lrow
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int i = 16 * it + lrow;
@@ -393,15 +542,16 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
                 const int p0 = 16 * wave + 4 * lgrp;
                 float o[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[r] = Y[it][r] + Dh * (float)sm.xT[(p0 + r) * S::TS + i];
+                for (int e = 0; e < 4; ++e)
+                    o[e] = Y[it][e] + Dh * (float)sm.xT[(p0 + e) * S::TS + i];
                 uint2 pk;
                 pk.x = pack2(o[0], o[1]);
                 pk.y = pack2(o[2], o[3]);
-                *reinterpret_cast<uint2 *>(y + (((b * L + t0 + s + i) * H + h) * kP + p0)) = pk;
+                *reinterpret_cast<uint2 *>(y + (((cx.b * L + cx.t0 + s + i) * H + cx.h) * kP + p0)) = pk;
             }
         }
-        if (sb + 1 < NSB && s + kSub < q) {
+        if (!kSnap && sb + 1 < NSB && s + kSub < q) {
+            const float before = s == 0 ? 0.f : sm.lam[s - 1];
             scale_state<N>(Hacc, __expf(sm.lam[s + kSub - 1] - before));
             state_update<N, Q>(Hacc, sm, wave, lrow, lgrp);
         }
@@ -409,11 +559,10 @@ __global__ __launch_bounds__(kThreads) void scan_mfma(
     }
 
     if (MODE == kFused && tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned done = atomicAdd(&counters[1], 1u);
         if (done + 1 == (unsigned)(nchains * nc)) {   // last workgroup: reset for the next launch
-            counters[0] = 0u;
-            counters[1] = 0u;
+            __hip_atomic_store(&counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&counters[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -431,16 +580,21 @@ hipError_t launch_mode(const ScanArgs &a, const Workspace &ws, dim3 grid) {
     }
     kern<<<grid, kThreads, smem, a.stream>>>(
         (const __bf16 *)a.x, a.dt, a.A, (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, a.D, a.init,
-        (__bf16 *)a.y, a.final_state, ws.states, ws.decay, ws.flags, ws.counters, ws.ring, a.B, a.L,
-        a.H, a.G);
+        (__bf16 *)a.y, a.final_state, ws.states, ws.decay, ws.flags, ws.counters, ws.ring,
+        (const __bf16 *)ws.gram, a.B, a.L, a.H, a.G);
     return hipGetLastError();
 }
 
 template <int N, int Q>
 hipError_t run(const ScanArgs &a, const Workspace &ws, bool fused) {
     const int nc = (int)((a.L + Q - 1) / Q);
+    const int64_t nsb = (int64_t)nc * (Q / kSub);
+    gram_kernel<N><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+        (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (fused) return launch_mode<N, Q, kFused>(a, ws, dim3((unsigned)(nc * a.B * a.H)));
-    hipError_t e = launch_mode<N, Q, kState>(a, ws, dim3((unsigned)nc, (unsigned)(a.B * a.H)));
+    e = launch_mode<N, Q, kState>(a, ws, dim3((unsigned)nc, (unsigned)(a.B * a.H)));
     if (e != hipSuccess) return e;
     e = launch_state_pass(ws.states, ws.decay, a.init, a.final_state, a.B, a.H, kP * N, nc, a.stream);
     if (e != hipSuccess) return e;
@@ -473,6 +627,11 @@ bool mfma_supported(int64_t P, int64_t N, int64_t Q) {
 }
 
 size_t fused_max_chains() { return (size_t)1 << 30; }
+
+size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q) {
+    const int64_t nc = (L + Q - 1) / Q;
+    return (size_t)(B * G * nc * Q * kSub) * sizeof(__bf16);
+}
 
 hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws, false); }
 

@@ -143,3 +143,25 @@ def test_empty_inputs():
                                     D, None, 256)
     torch.cuda.synchronize()
     assert y.shape == xb.shape and fin.shape == (0, H, P, N)
+
+
+def test_one_workspace_serves_different_shapes():
+    """Scratch written by one call (states of a large staged scan) must never
+    land where a later one-pass call keeps its hand-off counters and flags."""
+    import selective_state_space_chunk_amd as ssd
+    nbytes = max(ssd.ssd_chunk_scan_workspace_size(4, 1500, 8, 64, 1, 256, 64, torch.bfloat16),
+                 ssd.ssd_chunk_scan_workspace_size(3, 700, 10, 64, 1, 128, 128, torch.bfloat16))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    big = si.make_scan_inputs(4, 1500, 8, 64, 256, 1, dtype="bf16", init=True, seed=901)
+    announce("shared workspace: staged B4 L1500 H8 N256 Q64")
+    gpu_scan(to_device(big, "bf16"), 64, algo="staged", workspace_tensor=ws)
+    for shape in [(3, 700, 10, 128, 128), (1, 300, 2, 64, 64), (4, 1500, 8, 256, 64)]:
+        B, L, H, N, Q = shape
+        d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=True, seed=902 + L,
+                                regime="long_memory")
+        announce(f"shared workspace: fused B{B} L{L} H{H} N{N} Q{Q}")
+        y, fin = gpu_scan(to_device(d, "bf16"), Q, algo="fused", workspace_tensor=ws)
+        ssd.ssd_chunk_scan_workspace_check(ws, B, L, H, 64, 1, N, Q)
+        y_ref, f_ref = oracle_scan(d)
+        assert rel_err(to_np(y), y_ref) <= 2e-2
+        assert rel_err(to_np(fin), f_ref) <= 2e-2
