@@ -130,8 +130,9 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
 /*
  * As ssd_chunk_scan_fwd, with the kernel sequence chosen by the caller.  An
  * algorithm that does not cover the shape or dtype returns
- * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16,
- * P == 64 and N in {64, 128, 256}).
+ * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16 and
+ * P == 64; SSD_ALGO_STAGED takes N in {64, 128, 256}, SSD_ALGO_FUSED N in
+ * {64, 128}).
  */
 ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A,
                                    const void *Bm, const void *Cm, const float *D,

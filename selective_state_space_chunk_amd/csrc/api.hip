@@ -11,6 +11,7 @@ hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws);
 bool mfma_supported(int64_t P, int64_t N, int64_t Q);
 size_t fused_max_chains();
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
+bool fused_supported(int64_t N, int64_t Q);
 }
 
 namespace {
@@ -107,6 +108,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         return SSD_ERR_UNSUPPORTED;
     const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
     if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED) && !mfma_ok) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_FUSED && !fused_supported(N, Q)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && ((size_t)(B * H) > fused_max_chains() ||
                                    B * H * ((L + Q - 1) / Q) > 0x7fffffff))
         return SSD_ERR_UNSUPPORTED;
@@ -137,8 +139,8 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         } else {
             const int64_t nc = (L + Q - 1) / Q;
             // one pass while chains of blocks are short and many; staged otherwise
-            algo = (nc <= 64 && (size_t)(B * H) <= fused_max_chains() && B * H >= 64 &&
-                    B * H * nc <= 0x7fffffff)
+            algo = (nc <= 64 && fused_supported(N, Q) && (size_t)(B * H) <= fused_max_chains() &&
+                    B * H >= 64 && B * H * nc <= 0x7fffffff)
                        ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
         }
     }

@@ -79,6 +79,8 @@ struct Workspace {
 };
 
 hipError_t launch_reference_scan(const ScanArgs &a, const Workspace &ws);
+// Cm.Bm^T of every 64-token block (matrix-core paths), into ws.gram.
+hipError_t launch_gram(const ScanArgs &a, const Workspace &ws, int64_t nsb);
 // H_{c+1} = decay_c H_c + S_c over the blocks of every (b, h), in place (the
 // state entering each block replaces the block's own state); final state out.
 hipError_t launch_state_pass(float *states, const float *decay, const float *init, float *final_state,

@@ -96,7 +96,10 @@ __device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
 
 // ---------------------------------------------------------------------------
 // Gram kernel: G[i][j] = Cm_i . Bm_j for every 64-token block and group, the
-// causal 16x16 tiles only (the others are never read), bf16, row-major [i][j].
+// causal 16x16 tiles only (the others are never read), bf16.  Storage is in
+// matrix-core fragment order so that a wave reads a tile as one contiguous
+// 512-byte run: tile k (0..9, see tile_of) holds, for lane l = 16*lgrp + lrow,
+// G[16*it + lrow][16*jt + 4*lgrp + 0..3] at elements (64*k + l)*4 .. +3.
 // ---------------------------------------------------------------------------
 template <int N>
 __global__ __launch_bounds__(kThreads) void gram_kernel(const __bf16 *__restrict__ Bm,
@@ -124,11 +127,10 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(const __bf16 *__restrict
             if (ti < L) bc = *reinterpret_cast<const bf16x8 *>(crow + n0);
             acc = mfma(ab, bc, acc);          // rows j, column i
         }
-        const int i = 16 * it + lrow;
         uint2 pk;
         pk.x = pack2(acc[0], acc[1]);
         pk.y = pack2(acc[2], acc[3]);
-        *reinterpret_cast<uint2 *>(out + i * kSub + 16 * jt + 4 * lgrp) = pk;
+        *reinterpret_cast<uint2 *>(out + (k * 64 + lane) * 4) = pk;
     }
 }
 
@@ -155,7 +157,7 @@ __device__ __forceinline__ void load_sub(SubRegs<N> &r, const Ctx &cx, int s, bo
 #pragma unroll
     for (int k = 0; k < N / 64 && with_b; ++k) {
         const int u = tid + k * kThreads;
-        const int tp = u & 31, cg = u >> 5;
+        const int cg = u % (N / 8), tp = u / (N / 8);
         const int j0 = s + 2 * tp;
         const __bf16 *p0 = cx.Bm + (((cx.b * cx.L + cx.t0 + j0) * cx.G + cx.g) * N + 8 * cg);
         r.b[2 * k] = j0 < cx.q ? *reinterpret_cast<const uint4 *>(p0) : uint4{0, 0, 0, 0};
@@ -175,20 +177,16 @@ __device__ __forceinline__ void load_sub(SubRegs<N> &r, const Ctx &cx, int s, bo
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
             const int k = wave + 4 * m;
-            if (k < 10) {
-                int it, jt;
-                tile_of(k, it, jt);
-                r.g[m] = *reinterpret_cast<const uint2 *>(gb + (16 * it + lrow) * kSub + 16 * jt + 4 * lgrp);
-            }
+            if (k < 10) r.g[m] = *reinterpret_cast<const uint2 *>(gb + (k * 64 + lane) * 4);
         }
     }
 }
 
 // x of the whole block into registers: per sub-block, tokens 2tp, 2tp+1 and
-// columns 8pg..8pg+7 (tp = tid & 31, pg = tid >> 5).
+// columns 8pg..8pg+7 (pg = tid & 7, tp = tid >> 3: eight lanes cover one 128-byte row).
 template <int NSB>
 __device__ __forceinline__ void load_x(uint4 (&xr)[2 * NSB], const Ctx &cx) {
-    const int tid = threadIdx.x, tp = tid & 31, pg = tid >> 5;
+    const int tid = threadIdx.x, pg = tid & 7, tp = tid >> 3;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
         const int j0 = sb * kSub + 2 * tp;
@@ -205,7 +203,7 @@ __device__ __forceinline__ void stage(Smem<N, Q> &sm, const SubRegs<N> &r, uint4
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lrow = lane & 15, lgrp = lane >> 4;
     {
-        const int tp = tid & 31, pg = tid >> 5, j0 = 2 * tp;
+        const int pg = tid & 7, tp = tid >> 3, j0 = 2 * tp;
         const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -216,7 +214,7 @@ __device__ __forceinline__ void stage(Smem<N, Q> &sm, const SubRegs<N> &r, uint4
 #pragma unroll
     for (int k = 0; k < N / 64 && WITH_B; ++k) {
         const int u = tid + k * kThreads;
-        const int tp = u & 31, cg = u >> 5, j0 = 2 * tp;
+        const int cg = u % (N / 8), tp = u / (N / 8), j0 = 2 * tp;
         const float w0 = sm.wsub[s + j0], w1 = sm.wsub[s + j0 + 1];
         const uint4 v0 = r.b[2 * k], v1 = r.b[2 * k + 1];
         const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -635,6 +633,23 @@ size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q) {
 
 hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws, false); }
 
-hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws, true); }
+hipError_t launch_gram(const ScanArgs &a, const Workspace &ws, int64_t nsb) {
+    switch (a.N) {
+        case 64:
+            gram_kernel<64><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+                (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
+            break;
+        case 128:
+            gram_kernel<128><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+                (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
+            break;
+        case 256:
+            gram_kernel<256><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+                (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 }  // namespace ssd

@@ -22,7 +22,7 @@ SMALL = [
     ("bf16_one_token", 2, 1, 4, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
     ("bf16_ragged_init", 2, 300, 4, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
     ("bf16_long_memory_q64", 1, 1000, 3, 64, 64, 1, 64, "bf16", False, "long_memory", MFMA_ALGOS),
-    ("bf16_no_decay_groups_n256", 2, 513, 4, 64, 256, 2, 128, "bf16", True, "no_decay", MFMA_ALGOS),
+    ("bf16_no_decay_groups_n256", 2, 513, 4, 64, 256, 2, 128, "bf16", True, "no_decay", ["reference", "staged", "auto"]),
     ("bf16_long_memory_n128_q128", 2, 777, 6, 64, 128, 3, 128, "bf16", True, "long_memory", MFMA_ALGOS),
     ("bf16_many_chunks", 1, 4100, 2, 64, 128, 1, 64, "bf16", True, "long_memory", MFMA_ALGOS),
 ]
@@ -155,7 +155,7 @@ def test_one_workspace_serves_different_shapes():
     big = si.make_scan_inputs(4, 1500, 8, 64, 256, 1, dtype="bf16", init=True, seed=901)
     announce("shared workspace: staged B4 L1500 H8 N256 Q64")
     gpu_scan(to_device(big, "bf16"), 64, algo="staged", workspace_tensor=ws)
-    for shape in [(3, 700, 10, 128, 128), (1, 300, 2, 64, 64), (4, 1500, 8, 256, 64)]:
+    for shape in [(3, 700, 10, 128, 128), (1, 300, 2, 64, 64), (4, 1500, 8, 128, 64)]:
         B, L, H, N, Q = shape
         d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=True, seed=902 + L,
                                 regime="long_memory")
