@@ -143,11 +143,14 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    ssd_algo algo, hipStream_t stream);
 
 /*
- * Diagnostic: waits for `stream`, then reports whether a block-to-block
- * hand-off of SSD_ALGO_FUSED in this workspace ever gave up waiting (a bounded
- * wait that is never expected to expire; when it does, outputs of that call
- * are wrong).  Returns SSD_OK when none did, SSD_ERR_HIP when one did or a
- * HIP call failed; clears the indicator.  Same shape arguments as the scan.
+ * Diagnostic: waits for `stream`, then checks the hand-off state that
+ * SSD_ALGO_FUSED keeps in this workspace: no block-to-block hand-off ever gave
+ * up waiting (a bounded wait that is never expected to expire; when it does,
+ * outputs of that call are wrong), and the work counters and the hand-off flags
+ * of the B*H (batch, head) chains are back at zero, as every completed call
+ * leaves them.  Returns SSD_OK when all hold, SSD_ERR_HIP when one does not or
+ * a HIP call failed; clears the expired-wait indicator.  Same shape arguments
+ * as the scan.  Meant for tests and debugging: it synchronizes and copies.
  */
 ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes,
                                           int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,

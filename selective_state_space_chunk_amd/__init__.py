@@ -174,7 +174,8 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
 
 def ssd_chunk_scan_workspace_check(workspace_tensor: torch.Tensor, B: int, L: int, H: int, P: int,
                                    G: int, N: int, chunk_size: int, stream=None) -> None:
-    """Raise if a block-to-block hand-off in this workspace ever gave up waiting."""
+    """Raise unless the one-pass hand-off state in this workspace is clean: no
+    hand-off ever gave up waiting, and the counters and flags are back at zero."""
     lib = load_library()
     nbytes = workspace_tensor.numel() * workspace_tensor.element_size()
     st = lib.ssd_chunk_scan_workspace_check(_ptr(workspace_tensor), nbytes, B, L, H, P, G, N,

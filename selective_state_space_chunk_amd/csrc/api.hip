@@ -3,15 +3,16 @@
 #include "libssd.h"
 #include "common.h"
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 namespace ssd {
 hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws);
 hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws);
 bool mfma_supported(int64_t P, int64_t N, int64_t Q);
-size_t fused_max_chains();
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
-bool fused_supported(int64_t N, int64_t Q);
+bool fused_supported(int64_t H, int64_t G, int64_t N, int64_t Q);
 }
 
 namespace {
@@ -108,10 +109,8 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         return SSD_ERR_UNSUPPORTED;
     const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
     if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED) && !mfma_ok) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_FUSED && !fused_supported(N, Q)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_FUSED && ((size_t)(B * H) > fused_max_chains() ||
-                                   B * H * ((L + Q - 1) / Q) > 0x7fffffff))
-        return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_FUSED && !fused_supported(H, G, N, Q)) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_FUSED && B * H * ((L + Q - 1) / Q) > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
 
     const Layout l = layout(B, L, H, P, G, N, Q);
     if (has_work) {
@@ -139,8 +138,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         } else {
             const int64_t nc = (L + Q - 1) / Q;
             // one pass while chains of blocks are short and many; staged otherwise
-            algo = (nc <= 64 && fused_supported(N, Q) && (size_t)(B * H) <= fused_max_chains() &&
-                    B * H >= 64 && B * H * nc <= 0x7fffffff)
+            algo = (nc <= 64 && fused_supported(H, G, N, Q) && B * H >= 64 && B * H * nc <= 0x7fffffff)
                        ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
         }
     }
@@ -213,6 +211,16 @@ ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_byte
         const unsigned zero = 0;
         if (hipMemcpy(ctr + 2, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SSD_ERR_HIP;
         return SSD_ERR_HIP;
+    }
+    if (host[0] != 0 || host[1] != 0) return SSD_ERR_HIP;
+    const int64_t chains = B * H < kMaxChains ? B * H : kMaxChains;
+    if (chains > 0) {
+        std::vector<unsigned> flags((size_t)chains);
+        if (hipMemcpy(flags.data(), (char *)workspace + l.flags, flags.size() * sizeof(unsigned),
+                      hipMemcpyDeviceToHost) != hipSuccess)
+            return SSD_ERR_HIP;
+        for (unsigned f : flags)
+            if (f != 0) return SSD_ERR_HIP;
     }
     return SSD_OK;
 }

@@ -2,28 +2,41 @@
 //
 // Work items are (block c, batch b, head h) of Q tokens.  An item computes
 //   pass 1: the state its block produces from zero, S_c, sub-block by
-//           sub-block (64 tokens), keeping bf16 snapshots of the block-local
-//           state at every sub-block boundary;
+//           sub-block (64 tokens), keeping bf16 snapshots T of the
+//           block-local state at every sub-block boundary;
 //   hand-off: takes H_c (the state entering the block) from the item of
-//           block c-1 of the same (b, h), hands on H_{c+1} = exp(Lambda_end) H_c + S_c;
-//   pass 2: the outputs of every sub-block from H_c and the snapshots
-//           (the inter-block term Cm . (exp(Lambda_{s-1}) H_c + T) with its
-//           row decay, plus the masked intra-block product, plus D x),
-// which is the block decomposition of the "Mamba-2" note (section "taking each
-// path half way") and of the "Mamba-2 model walkthrough" (sections 6.1-6.2),
-// applied at two levels (blocks of Q, sub-blocks of 64).
+//           block c-1 of the same (b, h) and hands on
+//           H_{c+1} = exp(Lambda_end) H_c + S_c;
+//   pass 2: the outputs of every sub-block: the inter-block term
+//           exp(Lambda_i - Lambda_{s-1}) Cm_i . (exp(Lambda_{s-1}) H_c + T),
+//           the masked intra-block product sum_j M[i][j] x_j, and D x_i;
+// the block decomposition of the "Mamba-2" note (section "taking each path
+// half way") and of the "Mamba-2 model walkthrough" (sections 6.1-6.2),
+// applied at two levels (blocks of Q tokens, sub-blocks of 64).
 //
-// Execution.  A fixed grid of workgroups (two per CU) loops over items taken
-// from a ticket counter in block-major order.  Each item is 2*Q/64 steps (one
-// per sub-block and pass); every step ends in one barrier.  During step s a
-// workgroup computes from LDS buffer s%2, stages step s+1 into the other LDS
-// buffer from registers, and issues the global loads of step s+3 into the
-// register slot it just emptied.  Loads therefore run two to three steps ahead
-// of their use, and the next item's x, Bm, Cm, G and dt stream in while the
-// current item computes.  Tickets are taken three items ahead.  Waiting on a
-// predecessor always ends: the smallest unfinished ticket is always the one a
-// workgroup is processing (a ticket held ahead is larger than the one its
-// holder works on), and its predecessor, with a smaller ticket, is finished.
+// Execution.  A fixed grid of workgroups (two per CU, four waves each) loops
+// over items taken from a ticket counter in block-major order.  An item is
+// 2*Q/64 steps (one per sub-block and pass) and every step ends in one
+// barrier.  During step s a workgroup computes from LDS buffer s%2, stages step
+// s+1 into the other LDS buffer from registers, and issues the global loads of
+// step s+3 into the register slot it just emptied, so loads run two to three
+// steps ahead of their use and the next item's x, Bm, Cm, G, dt, A and D
+// stream in while the current item computes.
+//
+// Every global access in the step loop is an unconditional buffer load or
+// store: the buffer's size (per item, in scalar registers) masks the tail of
+// the sequence and items past the end of the queue (loads outside return 0,
+// stores outside are dropped).  With no conditional memory operations the
+// compiler can wait for exactly the loads a step needs instead of for every
+// load in flight.
+//
+// The hand-off wait and the loads of H_c sit at the end of the last pass-1
+// step, after that step's staging, where the only loads still in flight are
+// the ones the next step stages anyway.  The predecessor's flag is raised one
+// step after H_{c+1} is stored.  Tickets are taken four items ahead.  Waiting
+// on a predecessor always ends: the smallest unfinished ticket is always the
+// one some workgroup is working on (a ticket held ahead is larger than the one
+// its holder works on), and its predecessor, with a smaller ticket, is done.
 #include "common.h"
 
 #include <type_traits>
@@ -34,44 +47,65 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kP = 64;
 constexpr int kSub = 64;
 constexpr int kThreads = 256;
+constexpr int kAhead = 4;                // tickets taken this many items ahead
 constexpr unsigned kSpinLimit = 1u << 22;
-constexpr int TS = kSub + 8;      // row stride of [*][64] bf16 tiles (+16 bytes)
+constexpr int TS = kSub + 8;             // row stride of [*][64] bf16 tiles (+16 bytes)
+constexpr int kRaw = 0x00020000;         // buffer descriptor word 3: raw 32-bit access
+constexpr int kCoherent = 16;            // sc1: device-coherent access
 
 template <int N>
-struct StepBuf {                  // one step's staged operands
+struct StepBuf {                         // one step's staged operands
     static constexpr int RS = N + 8;
-    __bf16 xT[kP * TS];           // x transposed [p][j]
+    __bf16 xT[kP * TS];                  // x transposed [p][j]
     union {
-        __bf16 BwT[N * TS];       // pass 1: weighted Bm transposed [n][j]
+        __bf16 BwT[N * TS];              // pass 1: weighted Bm transposed [n][j]
         struct {
-            __bf16 Cs[kSub * RS]; // pass 2: Cm [i][n]
-            __bf16 Mm[kSub * TS]; // pass 2: masked decay matrix [i][j]
+            __bf16 Cs[kSub * RS];        // pass 2: Cm [i][n]
+            __bf16 Mm[kSub * TS];        // pass 2: masked decay matrix [i][j]; then y [i][p]
         } o;
     } u;
 };
 
-struct Item {               // one work item, uniform across the workgroup
+struct Item {                            // one work item, uniform across the workgroup
     int c, chain, b, h, g, t0, q, valid;
 };
 
 template <int N, int Q>
 struct FSmem {
     StepBuf<N> buf[2];
-    float lam[2][Q];              // per item parity: in-block prefix of dt*A
-    float dts[2][Q];              // per item parity: dt (0 past the end)
-    Item tq[4];                   // decoded ticket queue (item k at tq[k & 3])
+    float lam[2][Q];                     // per item parity: in-block prefix of dt*A
+    float dts[2][Q];                     // per item parity: dt (0 past the end)
+    float Ah[2], Dh[2];                  // per item parity: A_h, D_h
+    Item tq[2 * kAhead];                 // ticket queue (item k at tq[k % (2*kAhead)])
 };
 
 template <int N>
-struct Slot {                     // one step's global data, per thread
-    uint4 x[2];                   // tokens 2tp, 2tp+1, columns 8pg..8pg+7
-    uint4 m[N / 32];              // pass 1: Bm units; pass 2: Cm pieces
-    uint2 g[3];                   // pass 2: this wave's causal G tiles
-    float dt;                     // dt of the next item (carrier steps only)
+struct Slot {                            // one step's global data, per thread
+    uint4 x[2];                          // tokens 2tp, 2tp+1, columns 8pg..8pg+7
+    uint4 m[N / 32];                     // pass 1: Bm units; pass 2: Cm pieces
+    uint2 g[3];                          // pass 2: this wave's causal G tiles
+};
+
+struct Carry {                           // loaded with one step of each item, per thread:
+    float dt, Av, Dv;                    // the next item's dt (token tid), A_h and D_h
+};
+
+struct Args {
+    const __bf16 *x;
+    const float *dt, *A;
+    const __bf16 *Bm, *Cm;
+    const float *D, *init;
+    __bf16 *y;
+    float *final_state;
+    unsigned *flags, *counters;
+    float *ring;
+    const __bf16 *gram;
+    int64_t Bsz, L, H, G;
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -87,19 +121,29 @@ __device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
     it = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
     jt = k - (it * (it + 1)) / 2;
 }
-
-struct Args {
-    const __bf16 *x;
-    const float *dt, *A;
-    const __bf16 *Bm, *Cm;
-    const float *D, *init;
-    __bf16 *y;
-    float *final_state;
-    unsigned *flags, *counters;
-    float *ring;
-    const __bf16 *gram;
-    int64_t Bsz, L, H, G;
-};
+__device__ __forceinline__ rsrc_t rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRaw);
+}
+// (Only the vector and immediate offsets take part in the buffer's range
+// check, so every row offset goes into the vector offset.)
+// The buffer builtins move raw 32-bit words: every value goes in and out
+// through a bit cast (an implicit int <-> float conversion would convert).
+__device__ __forceinline__ uint4 ld16(rsrc_t r, int voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+template <int AUX>
+__device__ __forceinline__ f32x4 ld16f(rsrc_t r, int voff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX));
+}
+__device__ __forceinline__ float ld4f(rsrc_t r, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+template <int AUX, class T>
+__device__ __forceinline__ void st16(T v, rsrc_t r, int voff) {
+    static_assert(sizeof(T) == 16, "16-byte store");
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, AUX);
+}
 
 template <int Q>
 __device__ __forceinline__ Item decode(unsigned t, const Args &a, int64_t nchains, int nc) {
@@ -118,7 +162,7 @@ __device__ __forceinline__ Item decode(unsigned t, const Args &a, int64_t nchain
 
 // An item from the LDS queue, in scalar registers.
 __device__ __forceinline__ Item item_at(const Item *q, int64_t k) {
-    const Item &e = q[k & 3];
+    const Item &e = q[k % (2 * kAhead)];
     Item it;
     it.c = __builtin_amdgcn_readfirstlane(e.c);
     it.chain = __builtin_amdgcn_readfirstlane(e.chain);
@@ -131,51 +175,66 @@ __device__ __forceinline__ Item item_at(const Item *q, int64_t k) {
     return it;
 }
 
-// Global loads of one step (phase < NSB: pass 1 sub-block; else pass 2).
+// Size in bytes of a buffer over the item's rows 0..q-1 (row stride `stride`
+// elements, `width` elements used per row); 0 for an item past the end of the
+// queue, so that all its loads read 0 and its stores are dropped.
+__device__ __forceinline__ int row_bytes(const Item &it, int64_t stride, int width, int esize) {
+    return (it.valid && it.q > 0) ? (int)(((int64_t)(it.q - 1) * stride + width) * esize) : 0;
+}
+
+// Global loads of one step (PHASE < NSB: pass 1 sub-block; else pass 2).
 template <int N, int Q, int PHASE>
-__device__ __forceinline__ void load_step(Slot<N> &sl, const Args &a, const Item &it,
+__device__ __forceinline__ void load_step(Slot<N> &sl, Carry &cr, const Args &a, const Item &it,
                                           const Item &nxt, int64_t nsb, int tid) {
     constexpr int NSB = Q / kSub;
     constexpr bool p1 = PHASE < NSB;
-    constexpr bool carry_dt = PHASE == 2 * NSB - 2;
+    constexpr bool carry = PHASE == 2 * NSB - 2;       // also load the next item's dt, A, D
     constexpr int s = (p1 ? PHASE : PHASE - NSB) * kSub;
     const int wave = tid >> 6, lane = tid & 63;
-    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int64_t row0 = (int64_t)it.b * a.L + it.t0;
     {
         const int pg = tid & 7, tp = tid >> 3, j0 = s + 2 * tp;
-        const __bf16 *p0 = a.x + ((((int64_t)it.b * a.L + it.t0 + j0) * a.H + it.h) * kP + 8 * pg);
-        sl.x[0] = j0 < it.q ? *reinterpret_cast<const uint4 *>(p0) : uint4{0, 0, 0, 0};
-        sl.x[1] = j0 + 1 < it.q ? *reinterpret_cast<const uint4 *>(p0 + a.H * kP) : uint4{0, 0, 0, 0};
+        const rsrc_t rx = rsrc(a.x + (row0 * a.H + it.h) * kP, row_bytes(it, a.H * kP, kP, 2));
+        const int o = (int)(((int64_t)j0 * a.H * kP + 8 * pg) * 2);
+        sl.x[0] = ld16(rx, o);
+        sl.x[1] = ld16(rx, o + (int)(a.H * kP * 2));
     }
     if constexpr (p1) {
+        const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + it.g) * N, row_bytes(it, a.G * N, N, 2));
 #pragma unroll
         for (int k = 0; k < N / 64; ++k) {
             const int u = tid + k * kThreads;
             const int cg = u % (N / 8), tp = u / (N / 8), j0 = s + 2 * tp;
-            const __bf16 *p0 = a.Bm + ((((int64_t)it.b * a.L + it.t0 + j0) * a.G + it.g) * N + 8 * cg);
-            sl.m[2 * k] = j0 < it.q ? *reinterpret_cast<const uint4 *>(p0) : uint4{0, 0, 0, 0};
-            sl.m[2 * k + 1] = j0 + 1 < it.q ? *reinterpret_cast<const uint4 *>(p0 + a.G * N) : uint4{0, 0, 0, 0};
+            const int o = (int)(((int64_t)j0 * a.G * N + 8 * cg) * 2);
+            sl.m[2 * k] = ld16(rb, o);
+            sl.m[2 * k + 1] = ld16(rb, o + (int)(a.G * N * 2));
         }
     } else {
+        const rsrc_t rc = rsrc(a.Cm + (row0 * a.G + it.g) * N, row_bytes(it, a.G * N, N, 2));
 #pragma unroll
         for (int k = 0; k < N / 32; ++k) {
             const int u = tid + k * kThreads;
             const int j = u / (N / 8), cg = u % (N / 8);
-            sl.m[k] = s + j < it.q
-                          ? *reinterpret_cast<const uint4 *>(a.Cm + ((((int64_t)it.b * a.L + it.t0 + s + j) * a.G + it.g) * N + 8 * cg))
-                          : uint4{0, 0, 0, 0};
+            sl.m[k] = ld16(rc, (int)(((int64_t)(s + j) * a.G * N + 8 * cg) * 2));
         }
-        const int64_t sbg = (it.t0 + s) / kSub;
-        const __bf16 *gb = a.gram + (((int64_t)it.b * a.G + it.g) * nsb + sbg) * (int64_t)(kSub * kSub);
+        // this sub-block's G tiles in fragment order; every wave issues three
+        // loads (waves with two tiles load their last one twice)
+        const rsrc_t rg = rsrc(a.gram + (((int64_t)it.b * a.G + it.g) * nsb + it.t0 / kSub) * (kSub * kSub),
+                               it.valid ? NSB * kSub * kSub * 2 : 0);
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
-            const int k = wave + 4 * m;
-            if (k < 10) {
-                sl.g[m] = *reinterpret_cast<const uint2 *>(gb + (k * 64 + lane) * 4);
-            }
+            const int k = wave + 4 * m < 10 ? wave + 4 * m : 9;
+            sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                rg, ((s / kSub) * kSub * kSub + (k * 64 + lane) * 4) * 2, 0, 0));
         }
     }
-    if constexpr (carry_dt) sl.dt = (nxt.valid && tid < nxt.q) ? a.dt[((int64_t)nxt.b * a.L + nxt.t0 + tid) * a.H + nxt.h] : 0.f;
+    if constexpr (carry) {
+        const int64_t nrow0 = (int64_t)nxt.b * a.L + nxt.t0;
+        const rsrc_t rd = rsrc(a.dt + nrow0 * a.H + nxt.h, row_bytes(nxt, a.H, 1, 4));
+        cr.dt = ld4f(rd, (int)((int64_t)tid * a.H * 4));
+        cr.Av = ld4f(rsrc(a.A + nxt.h, nxt.valid ? 4 : 0), 0);
+        cr.Dv = ld4f(rsrc(a.D + nxt.h, nxt.valid ? 4 : 0), 0);
+    }
 }
 
 // Stage one step's operands from registers into an LDS buffer.
@@ -223,6 +282,7 @@ __device__ __forceinline__ void stage_step(StepBuf<N> &bf, const Slot<N> &sl, co
             const int j = u / (N / 8), cg = u % (N / 8);
             *reinterpret_cast<uint4 *>(&bf.u.o.Cs[j * B::RS + 8 * cg]) = sl.m[k];
         }
+        // masked decay matrix from this wave's G tiles
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
             const int k = wave + 4 * m;
@@ -246,10 +306,56 @@ __device__ __forceinline__ void stage_step(StepBuf<N> &bf, const Slot<N> &sl, co
             }
         }
         if (wave >= 2) {
+            // the tiles above the diagonal that the apply reads: (0,1) and (2,3)
             const int ti = wave == 2 ? 0 : 2;
-            *reinterpret_cast<uint2 *>(&bf.u.o.Mm[(16 * ti + lrow) * TS + 16 * (ti + 1) + 4 * lgrp]) = uint2{0u, 0u};
+            uint32_t z = 0;
+            asm volatile("" : "+v"(z));   // made here, not held in a register across the loop
+            *reinterpret_cast<uint2 *>(&bf.u.o.Mm[(16 * ti + lrow) * TS + 16 * (ti + 1) + 4 * lgrp]) = uint2{z, z};
         }
     }
+}
+
+// In-block inclusive prefix sums of dt*A (one wave, 64 values per round).
+// The lane permutes take their addresses from `lane` (not from the hardware
+// lane id) so that they are computed here rather than held across the loop.
+template <int Q>
+__device__ __forceinline__ void prefix(const float *dts, float *lam, float Ah, int lane) {
+    float carry = 0.f;
+#pragma unroll
+    for (int base = 0; base < Q; base += 64) {
+        float v = dts[base + lane] * Ah;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane - off) & 63) << 2, __float_as_int(v)));
+            if (lane >= off) v += o;
+        }
+        v += carry;
+        lam[base + lane] = v;
+        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    }
+}
+
+// Vector memory operations each thread issues in the step loop at phase ph:
+// the loads of step ph (x, then Bm or Cm, then in pass 2 the G tiles, and on
+// the carrier step dt, A and D) and, in pass 2, two stores of y.
+template <int N, int Q>
+constexpr int loads_of(int ph) {
+    return 2 + N / 32 + (ph >= Q / kSub ? 3 : 0) + (ph == 2 * (Q / kSub) - 2 ? 3 : 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `v` vector
+// memory operations are outstanding and does not wait on the other counters.
+constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The hand-off stores are issued at phase NSB; vector memory operations
+// complete in issue order, so at the raise point they are complete once no
+// more are outstanding than were issued after them: the two y stores of
+// phase NSB and, when the flag goes up one step later, the loads issued at
+// phase NSB (those of phase NSB+3) and the two y stores of phase NSB+1.
+template <int N, int Q>
+constexpr int raise_wait_count() {
+    constexpr int NSB = Q / kSub, STEPS = 2 * NSB;
+    return NSB + 1 < STEPS ? 2 + loads_of<N, Q>((NSB + 3) % STEPS) + 2 : 2;
 }
 
 template <int N, int Q>
@@ -260,75 +366,64 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
     constexpr int NT = N / 16;
     constexpr int NSB = Q / kSub;
     constexpr int STEPS = 2 * NSB;
-    constexpr int RAISE = NSB + 1 < STEPS ? NSB + 1 : NSB;   // step of the hand-off flag
+    constexpr int RAISE = NSB + 1 < STEPS ? NSB + 1 : NSB;   // step that raises the hand-off flag
+    constexpr auto raise_wait = [] { return vmcnt_imm(raise_wait_count<N, Q>()); };
     using BF = StepBuf<N>;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int lrow = lane & 15, lgrp = lane >> 4;
     const int64_t nchains = a.Bsz * a.H;
     const int nc = (int)((a.L + Q - 1) / Q);
     const int64_t nsb = (int64_t)nc * NSB;
-    const int64_t lane_off = (int64_t)(16 * wave + lrow) * N + 4 * lgrp;   // state layout, floats
 
-    if (tid == 0) {
-        for (int k = 0; k < 3; ++k) sm.tq[k] = decode<Q>(atomicAdd(&a.counters[0], 1u), a, nchains, nc);
+    if (threadIdx.x == 0) {
+        for (int k = 0; k < kAhead; ++k) sm.tq[k] = decode<Q>(atomicAdd(&a.counters[0], 1u), a, nchains, nc);
     }
     __syncthreads();
     Item cur = item_at(sm.tq, 0);
     if (cur.valid) {
-        // first item's prefix sums
-        const float d0 = tid < cur.q ? a.dt[((int64_t)cur.b * a.L + cur.t0 + tid) * a.H + cur.h] : 0.f;
-        if (tid < Q) sm.dts[0][tid] = d0;
-        __syncthreads();
-        if (wave == 0) {
-            const float Ah = a.A[cur.h];
-            float carry = 0.f;
-#pragma unroll
-            for (int base = 0; base < Q; base += 64) {
-                float v = sm.dts[0][base + lane] * Ah;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float o = __shfl_up(v, off);
-                    if (lane >= off) v += o;
-                }
-                v += carry;
-                sm.lam[0][base + lane] = v;
-                carry = __shfl(v, 63);
+        {
+            // the first item's dt, A, D and prefix sums
+            const int tid = threadIdx.x;
+            const float d0 = tid < cur.q ? a.dt[((int64_t)cur.b * a.L + cur.t0 + tid) * a.H + cur.h] : 0.f;
+            if (tid < Q) sm.dts[0][tid] = d0;
+            if (tid == 0) {
+                sm.Ah[0] = a.A[cur.h];
+                sm.Dh[0] = a.D[cur.h];
             }
+            __syncthreads();
+            if (tid < 64) prefix<Q>(sm.dts[0], sm.lam[0], sm.Ah[0], tid);
+            __syncthreads();
         }
-        __syncthreads();
 
         // prologue: steps 0 and 1 into the slots, stage step 0, step 2 into slot 0.
         // Step t belongs to item t / STEPS and has phase t % STEPS.
         Slot<N> slot[2];
+        Carry carry;
         {
-            const Item i0 = item_at(sm.tq, 0);
-            const Item i1 = item_at(sm.tq, 1 / STEPS);
-            const Item i2 = item_at(sm.tq, 2 / STEPS);
-            const Item n0 = item_at(sm.tq, 0 / STEPS + 1);
-            const Item n1 = item_at(sm.tq, 1 / STEPS + 1);
-            const Item n2 = item_at(sm.tq, 2 / STEPS + 1);
-            load_step<N, Q, 0>(slot[0], a, i0, n0, nsb, threadIdx.x);
-            if (i1.valid) load_step<N, Q, 1 % STEPS>(slot[1], a, i1, n1, nsb, threadIdx.x);
-            stage_step<N, Q, 0>(sm.buf[0], slot[0], sm.lam[0], sm.dts[0], threadIdx.x);
-            if constexpr (STEPS == 2) {   // step 0 carries the next item's dt
-                if (tid < Q) sm.dts[1][tid] = slot[0].dt;
+            const int tid = threadIdx.x;
+            load_step<N, Q, 0>(slot[0], carry, a, cur, item_at(sm.tq, 1), nsb, tid);
+            load_step<N, Q, 1 % STEPS>(slot[1], carry, a, item_at(sm.tq, 1 / STEPS),
+                                       item_at(sm.tq, 1 / STEPS + 1), nsb, tid);
+            stage_step<N, Q, 0>(sm.buf[0], slot[0], sm.lam[0], sm.dts[0], tid);
+            if constexpr (STEPS == 2) {   // step 0 carries the next item's dt, A, D
+                if (tid < Q) sm.dts[1][tid] = carry.dt;
+                if (tid == 0) {
+                    sm.Ah[1] = carry.Av;
+                    sm.Dh[1] = carry.Dv;
+                }
             }
-            if (i2.valid) load_step<N, Q, 2 % STEPS>(slot[0], a, i2, n2, nsb, threadIdx.x);
+            load_step<N, Q, 2 % STEPS>(slot[0], carry, a, item_at(sm.tq, 2 / STEPS),
+                                       item_at(sm.tq, 2 / STEPS + 1), nsb, tid);
         }
         __syncthreads();
 
-        f32x4 Hacc[NT];
+        f32x4 Hacc[NT];                  // pass 1: S_c; pass 2: H_c
+        f32x4 Hin[NT];                   // H_c from the last pass-1 step to the hand-off
         uint32_t Ts[NSB > 1 ? NSB - 1 : 1][2 * NT];
-        bool raise_pending = false;
-        unsigned raise_value = 0;
-        int raise_chain = 0;
+        unsigned ticket = 0;
 
-        // One step of item k at compile-time phase PH.  `sl` is the register
-        // slot of steps s+1 (staged now) and s+3 (loaded now).  Returns false
-        // when item k is not a valid work item (the queue ran out).
-        auto step = [&](auto phc, int64_t k, Slot<N> &sl) -> bool {
+        // One step of item k (`cur`) at compile-time phase PH.  `sl` is the
+        // register slot of steps s+1 (staged now) and s+3 (loaded now).
+        auto step = [&](auto phc, int64_t k, Slot<N> &sl) {
             constexpr int ph = decltype(phc)::value;
             // The lane id is made opaque to the optimizer at every step so that
             // addresses derived from it are recomputed here instead of being
@@ -338,14 +433,15 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
             asm volatile("" : "+v"(tid));
             const int wave = tid >> 6, lane = tid & 63;
             const int lrow = lane & 15, lgrp = lane >> 4;
-            const int64_t lane_off = (int64_t)(16 * wave + lrow) * N + 4 * lgrp;
+            const int lane_off = (16 * wave + lrow) * N + 4 * lgrp;   // state layout, floats
             const int par = (int)(k & 1);
-            cur = item_at(sm.tq, k);
-            if (!cur.valid) return false;
-            if (ph == 0 && tid == 0) sm.tq[(k + 3) & 3] = decode<Q>(atomicAdd(&a.counters[0], 1u), a, nchains, nc);
+            if constexpr (ph == 0) {
+                if (tid == 0) ticket = atomicAdd(&a.counters[0], 1u);   // item k + kAhead
+            }
             const float *lam = sm.lam[par];
             const float *dts = sm.dts[par];
             const BF &bf = sm.buf[ph & 1];
+            const int64_t row0 = (int64_t)cur.b * a.L + cur.t0;
 
             if constexpr (ph < NSB) {
                 // ---- pass 1: block-local state, sub-block ph
@@ -379,57 +475,23 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
                 constexpr int sbi = ph - NSB;
                 constexpr int sbs = sbi * kSub;
                 if constexpr (ph == NSB) {
-                    // ---- hand-off: H_c in, H_{c+1} = gamma H_c + S_c out
+                    // ---- hand-off out: H_{c+1} = gamma H_c + S_c to the
+                    // successor's ring slot (device-coherent: another CU reads
+                    // it in this launch), or to the final state (read by later
+                    // launches only).  Both branches store the same count.
                     const float gamma = __expf(lam[Q - 1]);
-                    f32x4 Hin[NT];
-                    if (cur.c == 0) {
-                        if (a.init) {
-                            const float *src = a.init + (int64_t)cur.chain * (kP * N) + lane_off;
-#pragma unroll
-                            for (int t = 0; t < NT; ++t) Hin[t] = *reinterpret_cast<const f32x4 *>(src + 16 * t);
-                        } else {
-#pragma unroll
-                            for (int t = 0; t < NT; ++t) Hin[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    } else {
-                        if (tid == 0) {
-                            unsigned spins = 0;
-                            while (__hip_atomic_load(&a.flags[cur.chain], __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT) < (unsigned)cur.c) {
-                                __builtin_amdgcn_s_sleep(1);
-                                if (++spins > kSpinLimit) {
-                                    atomicOr(&a.counters[2], 1u);
-                                    break;
-                                }
-                            }
-                            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                        }
-                        __syncthreads();
-                        // device-coherent 16-byte loads (sc1): written by another CU
-                        const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-                            a.ring + ((int64_t)cur.chain * 2 + (cur.c & 1)) * (kP * N), 0, kP * N * 4, 0x00020000);
-#pragma unroll
-                        for (int t = 0; t < NT; ++t)
-                            Hin[t] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)((lane_off + 16 * t) * 4), 0, 16);
-                    }
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) Hacc[t] = gamma * Hin[t] + Hacc[t];
                     if (cur.c + 1 < nc) {
-                        const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
-                            a.ring + ((int64_t)cur.chain * 2 + ((cur.c + 1) & 1)) * (kP * N), 0, kP * N * 4, 0x00020000);
+                        const rsrc_t rd = rsrc(a.ring + ((int64_t)cur.chain * 2 + ((cur.c + 1) & 1)) * (kP * N),
+                                               kP * N * 4);
 #pragma unroll
                         for (int t = 0; t < NT; ++t)
-                            __builtin_amdgcn_raw_buffer_store_b128(Hacc[t], dst, (int)((lane_off + 16 * t) * 4), 0, 16);
-                        raise_pending = true;
-                        raise_value = (unsigned)(cur.c + 1);
-                        raise_chain = cur.chain;
+                            st16<kCoherent>(gamma * Hin[t] + Hacc[t], rd, (lane_off + 16 * t) * 4);
                     } else {
-                        if (a.final_state) {
-                            float *dst = a.final_state + (int64_t)cur.chain * (kP * N) + lane_off;
+                        const rsrc_t rd = rsrc(a.final_state ? a.final_state + (int64_t)cur.chain * (kP * N) : a.ring,
+                                               a.final_state ? kP * N * 4 : 0);
 #pragma unroll
-                            for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t) = Hacc[t];
-                        }
-                        if (tid == 0) a.flags[cur.chain] = 0u;   // last user of this chain's flag
+                        for (int t = 0; t < NT; ++t)
+                            st16<0>(gamma * Hin[t] + Hacc[t], rd, (lane_off + 16 * t) * 4);
                     }
 #pragma unroll
                     for (int t = 0; t < NT; ++t) Hacc[t] = Hin[t];
@@ -479,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
                 // skip term; the sub-block's outputs go through LDS (the mask
                 // region, free once every wave is past the apply) so that they
                 // leave as whole 128-byte rows
-                const float Dh = a.D[cur.h];
+                const float Dh = sm.Dh[par];
                 __syncthreads();
                 __bf16 *ys = const_cast<__bf16 *>(bf.u.o.Mm);           // [i][p], row stride TS
 #pragma unroll
@@ -495,14 +557,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
                     *reinterpret_cast<uint2 *>(&ys[i * TS + p0]) = pk;
                 }
                 __syncthreads();
+                const rsrc_t ry = rsrc(a.y + (row0 * a.H + cur.h) * kP, row_bytes(cur, a.H * kP, kP, 2));
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const int u = tid + r * kThreads;                   // 512 pieces of 16 bytes
                     const int i = u >> 3, pc = u & 7;                  // token row, 8-column piece
-                    if (sbs + i < cur.q) {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(&ys[i * TS + 8 * pc]);
-                        *reinterpret_cast<uint4 *>(a.y + ((((int64_t)cur.b * a.L + cur.t0 + sbs + i) * a.H + cur.h) * kP + 8 * pc)) = v;
-                    }
+                    const uint4 v = *reinterpret_cast<const uint4 *>(&ys[i * TS + 8 * pc]);
+                    st16<0>(v, ry, (int)(((int64_t)(sbs + i) * a.H * kP + 8 * pc) * 2));
                 }
             }
 
@@ -515,53 +576,82 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
                     const int par1 = (int)(k1 & 1);
                     stage_step<N, Q, ph1>(sm.buf[(ph + 1) & 1], sl, sm.lam[par1], sm.dts[par1], tid);
                     if constexpr (ph1 == STEPS - 2) {
-                        if (tid < Q) sm.dts[par1 ^ 1][tid] = sl.dt;
-                    }
-                }
-            }
-            // ---- prefix sums of the next item (its dt reached LDS one step ago)
-            if constexpr (ph == STEPS - 2) {
-                if (wave == 0) {
-                    const Item nx = item_at(sm.tq, k + 1);
-                    if (nx.valid) {
-                        const float Ah = a.A[nx.h];
-                        float carry = 0.f;
-#pragma unroll
-                        for (int base = 0; base < Q; base += 64) {
-                            float v = sm.dts[par ^ 1][base + lane] * Ah;
-#pragma unroll
-                            for (int off = 1; off < 64; off <<= 1) {
-                                const float o = __shfl_up(v, off);
-                                if (lane >= off) v += o;
-                            }
-                            v += carry;
-                            sm.lam[par ^ 1][base + lane] = v;
-                            carry = __shfl(v, 63);
+                        // that step's slot carries the next item's dt, A, D
+                        if (tid < Q) sm.dts[par1 ^ 1][tid] = carry.dt;
+                        if (tid == 0) {
+                            sm.Ah[par1 ^ 1] = carry.Av;
+                            sm.Dh[par1 ^ 1] = carry.Dv;
                         }
                     }
                 }
             }
-            constexpr bool raise_step = ph == RAISE;
-            const bool raise_now = raise_step && raise_pending;
-            if (raise_now) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // hand-off stores done
+            // ---- prefix sums of the next item (its dt and A reached LDS one step ago)
+            if constexpr (ph == STEPS - 2) {
+                if (wave == 0) {
+                    const Item nx = item_at(sm.tq, k + 1);
+                    if (nx.valid) prefix<Q>(sm.dts[par ^ 1], sm.lam[par ^ 1], sm.Ah[par ^ 1], lane);
+                }
+            }
+            // ---- the ticket taken at phase 0 goes into the queue
+            if constexpr (ph == 1 % STEPS) {
+                if (tid == 0) sm.tq[(k + kAhead) % (2 * kAhead)] = decode<Q>(ticket, a, nchains, nc);
+            }
+            // ---- hand-off in: wait for the predecessor's flag, then load H_c
+            // (its ring slot, the initial state, or zeros from an empty buffer)
+            if constexpr (ph == NSB - 1) {
+                if (cur.c > 0) {
+                    if (tid == 0) {
+                        unsigned spins = 0;
+                        while (__hip_atomic_load(&a.flags[cur.chain], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) < (unsigned)cur.c) {
+                            __builtin_amdgcn_s_sleep(1);
+                            if (++spins > kSpinLimit) {   // never expected: record it and go on
+                                atomicOr(&a.counters[2], 1u);
+                                break;
+                            }
+                        }
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    }
+                    __syncthreads();
+                }
+                // The ring slot was written in this launch by another CU: a
+                // device-coherent load.  The initial state was written before
+                // the launch: an ordinary load (a device-coherent one need not
+                // see what an earlier kernel left in another L2).  Both
+                // branches load the same count.
+                if (cur.c > 0) {
+                    const rsrc_t rs = rsrc(a.ring + ((int64_t)cur.chain * 2 + (cur.c & 1)) * (kP * N), kP * N * 4);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        Hin[t] = ld16f<kCoherent>(rs, (lane_off + 16 * t) * 4);
+                } else {
+                    const rsrc_t rs = rsrc(a.init ? a.init + (int64_t)cur.chain * (kP * N) : a.ring,
+                                           a.init ? kP * N * 4 : 0);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        Hin[t] = ld16f<0>(rs, (lane_off + 16 * t) * 4);
+                }
+            }
+            // ---- raise the flag for the successor (the last block clears it
+            // for the next launch).  Every wave first sees its stores of
+            // H_{c+1} complete; after the barrier one lane publishes with
+            // release semantics (L2 write-back, then the flag), before this
+            // step's loads are issued so that the release waits only for
+            // loads issued a step ago.
+            if constexpr (ph == RAISE) {
+                __builtin_amdgcn_s_waitcnt(raise_wait());
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(&a.flags[cur.chain], cur.c + 1 < nc ? (unsigned)(cur.c + 1) : 0u,
+                                       __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
             // ---- issue the loads of step s+3 (item k3, phase ph3)
             {
                 constexpr int ph3 = (ph + 3) % STEPS;
                 const int64_t k3 = k + (ph + 3) / STEPS;
-                const Item it3 = item_at(sm.tq, k3);
-                if (it3.valid) {
-                    const Item nxt = item_at(sm.tq, k3 + 1);
-                    load_step<N, Q, ph3>(sl, a, it3, nxt, nsb, tid);
-                }
+                load_step<N, Q, ph3>(sl, carry, a, item_at(sm.tq, k3), item_at(sm.tq, k3 + 1), nsb, tid);
             }
             __syncthreads();
-            if (raise_now) {
-                if (tid == 0)
-                    __hip_atomic_store(&a.flags[raise_chain], raise_value, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                raise_pending = false;
-            }
-            return true;
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
@@ -571,23 +661,26 @@ __global__ __launch_bounds__(kThreads, 2) void scan_fused(Args a) {
         using I5 = std::integral_constant<int, 5 % STEPS>;
         using I6 = std::integral_constant<int, 6 % STEPS>;
         using I7 = std::integral_constant<int, 7 % STEPS>;
+        // every step of an item is valid or none is: one check per item
         for (int64_t k = 0;; ++k) {
-            if (!step(I0{}, k, slot[1])) break;
-            if (!step(I1{}, k, slot[0])) break;
+            cur = item_at(sm.tq, k);
+            if (!cur.valid) break;
+            step(I0{}, k, slot[1]);
+            step(I1{}, k, slot[0]);
             if constexpr (STEPS > 2) {
-                if (!step(I2{}, k, slot[1])) break;
-                if (!step(I3{}, k, slot[0])) break;
+                step(I2{}, k, slot[1]);
+                step(I3{}, k, slot[0]);
             }
             if constexpr (STEPS > 4) {
-                if (!step(I4{}, k, slot[1])) break;
-                if (!step(I5{}, k, slot[0])) break;
-                if (!step(I6{}, k, slot[1])) break;
-                if (!step(I7{}, k, slot[0])) break;
+                step(I4{}, k, slot[1]);
+                step(I5{}, k, slot[0]);
+                step(I6{}, k, slot[1]);
+                step(I7{}, k, slot[0]);
             }
         }
     }
     // leave: the last workgroup out resets the counters for the next launch
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         const unsigned out = atomicAdd(&a.counters[1], 1u);
         if (out + 1 == gridDim.x) {
             __hip_atomic_store(&a.counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -633,8 +726,12 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
 
 }  // namespace
 
-bool fused_supported(int64_t N, int64_t Q) {
-    return (N == 64 || N == 128) && (Q == 64 || Q == 128 || Q == 256);
+// Shapes the one-pass kernel takes: N and Q it is built for, and a block's rows
+// of x, Bm, Cm and dt within the 2^31-byte reach of a buffer offset.
+bool fused_supported(int64_t H, int64_t G, int64_t N, int64_t Q) {
+    if (!((N == 64 || N == 128) && (Q == 64 || Q == 128 || Q == 256))) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    return Q * H * kP * 2 < lim && Q * G * N * 2 < lim && Q * H * 4 < lim;
 }
 
 hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws) {

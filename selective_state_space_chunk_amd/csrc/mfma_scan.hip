@@ -32,19 +32,12 @@
 // into registers while the current one computes (Bm, Cm and G are shared by
 // all heads of a group and mostly hit in L2).
 //
-// Three modes share this code:
+// Two modes share this code, with the state pass (a short kernel over the
+// blocks of every (b, h)) between them:
 //   kState   the state each block produces from zero (its "chunk state") and
 //            its total decay, written to the workspace;
 //   kOutput  the outputs of each block from the state entering it (read from
-//            the workspace, where the pass kernel put it);
-//   kFused   both in one launch: a block computes its own state, takes the
-//            state entering it from its predecessor's workgroup, hands the
-//            state leaving it to its successor, then computes its outputs.
-//            Workgroups take tickets from a counter in block-major order, so
-//            the predecessor of ticket t holds ticket t - (B*H) and has
-//            already started: waiting on it always ends.  States are handed
-//            over through a two-slot ring per (b, h) and a flag counting the
-//            blocks published.
+//            the workspace, where the pass kernel put it).
 #include "common.h"
 
 namespace ssd {
@@ -57,9 +50,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kP = 64;        // head dimension handled by the matrix-core path
 constexpr int kSub = 64;      // tokens per sub-block
 constexpr int kThreads = 256;
-constexpr unsigned kSpinLimit = 1u << 22;   // hand-off polls before giving up
 
-enum Mode { kState = 0, kOutput = 1, kFused = 2 };
+enum Mode { kState = 0, kOutput = 1 };
 
 template <int N, int Q>
 struct Smem {
@@ -73,7 +65,6 @@ struct Smem {
     float dts[Q];                         // dt in the block (0 past the end)
     float wsub[Q];                        // exp(lam[e] - lam[j]) dt_j, e = end of j's sub-block
     float rdec[Q];                        // exp(lam[i] - lam[s - 1]), s = start of i's sub-block
-    unsigned ticket;
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -310,41 +301,19 @@ template <int N, int Q, int MODE>
 __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     const __bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm, const float *__restrict__ D,
-    const float *init, __bf16 *__restrict__ y, float *final_state, float *states,
-    float *decay, unsigned *flags, unsigned *counters, float *ring, const __bf16 *gram,
-    int64_t Bsz, int64_t L, int64_t H, int64_t G) {
+    __bf16 *__restrict__ y, float *states, float *decay, const __bf16 *gram,
+    int64_t L, int64_t H, int64_t G) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     using S = Smem<N, Q>;
     S &sm = *reinterpret_cast<S *>(smem_raw);
     constexpr int NT = N / 16;
     constexpr int NSB = Q / kSub;
-    // One pass keeps bf16 snapshots of the block-local state at every
-    // sub-block boundary, so its output pass needs no state recurrence.
-    constexpr bool kSnap = MODE == kFused;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lrow = lane & 15, lgrp = lane >> 4;
-    const int64_t nchains = Bsz * H;
     const int nc = (int)((L + Q - 1) / Q);
-
-    int64_t c, chain;
-    if (MODE == kFused) {
-        if (tid == 0) sm.ticket = atomicAdd(&counters[0], 1u);
-        __syncthreads();
-        const int64_t t = sm.ticket;
-        if (t >= nchains * nc) {
-            // counters were not zero at launch (workspace not zero-filled):
-            // record it and do nothing; no index below is ever formed from t
-            if (tid == 0) atomicOr(&counters[2], 2u);
-            return;
-        }
-        c = t / nchains;
-        chain = t % nchains;
-    } else {
-        c = blockIdx.x;
-        chain = blockIdx.y;
-    }
+    const int64_t c = blockIdx.x, chain = blockIdx.y;
     Ctx cx;
     cx.x = x; cx.Bm = Bm; cx.Cm = Cm; cx.gram = gram;
     cx.b = chain / H; cx.h = chain % H; cx.g = cx.h / (H / G);
@@ -357,7 +326,7 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     uint4 xr[2 * NSB];
     load_x<NSB>(xr, cx);
     SubRegs<N> r;
-    load_sub<N>(r, cx, 0, MODE != kOutput || !kSnap, MODE == kOutput);
+    load_sub<N>(r, cx, 0, true, MODE == kOutput);
 
     // in-block prefix sums of dt*A (first wave), then per-token weights and decays
     if (tid < Q) sm.dts[tid] = dtv;
@@ -389,10 +358,9 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     __syncthreads();
 
     f32x4 Hacc[NT];
-    uint32_t Ts[NSB > 1 ? NSB - 1 : 1][2 * NT];   // bf16 snapshots (one pass only)
     const int64_t state_off = ((cx.b * nc + c) * H + cx.h) * (int64_t)(kP * N);
 
-    if (MODE == kState || MODE == kFused) {
+    if (MODE == kState) {
         // the block's own state, from zero
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -401,82 +369,18 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
             const int s = sb * kSub;
             if (s >= q) break;
             stage<N, Q, true, false>(sm, r, xr[2 * sb], xr[2 * sb + 1], s);
-            if (sb + 1 < NSB && s + kSub < q)
-                load_sub<N>(r, cx, s + kSub, true, false);
-            else if (MODE == kFused)
-                load_sub<N>(r, cx, 0, false, true);   // first sub-block of the output pass
+            if (sb + 1 < NSB && s + kSub < q) load_sub<N>(r, cx, s + kSub, true, false);
             __syncthreads();
             const float before = s == 0 ? 0.f : sm.lam[s - 1];
             scale_state<N>(Hacc, __expf(sm.lam[s + kSub - 1] - before));
             state_update<N, Q>(Hacc, sm, wave, lrow, lgrp);
-            if (kSnap && sb + 1 < NSB) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    Ts[sb][2 * t] = pack2(Hacc[t][0], Hacc[t][1]);
-                    Ts[sb][2 * t + 1] = pack2(Hacc[t][2], Hacc[t][3]);
-                }
-            }
             __syncthreads();
         }
-        const float gamma = __expf(sm.lam[Q - 1]);
-        if (MODE == kState) {
-            store_state<N>(Hacc, states + state_off, wave, lrow, lgrp);
-            if (tid == 0) decay[chain * nc + c] = gamma;
-            return;
-        }
-        // take the entering state H_c, hand on H_{c+1} = gamma H_c + S_c
-        const int64_t lane_off = (int64_t)(16 * wave + lrow) * N + 4 * lgrp;   // floats
-        f32x4 Hin[NT];
-        if (c == 0) {
-            if (init) {
-                load_state<N>(Hin, init + chain * (int64_t)(kP * N), wave, lrow, lgrp);
-            } else {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) Hin[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        } else {
-            if (tid == 0) {
-                unsigned spins = 0;
-                while (__hip_atomic_load(&flags[chain], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       (unsigned)c) {
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++spins > kSpinLimit) {       // never expected: record and go on
-                        atomicOr(&counters[2], 1u);
-                        break;
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            }
-            __syncthreads();
-            // device-coherent 16-byte loads (sc1): the state was written by another CU
-            const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-                ring + (chain * 2 + (c & 1)) * (int64_t)(kP * N), 0, kP * N * 4, 0x00020000);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                Hin[t] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)((lane_off + 16 * t) * 4), 0, 16);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) Hacc[t] = gamma * Hin[t] + Hacc[t];
-        if (c + 1 < nc) {
-            const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
-                ring + (chain * 2 + ((c + 1) & 1)) * (int64_t)(kP * N), 0, kP * N * 4, 0x00020000);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                __builtin_amdgcn_raw_buffer_store_b128(Hacc[t], dst, (int)((lane_off + 16 * t) * 4), 0, 16);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's hand-off stores done
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_store(&flags[chain], (unsigned)(c + 1), __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            if (final_state) store_state<N>(Hacc, final_state + chain * (int64_t)(kP * N), wave, lrow, lgrp);
-            if (tid == 0) flags[chain] = 0u;      // last user of this chain's flag: leave it zero
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) Hacc[t] = Hin[t];
-    } else {
-        load_state<N>(Hacc, states + state_off, wave, lrow, lgrp);
+        store_state<N>(Hacc, states + state_off, wave, lrow, lgrp);
+        if (tid == 0) decay[chain * nc + c] = __expf(sm.lam[Q - 1]);
+        return;
     }
+    load_state<N>(Hacc, states + state_off, wave, lrow, lgrp);
 
     // outputs of the block from the entering state
     const float Dh = D[cx.h];
@@ -484,24 +388,18 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     for (int sb = 0; sb < NSB; ++sb) {
         const int s = sb * kSub;
         if (s >= q) break;
-        stage<N, Q, !kSnap, true>(sm, r, xr[2 * sb], xr[2 * sb + 1], s);
-        if (sb + 1 < NSB && s + kSub < q) load_sub<N>(r, cx, s + kSub, !kSnap, true);
+        stage<N, Q, true, true>(sm, r, xr[2 * sb], xr[2 * sb + 1], s);
+        if (sb + 1 < NSB && s + kSub < q) load_sub<N>(r, cx, s + kSub, true, true);
         __syncthreads();
 
         // inter-block part: Y^T[p][i] = sum_n H[p][n] Cm_i[n], with H the state
         // entering the sub-block, then the row decay exp(lam_i - lam_{s-1})
-        const float eb = kSnap ? (s == 0 ? 1.f : __expf(sm.lam[s - 1])) : 1.f;
         f32x4 Y[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) Y[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) {
-            f32x4 h0 = Hacc[2 * ks], h1 = Hacc[2 * ks + 1];
-            if (kSnap && sb > 0) {
-                const uint32_t *tw = &Ts[sb > 0 ? sb - 1 : 0][4 * ks];
-                h0 = eb * h0 + f32x4{lo_bf16(tw[0]), hi_bf16(tw[0]), lo_bf16(tw[1]), hi_bf16(tw[1])};
-                h1 = eb * h1 + f32x4{lo_bf16(tw[2]), hi_bf16(tw[2]), lo_bf16(tw[3]), hi_bf16(tw[3])};
-            }
+            const f32x4 h0 = Hacc[2 * ks], h1 = Hacc[2 * ks + 1];
             bf16x8 ah;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -548,20 +446,12 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
                 *reinterpret_cast<uint2 *>(y + (((cx.b * L + cx.t0 + s + i) * H + cx.h) * kP + p0)) = pk;
             }
         }
-        if (!kSnap && sb + 1 < NSB && s + kSub < q) {
+        if (sb + 1 < NSB && s + kSub < q) {
             const float before = s == 0 ? 0.f : sm.lam[s - 1];
             scale_state<N>(Hacc, __expf(sm.lam[s + kSub - 1] - before));
             state_update<N, Q>(Hacc, sm, wave, lrow, lgrp);
         }
         __syncthreads();
-    }
-
-    if (MODE == kFused && tid == 0) {
-        const unsigned done = atomicAdd(&counters[1], 1u);
-        if (done + 1 == (unsigned)(nchains * nc)) {   // last workgroup: reset for the next launch
-            __hip_atomic_store(&counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&counters[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 }
 
@@ -577,21 +467,19 @@ hipError_t launch_mode(const ScanArgs &a, const Workspace &ws, dim3 grid) {
         configured = true;
     }
     kern<<<grid, kThreads, smem, a.stream>>>(
-        (const __bf16 *)a.x, a.dt, a.A, (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, a.D, a.init,
-        (__bf16 *)a.y, a.final_state, ws.states, ws.decay, ws.flags, ws.counters, ws.ring,
-        (const __bf16 *)ws.gram, a.B, a.L, a.H, a.G);
+        (const __bf16 *)a.x, a.dt, a.A, (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, a.D,
+        (__bf16 *)a.y, ws.states, ws.decay, (const __bf16 *)ws.gram, a.L, a.H, a.G);
     return hipGetLastError();
 }
 
 template <int N, int Q>
-hipError_t run(const ScanArgs &a, const Workspace &ws, bool fused) {
+hipError_t run(const ScanArgs &a, const Workspace &ws) {
     const int nc = (int)((a.L + Q - 1) / Q);
     const int64_t nsb = (int64_t)nc * (Q / kSub);
     gram_kernel<N><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
         (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (fused) return launch_mode<N, Q, kFused>(a, ws, dim3((unsigned)(nc * a.B * a.H)));
     e = launch_mode<N, Q, kState>(a, ws, dim3((unsigned)nc, (unsigned)(a.B * a.H)));
     if (e != hipSuccess) return e;
     e = launch_state_pass(ws.states, ws.decay, a.init, a.final_state, a.B, a.H, kP * N, nc, a.stream);
@@ -600,20 +488,20 @@ hipError_t run(const ScanArgs &a, const Workspace &ws, bool fused) {
 }
 
 template <int N>
-hipError_t run_q(const ScanArgs &a, const Workspace &ws, bool fused) {
+hipError_t run_q(const ScanArgs &a, const Workspace &ws) {
     switch (a.Q) {
-        case 64: return run<N, 64>(a, ws, fused);
-        case 128: return run<N, 128>(a, ws, fused);
-        case 256: return run<N, 256>(a, ws, fused);
+        case 64: return run<N, 64>(a, ws);
+        case 128: return run<N, 128>(a, ws);
+        case 256: return run<N, 256>(a, ws);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t dispatch(const ScanArgs &a, const Workspace &ws, bool fused) {
+hipError_t dispatch(const ScanArgs &a, const Workspace &ws) {
     switch (a.N) {
-        case 64: return run_q<64>(a, ws, fused);
-        case 128: return run_q<128>(a, ws, fused);
-        case 256: return run_q<256>(a, ws, fused);
+        case 64: return run_q<64>(a, ws);
+        case 128: return run_q<128>(a, ws);
+        case 256: return run_q<256>(a, ws);
         default: return hipErrorInvalidValue;
     }
 }
@@ -624,14 +512,12 @@ bool mfma_supported(int64_t P, int64_t N, int64_t Q) {
     return P == kP && (N == 64 || N == 128 || N == 256) && (Q == 64 || Q == 128 || Q == 256);
 }
 
-size_t fused_max_chains() { return (size_t)1 << 30; }
-
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q) {
     const int64_t nc = (L + Q - 1) / Q;
     return (size_t)(B * G * nc * Q * kSub) * sizeof(__bf16);
 }
 
-hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws, false); }
+hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws); }
 
 hipError_t launch_gram(const ScanArgs &a, const Workspace &ws, int64_t nsb) {
     switch (a.N) {

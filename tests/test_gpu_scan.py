@@ -165,3 +165,34 @@ def test_one_workspace_serves_different_shapes():
         y_ref, f_ref = oracle_scan(d)
         assert rel_err(to_np(y), y_ref) <= 2e-2
         assert rel_err(to_np(fin), f_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("N,Q", [(128, 64), (128, 128), (128, 256), (64, 64), (256, 128)])
+def test_nothing_is_read_past_the_sequence_end(N, Q):
+    """x, dt, Bm and Cm are the first L rows of buffers whose remaining rows
+    hold NaN; a read past token L-1 (the ragged tail of the last block) would
+    make outputs non-finite."""
+    import selective_state_space_chunk_amd as ssd
+    B, L, H, P, extra = 1, 3 * Q + 5, 4, 64, 300
+    d = si.make_scan_inputs(B, L, H, P, N, 1, dtype="bf16", init=True, seed=4242 + Q + N, regime="long_memory")
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+
+    def padded(t):
+        big = torch.full((B, L + extra) + tuple(t.shape[2:]), float("nan"), dtype=t.dtype, device=t.device)
+        big[:, :L] = t
+        return big[:, :L]
+
+    for name in ("x", "dt", "Bm", "Cm"):
+        dd[name] = padded(dd[name])
+        assert dd[name].is_contiguous()
+    algos = ["reference", "staged"] + (["fused"] if N <= 128 else [])
+    for algo in algos:
+        announce(f"NaN past the end N{N} Q{Q} L{L} algo={algo}")
+        y = torch.full_like(dd["x"], float("nan"))
+        fin = torch.full((B, H, P, N), float("nan"), device="cuda")
+        ssd.ssd_chunk_scan_fwd(dd["x"], dd["dt"], dd["A"], dd["Bm"], dd["Cm"], dd["D"], dd["init"], Q,
+                               y=y, final_state=fin, algo=algo)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(y), y_ref) <= 2e-2
+        assert rel_err(to_np(fin), f_ref) <= 2e-2
