@@ -389,8 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void chain_kernel(Args a) {
     auto step = [&](int s, const Small &sm_cur, Small &sm_nxt) {
         const int par = s & 1;
 
-        // ---- loads: x, Bm, Cm of sub-block s+1; G tiles and dt of s+2
-        load_bulk<N>(bulk, a, o, b, h, g, s + 1 < nsub ? s + 1 : nsub - 1);
+        // ---- loads: G tiles and dt of sub-block s+2
         load_small<N>(sm_nxt, a, o, b, h, g, s + 2 < nsub ? s + 2 : nsub - 1, wave, lane);
         // ---- decays and masked-matrix tiles of sub-block s+1 (in registers until staged)
         uint2 mt[3];
@@ -398,6 +397,10 @@ __global__ __launch_bounds__(kThreads, 2) void chain_kernel(Args a) {
             wave_decays(wd, par ^ 1, sm_cur.dt, Ah, lane);
             m_tiles(wd, sm_cur.g, mt, wave, lrow, lgrp);
         }
+
+        // ---- loads: x, Bm and Cm of sub-block s+1 (issued after the decays,
+        // which wait on the dt loaded a step ago)
+        load_bulk<N>(bulk, a, o, b, h, g, s + 1 < nsub ? s + 1 : nsub - 1);
 
         // ---- inter-block part: Y^T[p][i] = exp(Lambda_i) sum_n H[p][n] Cm_i[n]
         f32x4 Y[4];
