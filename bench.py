@@ -37,8 +37,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_m2_2p7b.json")
+WORKLOAD_NAMES = {"m2_2p7b": "mamba2_2.7b_layer_ssd_chunk_scan", "m2_130m": "mamba2_130m_layer_ssd_chunk_scan",
+                  "tiny_fp32": "tiny_fp32_ssd_chunk_scan", "long_n128": "long_sequence_n128_ssd_chunk_scan",
+                  "long_n256": "long_sequence_n256_ssd_chunk_scan"}
 # the sources whose kernels run in one scan launch at this workload
-SCAN_SOURCES = ["chain_scan.hip", "mfma_scan.hip", "api.hip", "common.h"]
+SCAN_SOURCES = ["pipe_scan.hip", "mfma_scan.hip", "api.hip", "common.h"]
 
 
 def scan_sources_digest() -> str:
@@ -92,7 +95,7 @@ def make_device_sets(w, nsets, device):
             if v is None:
                 td[name] = None
             elif name in ("x", "Bm", "Cm"):
-                td[name] = torch.from_numpy(v).to(device=device, dtype=torch.bfloat16)
+                td[name] = torch.from_numpy(v).to(device=device, dtype=io_dtype(w))
             else:
                 td[name] = torch.from_numpy(v).to(device=device, dtype=torch.float32)
         td["y"] = torch.empty_like(td["x"])
@@ -101,11 +104,16 @@ def make_device_sets(w, nsets, device):
     return sets
 
 
+def io_dtype(w):
+    import torch
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
 def time_scan(w, steps, warmup, device):
     import torch
     import selective_state_space_chunk_amd as ssd
     sets = make_device_sets(w, 3, device)
-    nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, torch.bfloat16)
+    nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
     def run(k):
@@ -238,7 +246,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_fetch, "write_scale_bytes_per_kib": f_write, "kernels": {}}
     total = 0.0
-    for name in ("chain_kernel", "scan_fused", "gram_kernel", "scan_mfma", "ref_"):
+    for name in ("pipe_kernel", "chain_kernel", "scan_fused", "gram_kernel", "scan_mfma", "ref_"):
         try:
             fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
             wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)
@@ -266,6 +274,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--copy-mb", type=float, default=512.0)
+    ap.add_argument("--workload", default="m2_2p7b",
+                    help="scan workload to time (m2_2p7b is the headline; tiny_fp32, m2_130m, long_n128, "
+                         "long_n256 are the other scan shapes)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.copy_mb)
@@ -281,7 +292,10 @@ def main():
     import torch
     import ssd_inputs as si
     device = torch.device("cuda:0")
-    w = si.WORKLOADS["m2_2p7b"]
+    if args.workload not in si.WORKLOADS or si.WORKLOADS[args.workload].L < 2:
+        raise SystemExit(f"unknown scan workload {args.workload!r}")
+    w = si.WORKLOADS[args.workload]
+    headline = args.workload == "m2_2p7b"
     wall, per = time_scan(w, args.steps, args.warmup, device)
     ms_step = wall * 1000.0 / args.steps
     kern_ms = sum(per) / len(per)
@@ -299,19 +313,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "mamba2_2.7b_layer_ssd_chunk_scan", "batch": w.B, "seq_len": w.L,
+        "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name), "batch": w.B, "seq_len": w.L,
                    "heads": w.H, "head_dim": w.P, "state": w.N, "groups": w.G, "chunk": w.chunk,
-                   "init_state": True, "parallelism": "single_gpu"},
+                   "init_state": bool(w.init), "parallelism": "single_gpu"},
         "kernel_ms": {"mean": kern_ms, "median": per[len(per) // 2], "p10": per[len(per) // 10],
                       "p90": per[(9 * len(per)) // 10]},
-        "roofline": {"bound": "hbm", "kernels": "gram_kernel + chain_kernel<128> (one ssd_chunk_scan_fwd call)",
+        "roofline": {"bound": "hbm", "kernels": "gram_kernel + pipe_kernel<128> (one ssd_chunk_scan_fwd call)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic() if headline else None,
                      "algorithmic_bytes": byts, "algorithmic_flops": flops,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    if not headline:
+        del out["roofline"]["kernels"]
     if not args.no_decode:
         B, H, P, N, G = 256, 80, 64, 128, 1
         sp = time_step(B, H, P, N, G, max(20, args.steps // 2), 5, device)
@@ -324,7 +340,7 @@ def main():
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "algorithmic_bytes": sb}}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

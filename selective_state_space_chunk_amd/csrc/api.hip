@@ -15,6 +15,8 @@ size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
 bool fused_supported(int64_t H, int64_t G, int64_t N, int64_t Q);
 hipError_t launch_chain_scan(const ScanArgs &a, const Workspace &ws);
 bool chain_supported(int64_t H, int64_t G, int64_t N);
+hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
+bool pipe_supported(int64_t H, int64_t G, int64_t N);
 }
 
 namespace {
@@ -107,12 +109,14 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
-        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN)
+        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE)
         return SSD_ERR_UNSUPPORTED;
     const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
-    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN) && !mfma_ok)
+    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN || algo == SSD_ALGO_PIPE) &&
+        !mfma_ok)
         return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_CHAIN && !chain_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_PIPE && !pipe_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && !fused_supported(H, G, N, Q)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && B * H * ((L + Q - 1) / Q) > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
 
@@ -144,8 +148,8 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
             // one workgroup per (batch, head) sequence when there are enough
             // sequences to occupy the device; else one pass while chains of
             // blocks are short and many; staged otherwise
-            if (chain_supported(H, G, N) && B * H >= 160)
-                algo = SSD_ALGO_CHAIN;
+            if (pipe_supported(H, G, N) && B * H >= 160)
+                algo = SSD_ALGO_PIPE;
             else
                 algo = (nc <= 64 && fused_supported(H, G, N, Q) && B * H >= 64 && B * H * nc <= 0x7fffffff)
                            ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
@@ -157,6 +161,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         case SSD_ALGO_STAGED: e = launch_staged_scan(a, ws); break;
         case SSD_ALGO_FUSED: e = launch_fused_scan(a, ws); break;
         case SSD_ALGO_CHAIN: e = launch_chain_scan(a, ws); break;
+        case SSD_ALGO_PIPE: e = launch_pipe_scan(a, ws); break;
         default: return SSD_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

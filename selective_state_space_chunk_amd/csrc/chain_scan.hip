@@ -336,6 +336,17 @@ __device__ __forceinline__ void stage(ChainSmem<N> &sm, const Bulk<N> &sl, const
     }
 }
 
+constexpr int kXcds = 8;
+
+// Sequence of workgroup `blk` out of `n`: XCD x = blk % 8 runs the workgroups
+// blk = x, x+8, x+16, ...; the k-th of them takes sequence start(x) + k, where
+// the XCDs' ranges split [0, n) into eight contiguous parts (the first n % 8
+// one longer).  A bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_chain(int64_t blk, int64_t n) {
+    const int64_t x = blk % kXcds, k = blk / kXcds, per = n / kXcds, rem = n % kXcds;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
 template <int N>
 __global__ __launch_bounds__(kThreads, 2) void chain_kernel(Args a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -344,8 +355,11 @@ __global__ __launch_bounds__(kThreads, 2) void chain_kernel(Args a) {
     constexpr int NT = N / 16;
     constexpr int KS = N / 32;
 
-    // (batch, head, group) of this workgroup, in scalar registers
-    const int64_t chain = blockIdx.x;
+    // (batch, head, group) of this workgroup, in scalar registers.  Workgroups
+    // are dealt to the eight XCDs round-robin by index; each XCD is given a
+    // contiguous range of sequences instead, so that the Bm, Cm, gram tiles and
+    // dt lines its heads share stay in that XCD's L2.
+    const int64_t chain = xcd_chain(blockIdx.x, gridDim.x);
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));

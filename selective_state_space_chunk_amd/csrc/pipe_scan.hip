@@ -1,0 +1,611 @@
+// Chunk scan with one workgroup per (batch, head) sequence and two wave
+// roles, on gfx950 matrix cores (bf16 operands, fp32 accumulation).
+//
+// The arithmetic is that of the per-sequence kernel in chain_scan.hip: the
+// sequence is walked in sub-blocks of 64 tokens, the P x N state stays in
+// matrix-core accumulators from the first token to the last, and per
+// sub-block, with Lambda the inclusive prefix sum of dt*A inside it, the
+// block decomposition of the "Mamba-2" note (section "taking each path half
+// way") and of the "Mamba-2 model walkthrough" (sections 6.1-6.2) gives
+//   y_i = exp(Lambda_i) Cm_i . H  +  sum_{j<=i} G[i][j] exp(Lambda_i - Lambda_j) dt_j x_j  +  D x_i
+//   H  <- exp(Lambda_63) H  +  sum_j Bm_j (outer) (exp(Lambda_63 - Lambda_j) dt_j x_j)
+// with G[i][j] = Cm_i . Bm_j from the gram kernel and H the state entering
+// the sub-block.
+//
+// What differs is the division of labour.  A workgroup has eight waves, two
+// on each SIMD, with different jobs, so that each SIMD always has a second
+// instruction stream to issue from while one waits on LDS or memory:
+//   state waves 0-3   own rows p = 16w..16w+15 of the state.  In step t they
+//                     form the inter-block term of sub-block t from the state
+//                     entering it (written to LDS for the output waves) and
+//                     then advance the state over sub-block t;
+//   output waves 4-7  finish sub-block t-1 for the same rows: the inter-block
+//                     term from LDS, the masked intra-block product (the skip
+//                     term D x_i rides on the diagonal of the masked matrix),
+//                     and the stores of y; and build the masked decay matrix of
+//                     sub-block t for the next step.
+// The state waves stage the next sub-block's x, the output waves its Bm and Cm.
+// One barrier per step; LDS buffers rotate so that nothing written in a step
+// is read in the same step by another wave.
+#include "common.h"
+
+#include <type_traits>
+
+namespace ssd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kP = 64;
+constexpr int kSub = 64;
+constexpr int kThreads = 512;
+constexpr int kRaw = 0x00020000;   // buffer descriptor word 3: raw 32-bit access
+constexpr int kXcds = 8;
+
+struct WaveDecays {          // one wave's decays of the sub-block it works on
+    float lam[kSub];         // Lambda log2(e)
+    float dt[kSub];          // dt (0 past the end)
+    float w[kSub];           // exp(Lambda_63 - Lambda_j) dt_j
+    float rdec[kSub];        // exp(Lambda_i)
+};
+
+template <int N>
+struct PipeSmem {
+    __bf16 X[3][kSub * kP];        // x [j][p] of sub-blocks t-1, t, t+1 (by t % 3), chunks swizzled (xsw)
+    __bf16 Bt[2][kSub * N];        // Bm [j][n] (by t % 2), chunks swizzled (bsw)
+    __bf16 Ct[2][kSub * N];        // Cm [i][n] (by t % 2), chunks swizzled (csw)
+    __bf16 Mm[2][kSub * kSub];     // masked decay matrix [i][j] (by t % 2), chunks swizzled (msw)
+    f32x4 YI[2][4][4][64];         // inter-block term, [parity][row group][token tile][lane]
+    WaveDecays wd[8];
+};
+
+__device__ __forceinline__ int xsw(int r) { return ((r >> 1) & 1) * 2 + ((r >> 3) & 1) * 4; }
+template <int N>
+__device__ __forceinline__ int bsw(int r) {
+    if constexpr (N == 128) return 2 * (r & 3) + 8 * ((r >> 3) & 1);
+    else return xsw(r);
+}
+// Cm rows: rows 16 apart get different chunk permutations, so that the
+// fragment reads of consecutive 16-row tiles never fall on the same banks
+// (the compiler would otherwise pair them into one two-address read whose
+// halves collide).
+template <int N>
+__device__ __forceinline__ int csw(int r) {
+    if constexpr (N == 128) return (r & 15) ^ (((r >> 4) & 3) << 2);
+    else return ((r >> 1) & 7) ^ (((r >> 4) & 3) << 1);
+}
+// byte XOR that csw applies to the rows of 16-row tile `it` beyond row-in-tile bits
+template <int N>
+__device__ __forceinline__ constexpr int csw_tile_bytes(int it) { return (N == 128 ? 64 : 32) * (it & 3); }
+// masked decay matrix rows (128 bytes): chunk c of row r at c ^ msw(r)
+__device__ __forceinline__ int msw(int r) { return (r >> 1) & 7; }
+
+// One sub-block's x is loaded and staged by the state waves, its Bm and Cm by
+// the output waves (thread u = tid or tid - 256 of its role).
+struct BulkX {
+    uint4 x[2];              // x chunks u + 256k: row (u + 256k)/8, chunk u%8
+};
+template <int N>
+struct BulkBC {
+    uint4 b[N / 32];         // Bm chunks u + 256k: row (u + 256k)/(N/8), chunk u%(N/8)
+    uint4 c[N / 32];         // Cm, same mapping
+};
+struct Small {               // one sub-block's dt (lane = token) and, for output waves, G tiles
+    uint2 g[3];
+    float dt;
+};
+
+struct Args {
+    const __bf16 *x;
+    const float *dt, *A;
+    const __bf16 *Bm, *Cm;
+    const float *D, *init;
+    __bf16 *y;
+    float *final_state;
+    const __bf16 *gram;
+    int64_t L, H, G, nsb;
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Two floats to two bfloat16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 lo, f32x4 hi) {
+    return __builtin_convertvector(f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, bf16x8);
+}
+// 2^x on the transcendental unit (v_exp_f32).  The decays are kept in base-2
+// units (Lambda * log2 e), so exp(Lambda_i - Lambda_j) = exp2(lam_i - lam_j).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
+    it = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+    jt = k - (it * (it + 1)) / 2;
+}
+// Buffer descriptors: only the vector and immediate offsets are range-checked
+// (loads outside return 0, stores outside are dropped).  Every buffer here is
+// uniform across the workgroup; readfirstlane keeps the descriptor scalar.
+__device__ __forceinline__ rsrc_t rsrc(const void *base, int bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void *q = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRaw);
+}
+__device__ __forceinline__ uint4 ld16(rsrc_t r, int voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// a+4q names row kbase+q, columns 4a..4a+3 of a row-major tile, and lane i
+// receives rows kbase..kbase+3 of column i.
+__device__ __forceinline__ bf16x4 tr4(const unsigned char *p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+template <class T>
+__device__ __forceinline__ T lds_ld(const unsigned char *p) { return *reinterpret_cast<const T *>(p); }
+template <class T>
+__device__ __forceinline__ void lds_st(unsigned char *p, T v) { *reinterpret_cast<T *>(p) = v; }
+
+__device__ __forceinline__ int64_t xcd_chain(int64_t blk, int64_t n) {
+    const int64_t x = blk % kXcds, k = blk / kXcds, per = n / kXcds, rem = n % kXcds;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
+// Per-lane byte offsets, fixed for the whole sequence (pq = this wave's
+// 16-row group of p).
+template <int N>
+struct LaneOffs {
+    static constexpr int NT = N / 16, KS = N / 32;
+    static constexpr int RB = N * 2;          // bytes per Bm / Cm row
+    static constexpr int CPR = N / 8;         // 16-byte chunks per Bm / Cm row
+    int xtr;          // X, transposing reads:    + ks*4096 (+512 for rows +4)
+    int mm[2];        // Mm, fragment reads (by ks): + it*2048
+    int mw;           // Mm, tile writes:         + 16 ti * 128, chunk bytes ^ 32 tj
+    int ct[KS][2];    // Ct, pieces n0 and n1:    + it*16*RB, chunk bytes ^ csw_tile_bytes(it)
+    int bt[NT];       // Bt, transposing reads:   + ks*32*RB (+4*RB for rows +4)
+    int sx;           // x stage writes (state waves):       + k*4096
+    int gx;           // x global loads (state waves):       + k*32*H*P*2
+    int sb;           // Bm stage writes (output waves):     + k*(256/CPR)*RB
+    int sc[N / 32];   // Cm stage writes (output waves), by k
+    int gb;           // Bm, Cm global loads (output waves): + k*(256/CPR)*G*N*2
+    int gd;           // dt loads
+    int gy;           // y stores:                + it*16*H*P*2
+};
+
+template <int N>
+__device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, int64_t G) {
+    using O = LaneOffs<N>;
+    const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4, qa = lane & 3, qq = (lane & 15) >> 2;
+    O o;
+    const int r = 8 * lgrp + qq;                  // row (within a k-step) of the transposing reads
+    o.xtr = r * 128 + (((2 * pq + (qa >> 1)) ^ xsw(r)) * 16) + (qa & 1) * 8;
+    o.mm[0] = lrow * 128 + ((lgrp ^ msw(lrow)) * 16);
+    o.mm[1] = lrow * 128 + (((4 + lgrp) ^ msw(lrow)) * 16);
+    o.mw = lrow * 128 + (((lgrp >> 1) ^ msw(lrow)) * 16) + (lgrp & 1) * 8;
+#pragma unroll
+    for (int ks = 0; ks < O::KS; ++ks)
+#pragma unroll
+        for (int wh = 0; wh < 2; ++wh) {
+            const int n = 32 * ks + 16 * wh + 4 * lgrp;
+            o.ct[ks][wh] = lrow * O::RB + (((n >> 3) ^ csw<N>(lrow)) * 16) + (n & 7) * 2;   // tile 0
+        }
+#pragma unroll
+    for (int t = 0; t < O::NT; ++t) {
+        const int col = 16 * t + 4 * qa;
+        o.bt[t] = r * O::RB + (((col >> 3) ^ bsw<N>(r)) * 16) + (col & 7) * 2;
+    }
+    {
+        const int u = tid & 255;
+        const int j = u >> 3, c = u & 7;
+        o.sx = j * 128 + ((c ^ xsw(j)) * 16);   // row j + 32 has the same swizzle
+        o.gx = (int)(((int64_t)j * H * kP + 8 * c) * 2);
+        const int jb = u / O::CPR, cb = u % O::CPR;
+        o.sb = jb * O::RB + ((cb ^ bsw<N>(jb)) * 16);   // rows jb + 256k/CPR: same swizzle
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+            const int jk = jb + k * (256 / O::CPR);
+            o.sc[k] = jk * O::RB + ((cb ^ csw<N>(jk)) * 16);
+        }
+        o.gb = (int)(((int64_t)jb * G * N + 8 * cb) * 2);
+    }
+    o.gd = (int)((int64_t)lane * H * 4);
+    o.gy = (int)(((int64_t)lrow * H * kP + 16 * pq + 4 * lgrp) * 2);
+    return o;
+}
+
+__device__ __forceinline__ int sub_tokens(const Args &a, int sb) {
+    const int64_t rem = a.L - (int64_t)sb * kSub;
+    return rem < kSub ? (int)rem : kSub;
+}
+
+// Global loads of this thread's share of sub-block sb's x (state waves) or Bm
+// and Cm (output waves), masked past the end of the sequence.
+template <int N>
+__device__ __forceinline__ void load_x(BulkX &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t h, int sb) {
+    const int q = sub_tokens(a, sb);
+    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
+    const rsrc_t r = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
+    const int step = (int)(32 * a.H * kP * 2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) sl.x[k] = ld16(r, o.gx + k * step);
+}
+template <int N>
+__device__ __forceinline__ void load_bc(BulkBC<N> &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t g,
+                                        int sb) {
+    using O = LaneOffs<N>;
+    const int q = sub_tokens(a, sb);
+    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
+    const int bytes = (int)(((int64_t)(q - 1) * a.G * N + N) * 2);
+    const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, bytes);
+    const rsrc_t rc = rsrc(a.Cm + (row0 * a.G + g) * N, bytes);
+    const int step = (int)((256 / O::CPR) * a.G * N * 2);
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) {
+        sl.b[k] = ld16(rb, o.gb + k * step);
+        sl.c[k] = ld16(rc, o.gb + k * step);
+    }
+}
+template <int N>
+__device__ __forceinline__ void stage_x(PipeSmem<N> &sm, int xbuf, const BulkX &sl, const LaneOffs<N> &o) {
+    unsigned char *Xb = reinterpret_cast<unsigned char *>(sm.X[xbuf]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) lds_st<uint4>(Xb + o.sx + k * 4096, sl.x[k]);
+}
+template <int N>
+__device__ __forceinline__ void stage_bc(PipeSmem<N> &sm, int par, const BulkBC<N> &sl, const LaneOffs<N> &o) {
+    using O = LaneOffs<N>;
+    unsigned char *Bb = reinterpret_cast<unsigned char *>(sm.Bt[par]);
+    unsigned char *Cb = reinterpret_cast<unsigned char *>(sm.Ct[par]);
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) {
+        lds_st<uint4>(Bb + o.sb + k * (256 / O::CPR) * O::RB, sl.b[k]);
+        lds_st<uint4>(Cb + o.sc[k], sl.c[k]);
+    }
+}
+
+// dt of sub-block sb (lane = token) and, for output waves, their G tiles.
+template <int N, bool kOut>
+__device__ __forceinline__ void load_small(Small &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t h,
+                                           int64_t g, int sb, int ow, int lane) {
+    const int q = sub_tokens(a, sb);
+    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
+    if constexpr (kOut) {
+        const rsrc_t rg = rsrc(a.gram + ((b * a.G + g) * a.nsb + sb) * (int64_t)(kSub * kSub), kSub * kSub * 2);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int k = ow + 4 * m < 10 ? ow + 4 * m : 9;   // waves with two tiles load their last twice
+            sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
+        }
+    }
+    const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(q - 1) * a.H + 1) * 4));
+    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts.
+__device__ __forceinline__ float wave_scan(float v) {
+    auto shr = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, true));
+    };
+    v += shr(v, std::integral_constant<int, 0x111>{});   // row_shr:1
+    v += shr(v, std::integral_constant<int, 0x112>{});   // row_shr:2
+    v += shr(v, std::integral_constant<int, 0x114>{});   // row_shr:4
+    v += shr(v, std::integral_constant<int, 0x118>{});   // row_shr:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));   // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return v;
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    PipeSmem<N> &sm = *reinterpret_cast<PipeSmem<N> *>(smem_raw);
+    using O = LaneOffs<N>;
+    constexpr int NT = N / 16;
+    constexpr int KS = N / 32;
+
+    const int64_t chain = xcd_chain(blockIdx.x, gridDim.x);
+    const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
+    const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
+    const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
+    const int nsub = (int)((a.L + kSub - 1) / kSub);
+    const float Ah2 = a.A[h] * kLog2e, Dh = a.D[h];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pq = wave & 3;
+    const bool state_wave = wave < 4;
+    const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
+    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
+    WaveDecays &wd = sm.wd[wave];
+
+    Small small[2];
+
+    if (state_wave) {
+        // ------------------------------------------------------------------
+        // state waves: rows p = 16pq..16pq+15 of H, held transposed (rows n,
+        // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow
+        // prologue: x of sub-block 0 staged; x of sub-block 1 and dt of
+        // sub-blocks 0 and 1 in flight
+        BulkX bulk[2];   // x of sub-block t+1 (staged at the end of step t) and t+2 (in flight)
+        load_x<N>(bulk[0], a, o, b, h, 0);
+        load_small<N, false>(small[0], a, o, b, h, g, 0, 0, lane);
+        load_small<N, false>(small[1], a, o, b, h, g, nsub > 1 ? 1 : 0, 0, lane);
+        stage_x<N>(sm, 0, bulk[0], o);
+        load_x<N>(bulk[1], a, o, b, h, nsub > 1 ? 1 : 0);
+        __syncthreads();
+        f32x4 Hacc[NT];
+        {
+            const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + chain * (kP * N)) : (const void *)a.x,
+                                   a.init ? kP * N * 4 : 0);
+            const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                Hacc[t] = __builtin_bit_cast(f32x4,
+                                             __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off + 16 * t) * 4, 0, 0));
+        }
+        auto step = [&](int t, int par, Small &sl) {
+            const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[t % 3]);
+            const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
+            const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
+            // decays of sub-block t (this wave's own copy)
+            const float dt = sl.dt;
+            const float v = wave_scan(dt * Ah2);
+            const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+            wd.w[lane] = ex2(lend - v) * dt;
+            wd.rdec[lane] = ex2(v);
+            const float gam = ex2(lend);
+            // dt of sub-block t+2 into the slot just read; x, Bm, Cm of t+2
+            load_small<N, false>(sl, a, o, b, h, g, t + 2 < nsub ? t + 2 : nsub - 1, 0, lane);
+            load_x<N>(bulk[par], a, o, b, h, t + 2 < nsub ? t + 2 : nsub - 1);
+
+            // LDS reads first (the Cm fragments of the inter-block term, the x
+            // fragments and weights of the update); the Bm fragments are read
+            // while the first products run
+            bf16x8 cf[KS][4];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const bf16x4 c0 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][0] ^ csw_tile_bytes<N>(it)));
+                    const bf16x4 c1 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][1] ^ csw_tile_bytes<N>(it)));
+                    cf[ks][it] = bf16x8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                }
+            bf16x8 xf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
+                const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
+                xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+            f32x4 wv[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                wv[ks][0] = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp]);
+                wv[ks][1] = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp + 4]);
+            }
+            const f32x4 rd = {wd.rdec[lrow], wd.rdec[16 + lrow], wd.rdec[32 + lrow], wd.rdec[48 + lrow]};
+            __builtin_amdgcn_sched_barrier(0);
+
+            // inter-block term of sub-block t: Y^T[p][i] = exp(Lambda_i) sum_n H[p][n] Cm_i[n]
+            f32x4 Y[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) Y[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 bt[2][NT];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ah = to_bf16x8(Hacc[2 * ks], Hacc[2 * ks + 1]);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) Y[it] = mfma(ah, cf[ks][it], Y[it]);
+                // Bm fragments of k-step kb = 2ks/KS (half of them after each half of the products)
+                if (ks == KS / 2 - 1 || ks == KS - 1) {
+                    const int kb = ks == KS - 1 ? 1 : 0;
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) {
+                        const bf16x4 lo = tr4(Bb + o.bt[u] + kb * 32 * O::RB);
+                        const bf16x4 hi = tr4(Bb + o.bt[u] + kb * 32 * O::RB + 4 * O::RB);
+                        bt[kb][u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) sm.YI[par][pq][it][lane] = Y[it] * rd[it];
+
+            // state update over sub-block t: H <- exp(Lambda_63) H + sum_j Bm_j (outer) (w_j x_j)
+#pragma unroll
+            for (int u = 0; u < NT; ++u) Hacc[u] *= gam;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f32x4 x0, x1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] = (float)xf[ks][e] * wv[ks][0][e];
+                    x1[e] = (float)xf[ks][4 + e] * wv[ks][1][e];
+                }
+                const bf16x8 xw = to_bf16x8(x0, x1);
+#pragma unroll
+                for (int u = 0; u < NT; ++u) Hacc[u] = mfma(bt[ks][u], xw, Hacc[u]);
+            }
+            if (t + 1 < nsub) stage_x<N>(sm, (t + 1) % 3, bulk[par ^ 1], o);
+            __syncthreads();
+        };
+        int t = 0;
+        for (; t + 1 < nsub; t += 2) {
+            step(t, 0, small[0]);
+            step(t + 1, 1, small[1]);
+        }
+        if (t < nsub) step(t, 0, small[0]);
+        __syncthreads();   // matches the output waves' final step
+        if (a.final_state) {
+            float *dst = a.final_state + chain * (kP * N) + (16 * pq + lrow) * N + 4 * lgrp;
+#pragma unroll
+            for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
+        }
+    } else {
+        // ------------------------------------------------------------------
+        // output waves: tiles of M for sub-block t, outputs of sub-block t-1
+        // (lane holds token i = 16it + lrow, p = 16pq + 4lgrp + 0..3)
+        // prologue: Bm, Cm of sub-block 0 staged; those of sub-block 1 and dt
+        // and G tiles of sub-blocks 0 and 1 in flight
+        BulkBC<N> bulk[2];   // Bm, Cm of sub-block t+1 (staged at the end of step t) and t+2
+        load_bc<N>(bulk[0], a, o, b, g, 0);
+        load_small<N, true>(small[0], a, o, b, h, g, 0, pq, lane);
+        load_small<N, true>(small[1], a, o, b, h, g, nsub > 1 ? 1 : 0, pq, lane);
+        stage_bc<N>(sm, 0, bulk[0], o);
+        load_bc<N>(bulk[1], a, o, b, g, nsub > 1 ? 1 : 0);
+        __syncthreads();
+        const unsigned char *Mb[2] = {reinterpret_cast<const unsigned char *>(sm.Mm[0]),
+                                      reinterpret_cast<const unsigned char *>(sm.Mm[1])};
+        auto step = [&](int t, int par, Small &sl) {
+            if (t < nsub) {
+                // decays and this wave's tiles of M for sub-block t
+                const float dt = sl.dt;
+                const float v = wave_scan(dt * Ah2);
+                wd.lam[lane] = v;
+                wd.dt[lane] = dt;
+                uint2 mt[3];
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const int k = pq + 4 * m < 10 ? pq + 4 * m : 9;
+                    int ti, tj;
+                    tile_of(k, ti, tj);
+                    const int i = 16 * ti + lrow, j0 = 16 * tj + 4 * lgrp;
+                    const float li = wd.lam[i];
+                    const f32x4 lj = *reinterpret_cast<const f32x4 *>(&wd.lam[j0]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4 *>(&wd.dt[j0]);
+                    const uint32_t gw[2] = {sl.g[m].x, sl.g[m].y};
+                    float mv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float gv = (e & 1) ? hi_bf16(gw[e >> 1]) : lo_bf16(gw[e >> 1]);
+                        const float d = j0 + e <= i ? li - lj[e] : -__builtin_inff();
+                        // the skip term D x_i rides on the diagonal
+                        mv[e] = __builtin_fmaf(gv * ex2(d), dj[e], j0 + e == i ? Dh : 0.f);
+                    }
+                    mt[m] = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
+                }
+                unsigned char *Mw = reinterpret_cast<unsigned char *>(sm.Mm[par]);
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const int k = pq + 4 * m;
+                    if (k < 10) {
+                        int ti, tj;
+                        tile_of(k, ti, tj);
+                        lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * tj)), mt[m]);
+                    }
+                }
+                if (pq >= 2) {
+                    // the tiles above the diagonal that the products read: (0,1) and (2,3)
+                    const int ti = pq == 2 ? 0 : 2;
+                    uint32_t z = 0;
+                    asm volatile("" : "+v"(z));
+                    lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * (ti + 1))), uint2{z, z});
+                }
+                load_small<N, true>(sl, a, o, b, h, g, t + 2 < nsub ? t + 2 : nsub - 1, pq, lane);
+                load_bc<N>(bulk[par], a, o, b, g, t + 2 < nsub ? t + 2 : nsub - 1);
+            }
+            if (t >= 1) {
+                // outputs of sub-block s = t-1
+                const int s = t - 1;
+                const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[s % 3]);
+                const unsigned char *Mr = Mb[par ^ 1];
+                f32x4 Y[4];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) Y[it] = sm.YI[par ^ 1][pq][it][lane];
+                bf16x8 xf[2], mf[4][2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
+                    const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
+                    xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (!(ks == 1 && it < 2)) mf[it][ks] = lds_ld<bf16x8>(Mr + o.mm[ks] + it * 2048);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
+                const int64_t t0 = (int64_t)s * kSub;
+                const int q = sub_tokens(a, s);
+                const rsrc_t ry = rsrc(a.y + ((b * a.L + t0) * a.H + h) * kP,
+                                       (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
+                const int ystep = (int)(16 * a.H * kP * 2);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const uint2 pk = uint2{pack2(Y[it][0], Y[it][1]), pack2(Y[it][2], Y[it][3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), ry, o.gy + it * ystep, 0, 0);
+                }
+            }
+            if (t + 1 < nsub) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
+            __syncthreads();
+        };
+        int t = 0;
+        for (; t + 1 < nsub; t += 2) {
+            step(t, 0, small[0]);
+            step(t + 1, 1, small[1]);
+        }
+        if (t < nsub) {
+            step(t, 0, small[0]);
+            step(t + 1, 1, small[1]);   // outputs of the last sub-block
+        } else {
+            step(t, 0, small[0]);
+        }
+    }
+}
+
+template <int N>
+hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
+    const int64_t nsb = (sa.L + kSub - 1) / kSub;
+    hipError_t e = launch_gram(sa, ws, nsb);
+    if (e != hipSuccess) return e;
+    const size_t smem = sizeof(PipeSmem<N>);
+    auto kern = pipe_kernel<N>;
+    static bool configured = false;
+    if (!configured) {
+        e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    Args a{(const __bf16 *)sa.x, sa.dt, sa.A, (const __bf16 *)sa.Bm, (const __bf16 *)sa.Cm, sa.D,
+           sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, sa.L, sa.H, sa.G, nsb};
+    kern<<<dim3((unsigned)(sa.B * sa.H)), kThreads, smem, sa.stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool pipe_supported(int64_t H, int64_t G, int64_t N) {
+    if (!(N == 64 || N == 128)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)kSub * H * kP * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
+}
+
+hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws) {
+    switch (a.N) {
+        case 64: return launch<64>(a, ws);
+        case 128: return launch<128>(a, ws);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssd

@@ -11,7 +11,7 @@ from gpu_util import TOL, announce, gpu_scan, oracle_scan, rel_err, to_device, t
 
 pytestmark = pytest.mark.gpu
 
-MFMA_ALGOS = ["reference", "staged", "fused", "chain"]
+MFMA_ALGOS = ["reference", "staged", "fused", "chain", "pipe"]
 
 # (name, B, L, H, P, N, G, chunk, dtype, init, regime, algos)
 SMALL = [
@@ -76,7 +76,7 @@ def test_chunk_size_independence_on_gpu():
     dd = to_device(d, "bf16")
     outs = []
     for Q in (64, 128, 256):
-        for algo in ("staged", "fused", "chain"):
+        for algo in ("staged", "fused", "chain", "pipe"):
             announce(f"chunk independence Q{Q} algo={algo}")
             y, fin = gpu_scan(dd, Q, algo=algo)
             outs.append((to_np(y), to_np(fin)))
@@ -86,7 +86,7 @@ def test_chunk_size_independence_on_gpu():
         assert rel_err(y, outs[0][0]) <= 2e-2 and rel_err(fin, outs[0][1]) <= 2e-2
 
 
-@pytest.mark.parametrize("algo", ["reference", "staged", "fused", "chain"])
+@pytest.mark.parametrize("algo", ["reference", "staged", "fused", "chain", "pipe"])
 def test_split_resume_on_gpu(algo):
     """Running the first k tokens, then the rest from the returned state,
     matches one run over the whole sequence."""
@@ -186,7 +186,7 @@ def test_nothing_is_read_past_the_sequence_end(N, Q):
     for name in ("x", "dt", "Bm", "Cm"):
         dd[name] = padded(dd[name])
         assert dd[name].is_contiguous()
-    algos = ["reference", "staged"] + (["fused", "chain"] if N <= 128 else [])
+    algos = ["reference", "staged"] + (["fused", "chain", "pipe"] if N <= 128 else [])
     for algo in algos:
         announce(f"NaN past the end N{N} Q{Q} L{L} algo={algo}")
         y = torch.full_like(dd["x"], float("nan"))
