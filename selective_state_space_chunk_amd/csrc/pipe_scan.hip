@@ -113,8 +113,22 @@ struct Args {
     __bf16 *y;
     float *final_state;
     const __bf16 *gram;
+    float *seg;              // segment states [nextra][nseg-1][P][N], then their log2 decays [nextra][nseg-1]
     int64_t L, H, G, nsb;
+    int nmain;               // workgroups of the main kernel, one own sequence each
+    int nextra;              // further sequences, each cut into nseg segments of seglen sub-blocks;
+    int nseg, seglen;        //   segment q of extra sequence e runs on workgroup q*nextra + e
 };
+
+// Segment-state buffers in Args::seg.
+template <int N>
+__device__ __forceinline__ float *seg_state(const Args &a, int e, int q) {
+    return a.seg + ((int64_t)e * (a.nseg - 1) + q) * (kP * N);
+}
+template <int N>
+__device__ __forceinline__ float *seg_log2decay(const Args &a, int e, int q) {
+    return a.seg + (int64_t)a.nextra * (a.nseg - 1) * (kP * N) + (int64_t)e * (a.nseg - 1) + q;
+}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -318,12 +332,27 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     constexpr int NT = N / 16;
     constexpr int KS = N / 32;
 
-    const int64_t chain = xcd_chain(blockIdx.x, gridDim.x);
+    // this workgroup's own sequence (steps 0..nsub-1) and, after it, segment xq
+    // of a further sequence (steps nsub..T-1, sub-blocks seg0..seg0+xlen-1)
+    const int nsub = (int)((a.L + kSub - 1) / kSub);
+    const int64_t chain = xcd_chain(blockIdx.x, a.nmain);
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
-    const int nsub = (int)((a.L + kSub - 1) / kSub);
-    const float Ah2 = a.A[h] * kLog2e, Dh = a.D[h];
+    const float Ah2v = a.A[h] * kLog2e, Dhv = a.D[h];
+    const bool has_x = (int)blockIdx.x < a.nextra * a.nseg;
+    const int xe = has_x ? (int)blockIdx.x % a.nextra : 0;
+    const int xq = has_x ? (int)blockIdx.x / a.nextra : 0;
+    const int64_t xchain = has_x ? a.nmain + xe : chain;
+    const int64_t bx = __builtin_amdgcn_readfirstlane((int)(xchain / a.H));
+    const int64_t hx = __builtin_amdgcn_readfirstlane((int)(xchain % a.H));
+    const int64_t gx = __builtin_amdgcn_readfirstlane((int)(hx / (a.H / a.G)));
+    const float Ahx2 = a.A[hx] * kLog2e, Dhx = a.D[hx];
+    const int seg0 = xq * a.seglen;
+    const int xlen = has_x ? (nsub - seg0 < a.seglen ? nsub - seg0 : a.seglen) : 0;
+    const int T = nsub + xlen;
+    // sub-block of step tau, and of the step whose loads are issued at tau
+    auto sb_of = [&](int tau) { return tau < nsub ? tau : seg0 + (tau - nsub); };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -341,27 +370,58 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow
         // prologue: x of sub-block 0 staged; x of sub-block 1 and dt of
         // sub-blocks 0 and 1 in flight
-        BulkX bulk[2];   // x of sub-block t+1 (staged at the end of step t) and t+2 (in flight)
-        load_x<N>(bulk[0], a, o, b, h, 0);
-        load_small<N, false>(small[0], a, o, b, h, g, 0, 0, lane);
-        load_small<N, false>(small[1], a, o, b, h, g, nsub > 1 ? 1 : 0, 0, lane);
-        stage_x<N>(sm, 0, bulk[0], o);
-        load_x<N>(bulk[1], a, o, b, h, nsub > 1 ? 1 : 0);
+        BulkX bulk[2];   // x of step t+1 (staged at the end of step t) and t+2 (in flight)
+        {
+            const int t1 = T > 1 ? 1 : 0;
+            const bool x1 = t1 >= nsub;
+            load_x<N>(bulk[0], a, o, b, h, 0);
+            load_small<N, false>(small[0], a, o, b, h, g, 0, 0, lane);
+            load_small<N, false>(small[1], a, o, x1 ? bx : b, x1 ? hx : h, x1 ? gx : g, sb_of(t1), 0, lane);
+            stage_x<N>(sm, 0, bulk[0], o);
+            load_x<N>(bulk[1], a, o, x1 ? bx : b, x1 ? hx : h, sb_of(t1));
+        }
         __syncthreads();
         f32x4 Hacc[NT];
         {
             const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + chain * (kP * N)) : (const void *)a.x,
                                    a.init ? kP * N * 4 : 0);
-            const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
+            const int lane_off0 = (16 * pq + lrow) * N + 4 * lgrp;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 Hacc[t] = __builtin_bit_cast(f32x4,
-                                             __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off + 16 * t) * 4, 0, 0));
+                                             __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off0 + 16 * t) * 4, 0, 0));
         }
+        const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
         auto step = [&](int t, int par, Small &sl) {
             const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[t % 3]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
             const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
+            if (has_x && t == nsub) {
+                // own sequence done: its final state out; the segment's entering
+                // state in, from the initial state and the states and decays of
+                // the earlier segments (written by the segment-state kernel)
+                if (a.final_state) {
+                    float *dst = a.final_state + chain * (kP * N) + lane_off;
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
+                }
+                {
+                    const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + xchain * (kP * N)) : (const void *)a.x,
+                                           a.init ? kP * N * 4 : 0);
+#pragma unroll
+                    for (int u = 0; u < NT; ++u)
+                        Hacc[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                ri, (lane_off + 16 * u) * 4, 0, 0));
+                }
+                for (int qq = 0; qq < xq; ++qq) {
+                    const float gq = ex2(*seg_log2decay<N>(a, xe, qq));
+                    const float *sq = seg_state<N>(a, xe, qq) + lane_off;
+#pragma unroll
+                    for (int u = 0; u < NT; ++u) Hacc[u] = gq * Hacc[u] + *reinterpret_cast<const f32x4 *>(sq + 16 * u);
+                }
+            }
+            const bool xs = t >= nsub;
+            const float Ah2 = xs ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
             const float dt = sl.dt;
             const float v = wave_scan(dt * Ah2);
@@ -369,9 +429,13 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             wd.w[lane] = ex2(lend - v) * dt;
             wd.rdec[lane] = ex2(v);
             const float gam = ex2(lend);
-            // dt of sub-block t+2 into the slot just read; x, Bm, Cm of t+2
-            load_small<N, false>(sl, a, o, b, h, g, t + 2 < nsub ? t + 2 : nsub - 1, 0, lane);
-            load_x<N>(bulk[par], a, o, b, h, t + 2 < nsub ? t + 2 : nsub - 1);
+            // dt of step t+2 into the slot just read; x of step t+2
+            {
+                const int tl = t + 2 < T ? t + 2 : T - 1;
+                const bool xl = tl >= nsub;
+                load_small<N, false>(sl, a, o, xl ? bx : b, xl ? hx : h, xl ? gx : g, sb_of(tl), 0, lane);
+                load_x<N>(bulk[par], a, o, xl ? bx : b, xl ? hx : h, sb_of(tl));
+            }
 
             // LDS reads first (the Cm fragments of the inter-block term, the x
             // fragments and weights of the update); the Bm fragments are read
@@ -442,18 +506,20 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 #pragma unroll
                 for (int u = 0; u < NT; ++u) Hacc[u] = mfma(bt[ks][u], xw, Hacc[u]);
             }
-            if (t + 1 < nsub) stage_x<N>(sm, (t + 1) % 3, bulk[par ^ 1], o);
+            if (t + 1 < T) stage_x<N>(sm, (t + 1) % 3, bulk[par ^ 1], o);
             __syncthreads();
         };
         int t = 0;
-        for (; t + 1 < nsub; t += 2) {
+        for (; t + 1 < T; t += 2) {
             step(t, 0, small[0]);
             step(t + 1, 1, small[1]);
         }
-        if (t < nsub) step(t, 0, small[0]);
+        if (t < T) step(t, 0, small[0]);
         __syncthreads();   // matches the output waves' final step
-        if (a.final_state) {
-            float *dst = a.final_state + chain * (kP * N) + (16 * pq + lrow) * N + 4 * lgrp;
+        // final state of the own sequence, or (the segment ran last) of the
+        // further sequence after its last segment
+        if (a.final_state && (!has_x || xq == a.nseg - 1)) {
+            float *dst = a.final_state + (has_x ? xchain : chain) * (kP * N) + lane_off;
 #pragma unroll
             for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
         }
@@ -463,18 +529,25 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // (lane holds token i = 16it + lrow, p = 16pq + 4lgrp + 0..3)
         // prologue: Bm, Cm of sub-block 0 staged; those of sub-block 1 and dt
         // and G tiles of sub-blocks 0 and 1 in flight
-        BulkBC<N> bulk[2];   // Bm, Cm of sub-block t+1 (staged at the end of step t) and t+2
-        load_bc<N>(bulk[0], a, o, b, g, 0);
-        load_small<N, true>(small[0], a, o, b, h, g, 0, pq, lane);
-        load_small<N, true>(small[1], a, o, b, h, g, nsub > 1 ? 1 : 0, pq, lane);
-        stage_bc<N>(sm, 0, bulk[0], o);
-        load_bc<N>(bulk[1], a, o, b, g, nsub > 1 ? 1 : 0);
+        BulkBC<N> bulk[2];   // Bm, Cm of step t+1 (staged at the end of step t) and t+2
+        {
+            const int t1 = T > 1 ? 1 : 0;
+            const bool x1 = t1 >= nsub;
+            load_bc<N>(bulk[0], a, o, b, g, 0);
+            load_small<N, true>(small[0], a, o, b, h, g, 0, pq, lane);
+            load_small<N, true>(small[1], a, o, x1 ? bx : b, x1 ? hx : h, x1 ? gx : g, sb_of(t1), pq, lane);
+            stage_bc<N>(sm, 0, bulk[0], o);
+            load_bc<N>(bulk[1], a, o, x1 ? bx : b, x1 ? gx : g, sb_of(t1));
+        }
         __syncthreads();
         const unsigned char *Mb[2] = {reinterpret_cast<const unsigned char *>(sm.Mm[0]),
                                       reinterpret_cast<const unsigned char *>(sm.Mm[1])};
         auto step = [&](int t, int par, Small &sl) {
-            if (t < nsub) {
-                // decays and this wave's tiles of M for sub-block t
+            if (t < T) {
+                // decays and this wave's tiles of M for step t
+                const bool xs = t >= nsub;
+                const float Ah2 = xs ? Ahx2 : Ah2v;
+                const float Dh = xs ? Dhx : Dhv;
                 const float dt = sl.dt;
                 const float v = wave_scan(dt * Ah2);
                 wd.lam[lane] = v;
@@ -517,13 +590,16 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                     asm volatile("" : "+v"(z));
                     lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * (ti + 1))), uint2{z, z});
                 }
-                load_small<N, true>(sl, a, o, b, h, g, t + 2 < nsub ? t + 2 : nsub - 1, pq, lane);
-                load_bc<N>(bulk[par], a, o, b, g, t + 2 < nsub ? t + 2 : nsub - 1);
+                const int tl = t + 2 < T ? t + 2 : T - 1;
+                const bool xl = tl >= nsub;
+                load_small<N, true>(sl, a, o, xl ? bx : b, xl ? hx : h, xl ? gx : g, sb_of(tl), pq, lane);
+                load_bc<N>(bulk[par], a, o, xl ? bx : b, xl ? gx : g, sb_of(tl));
             }
             if (t >= 1) {
-                // outputs of sub-block s = t-1
-                const int s = t - 1;
-                const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[s % 3]);
+                // outputs of step t-1 (sub-block s)
+                const bool xo = t - 1 >= nsub;
+                const int s = sb_of(t - 1);
+                const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[(t - 1) % 3]);
                 const unsigned char *Mr = Mb[par ^ 1];
                 f32x4 Y[4];
 #pragma unroll
@@ -547,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                         if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
                 const int64_t t0 = (int64_t)s * kSub;
                 const int q = sub_tokens(a, s);
-                const rsrc_t ry = rsrc(a.y + ((b * a.L + t0) * a.H + h) * kP,
+                const rsrc_t ry = rsrc(a.y + ((( xo ? bx : b) * a.L + t0) * a.H + (xo ? hx : h)) * kP,
                                        (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
                 const int ystep = (int)(16 * a.H * kP * 2);
 #pragma unroll
@@ -556,15 +632,15 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), ry, o.gy + it * ystep, 0, 0);
                 }
             }
-            if (t + 1 < nsub) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
+            if (t + 1 < T) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
             __syncthreads();
         };
         int t = 0;
-        for (; t + 1 < nsub; t += 2) {
+        for (; t + 1 < T; t += 2) {
             step(t, 0, small[0]);
             step(t + 1, 1, small[1]);
         }
-        if (t < nsub) {
+        if (t < T) {
             step(t, 0, small[0]);
             step(t + 1, 1, small[1]);   // outputs of the last sub-block
         } else {
@@ -573,11 +649,154 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     }
 }
 
+// The state that segment q of further sequence e produces from a zero state,
+// S = sum over its sub-blocks of the state update, and log2 of its total decay
+// (the sum of dt*A over the segment, in base-2 units).  Four waves, each
+// owning 16 rows p of the state, as the state waves of pipe_kernel; only the
+// update, no outputs.  The main kernel combines these into each segment's
+// entering state: H_{q+1} = 2^(log2 decay_q) H_q + S_q.
+template <int N>
+__global__ __launch_bounds__(256, 1) void seg_state_kernel(Args a) {
+    __shared__ __align__(16) __bf16 lds_x[2][kSub * kP];
+    __shared__ __align__(16) __bf16 lds_bt[2][kSub * N];
+    __shared__ __align__(16) WaveDecays lds_wd[4];
+    using O = LaneOffs<N>;
+    constexpr int NT = N / 16;
+    const int xe = (int)blockIdx.x % a.nextra, q = (int)blockIdx.x / a.nextra;
+    const int64_t chain = a.nmain + xe;
+    const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
+    const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
+    const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
+    const float Ah2 = a.A[h] * kLog2e;
+    const int s0 = q * a.seglen, len = a.seglen;   // segments before the last are full and inside the sequence
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
+    const LaneOffs<N> o = lane_offsets<N>(tid, wave, a.H, a.G);
+    WaveDecays &wd = lds_wd[wave];
+
+    BulkX bx[2];
+    BulkBC<N> bb[2];   // only the Bm half is used
+    Small sl[2];
+    auto load = [&](int k, int slot) {
+        load_x<N>(bx[slot], a, o, b, h, s0 + k);
+        load_small<N, false>(sl[slot], a, o, b, h, g, s0 + k, 0, lane);
+        const int qn = sub_tokens(a, s0 + k);
+        const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+        const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, (int)(((int64_t)(qn - 1) * a.G * N + N) * 2));
+        const int step = (int)((256 / O::CPR) * a.G * N * 2);
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk) bb[slot].b[kk] = ld16(rb, o.gb + kk * step);
+    };
+    auto stage = [&](int slot) {
+        unsigned char *Xb = reinterpret_cast<unsigned char *>(lds_x[slot]);
+        unsigned char *Bb = reinterpret_cast<unsigned char *>(lds_bt[slot]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) lds_st<uint4>(Xb + o.sx + k * 4096, bx[slot].x[k]);
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) lds_st<uint4>(Bb + o.sb + k * (256 / O::CPR) * O::RB, bb[slot].b[k]);
+    };
+    load(0, 0);
+    load(len > 1 ? 1 : 0, 1);
+    stage(0);
+    __syncthreads();
+
+    f32x4 Hacc[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) Hacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float log2dec = 0.f;
+    auto step = [&](int k, int slot) {
+        const unsigned char *Xb = reinterpret_cast<const unsigned char *>(lds_x[slot]);
+        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(lds_bt[slot]);
+        const float dt = sl[slot].dt;
+        const float v = wave_scan(dt * Ah2);
+        const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        wd.w[lane] = ex2(lend - v) * dt;
+        const float gam = ex2(lend);
+        log2dec += lend;
+        if (k + 2 < len) load(k + 2, slot);
+        bf16x8 xf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
+            const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
+            xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int u = 0; u < NT; ++u) Hacc[u] *= gam;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp + 4]);
+            f32x4 x0, x1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x0[e] = (float)xf[ks][e] * w0[e];
+                x1[e] = (float)xf[ks][4 + e] * w1[e];
+            }
+            const bf16x8 xw = to_bf16x8(x0, x1);
+#pragma unroll
+            for (int t0 = 0; t0 < NT; t0 += 4) {
+                bf16x8 bt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bf16x4 lo = tr4(Bb + o.bt[t0 + u] + ks * 32 * O::RB);
+                    const bf16x4 hi = tr4(Bb + o.bt[t0 + u] + ks * 32 * O::RB + 4 * O::RB);
+                    bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) Hacc[t0 + u] = mfma(bt[u], xw, Hacc[t0 + u]);
+            }
+        }
+        if (k + 1 < len) stage(slot ^ 1);
+        __syncthreads();
+    };
+    int k = 0;
+    for (; k + 1 < len; k += 2) {
+        step(k, 0);
+        step(k + 1, 1);
+    }
+    if (k < len) step(k, 0);
+    float *dst = seg_state<N>(a, xe, q) + (16 * wave + lrow) * N + 4 * lgrp;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
+    if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int N>
 hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int64_t nsb = (sa.L + kSub - 1) / kSub;
     hipError_t e = launch_gram(sa, ws, nsb);
     if (e != hipSuccess) return e;
+    // One workgroup per compute unit when there are more sequences than
+    // compute units (but fewer than twice as many): each workgroup runs one
+    // sequence whole and then one segment of a remaining sequence, whose
+    // entering state comes from the segment states of a first, shorter kernel.
+    const int64_t chains = sa.B * sa.H;
+    const int cus = device_cus();
+    int nmain = (int)chains, nextra = 0, nseg = 1, seglen = (int)nsb;
+    if (cus > 0 && chains > cus && chains < 2 * (int64_t)cus && nsb >= 2) {
+        nmain = cus;
+        nextra = (int)(chains - cus);
+        nseg = cus / nextra;
+        if (nseg > nsb) nseg = (int)nsb;
+        seglen = (int)((nsb + nseg - 1) / nseg);
+        nseg = (int)((nsb + seglen - 1) / seglen);
+    }
     const size_t smem = sizeof(PipeSmem<N>);
     auto kern = pipe_kernel<N>;
     static bool configured = false;
@@ -587,8 +806,14 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
         configured = true;
     }
     Args a{(const __bf16 *)sa.x, sa.dt, sa.A, (const __bf16 *)sa.Bm, (const __bf16 *)sa.Cm, sa.D,
-           sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, sa.L, sa.H, sa.G, nsb};
-    kern<<<dim3((unsigned)(sa.B * sa.H)), kThreads, smem, sa.stream>>>(a);
+           sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, ws.ring,
+           sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
+    if (nextra > 0 && nseg > 1) {
+        seg_state_kernel<N><<<dim3((unsigned)(nextra * (nseg - 1))), 256, 0, sa.stream>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    kern<<<dim3((unsigned)nmain), kThreads, smem, sa.stream>>>(a);
     return hipGetLastError();
 }
 

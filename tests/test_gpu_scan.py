@@ -196,3 +196,29 @@ def test_nothing_is_read_past_the_sequence_end(N, Q):
         torch.cuda.synchronize()
         assert rel_err(to_np(y), y_ref) <= 2e-2
         assert rel_err(to_np(fin), f_ref) <= 2e-2
+
+
+# More (batch, head) sequences than compute units (256 on MI355X) but fewer
+# than twice as many: the pipe algorithm runs one sequence whole per
+# workgroup and spreads the rest as segments over all workgroups, with the
+# segments' entering states from a first kernel.  (B, H, L, N, regime, init)
+BALANCED = [
+    (1, 300, 1024, 128, "long_memory", True),
+    (2, 150, 320, 64, "default", True),
+    (1, 257, 64 * 9 + 5, 128, "default", False),
+    (1, 300, 65, 128, "long_memory", True),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=[f"B{c[0]}_H{c[1]}_L{c[2]}_N{c[3]}" for c in BALANCED])
+def test_more_sequences_than_compute_units(case):
+    B, H, L, N, regime, init = case
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=init, seed=900 + H, regime=regime)
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+    announce(f"balanced B{B} H{H} L{L} N{N} {regime} algo=pipe")
+    for rep in range(2):
+        y, fin = gpu_scan(dd, 256, algo="pipe")
+        ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+        print(f"    call {rep}: y err {ey:.3e}  final err {ef:.3e}", flush=True)
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
