@@ -248,6 +248,43 @@ __device__ __forceinline__ int sub_tokens(const Args &a, int sb) {
 
 // Global loads of this thread's share of sub-block sb's x (state waves) or Bm
 // and Cm (output waves), masked past the end of the sequence.
+// Loads of one sub-block given the element offset of its first row in each
+// tensor and its number of tokens q (rows past q read as zeros).
+template <int N>
+__device__ __forceinline__ void load_x_at(BulkX &sl, const Args &a, const LaneOffs<N> &o, int64_t xo, int q) {
+    const rsrc_t r = rsrc(a.x + xo, q > 0 ? (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2) : 0);
+    const int step = (int)(32 * a.H * kP * 2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) sl.x[k] = ld16(r, o.gx + k * step);
+}
+template <int N>
+__device__ __forceinline__ void load_bc_at(BulkBC<N> &sl, const Args &a, const LaneOffs<N> &o, int64_t bo, int q) {
+    using O = LaneOffs<N>;
+    const int bytes = q > 0 ? (int)(((int64_t)(q - 1) * a.G * N + N) * 2) : 0;
+    const rsrc_t rb = rsrc(a.Bm + bo, bytes);
+    const rsrc_t rc = rsrc(a.Cm + bo, bytes);
+    const int step = (int)((256 / O::CPR) * a.G * N * 2);
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) {
+        sl.b[k] = ld16(rb, o.gb + k * step);
+        sl.c[k] = ld16(rc, o.gb + k * step);
+    }
+}
+template <int N, bool kOut>
+__device__ __forceinline__ void load_small_at(Small &sl, const Args &a, const LaneOffs<N> &o, int64_t go, int64_t dof,
+                                              int q, int ow, int lane) {
+    if constexpr (kOut) {
+        const rsrc_t rg = rsrc(a.gram + go, q > 0 ? kSub * kSub * 2 : 0);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int k = ow + 4 * m < 10 ? ow + 4 * m : 9;   // waves with two tiles load their last twice
+            sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
+        }
+    }
+    const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
+    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+}
+
 template <int N>
 __device__ __forceinline__ void load_x(BulkX &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t h, int sb) {
     const int q = sub_tokens(a, sb);
@@ -353,6 +390,22 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int T = nsub + xlen;
     // sub-block of step tau, and of the step whose loads are issued at tau
     auto sb_of = [&](int tau) { return tau < nsub ? tau : seg0 + (tau - nsub); };
+    auto q_of = [&](int tau) {
+        const int rem = (int)a.L - sb_of(tau) * kSub;
+        return rem < kSub ? rem : kSub;
+    };
+    // element offsets of step tau's first row in x / y, dt, Bm / Cm and the
+    // gram tiles: the own sequence's base, or the segment's base shifted so
+    // that the step index addresses it directly
+    const int64_t SX = kSub * a.H * kP, SD = kSub * a.H, SB = kSub * a.G * N, SG = kSub * kSub;
+    const int64_t xo0 = (b * a.L * a.H + h) * kP, xo1 = (bx * a.L * a.H + hx) * kP + (int64_t)(seg0 - nsub) * SX;
+    const int64_t do0 = b * a.L * a.H + h, do1 = bx * a.L * a.H + hx + (int64_t)(seg0 - nsub) * SD;
+    const int64_t bo0 = (b * a.L * a.G + g) * N, bo1 = (bx * a.L * a.G + gx) * N + (int64_t)(seg0 - nsub) * SB;
+    const int64_t go0 = (b * a.G + g) * a.nsb * SG, go1 = (bx * a.G + gx) * a.nsb * SG + (int64_t)(seg0 - nsub) * SG;
+    auto x_at = [&](int tau) { return (tau < nsub ? xo0 : xo1) + tau * SX; };
+    auto d_at = [&](int tau) { return (tau < nsub ? do0 : do1) + tau * SD; };
+    auto b_at = [&](int tau) { return (tau < nsub ? bo0 : bo1) + tau * SB; };
+    auto g_at = [&](int tau) { return (tau < nsub ? go0 : go1) + tau * SG; };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -373,12 +426,11 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         BulkX bulk[2];   // x of step t+1 (staged at the end of step t) and t+2 (in flight)
         {
             const int t1 = T > 1 ? 1 : 0;
-            const bool x1 = t1 >= nsub;
-            load_x<N>(bulk[0], a, o, b, h, 0);
-            load_small<N, false>(small[0], a, o, b, h, g, 0, 0, lane);
-            load_small<N, false>(small[1], a, o, x1 ? bx : b, x1 ? hx : h, x1 ? gx : g, sb_of(t1), 0, lane);
+            load_x_at<N>(bulk[0], a, o, x_at(0), q_of(0));
+            load_small_at<N, false>(small[0], a, o, 0, d_at(0), q_of(0), 0, lane);
+            load_small_at<N, false>(small[1], a, o, 0, d_at(t1), q_of(t1), 0, lane);
             stage_x<N>(sm, 0, bulk[0], o);
-            load_x<N>(bulk[1], a, o, x1 ? bx : b, x1 ? hx : h, sb_of(t1));
+            load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
         }
         __syncthreads();
         f32x4 Hacc[NT];
@@ -392,34 +444,34 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                                              __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off0 + 16 * t) * 4, 0, 0));
         }
         const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
-        auto step = [&](int t, int par, Small &sl) {
+        // own sequence done: its final state out; the segment's entering state
+        // in, from the initial state and the states and log2 decays of the
+        // earlier segments (written by the segment-state kernel)
+        auto switch_to_segment = [&]() __attribute__((always_inline)) {
+            if (a.final_state) {
+                float *dst = a.final_state + chain * (kP * N) + lane_off;
+#pragma unroll
+                for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
+            }
+            {
+                const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + xchain * (kP * N)) : (const void *)a.x,
+                                       a.init ? kP * N * 4 : 0);
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    Hacc[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            ri, (lane_off + 16 * u) * 4, 0, 0));
+            }
+            for (int qq = 0; qq < xq; ++qq) {
+                const float gq = ex2(*seg_log2decay<N>(a, xe, qq));
+                const float *sq = seg_state<N>(a, xe, qq) + lane_off;
+#pragma unroll
+                for (int u = 0; u < NT; ++u) Hacc[u] = gq * Hacc[u] + *reinterpret_cast<const f32x4 *>(sq + 16 * u);
+            }
+        };
+        auto step = [&](int t, int par, Small &sl) __attribute__((always_inline)) {
             const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[t % 3]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
             const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
-            if (has_x && t == nsub) {
-                // own sequence done: its final state out; the segment's entering
-                // state in, from the initial state and the states and decays of
-                // the earlier segments (written by the segment-state kernel)
-                if (a.final_state) {
-                    float *dst = a.final_state + chain * (kP * N) + lane_off;
-#pragma unroll
-                    for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
-                }
-                {
-                    const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + xchain * (kP * N)) : (const void *)a.x,
-                                           a.init ? kP * N * 4 : 0);
-#pragma unroll
-                    for (int u = 0; u < NT; ++u)
-                        Hacc[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                ri, (lane_off + 16 * u) * 4, 0, 0));
-                }
-                for (int qq = 0; qq < xq; ++qq) {
-                    const float gq = ex2(*seg_log2decay<N>(a, xe, qq));
-                    const float *sq = seg_state<N>(a, xe, qq) + lane_off;
-#pragma unroll
-                    for (int u = 0; u < NT; ++u) Hacc[u] = gq * Hacc[u] + *reinterpret_cast<const f32x4 *>(sq + 16 * u);
-                }
-            }
             const bool xs = t >= nsub;
             const float Ah2 = xs ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
@@ -432,9 +484,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             // dt of step t+2 into the slot just read; x of step t+2
             {
                 const int tl = t + 2 < T ? t + 2 : T - 1;
-                const bool xl = tl >= nsub;
-                load_small<N, false>(sl, a, o, xl ? bx : b, xl ? hx : h, xl ? gx : g, sb_of(tl), 0, lane);
-                load_x<N>(bulk[par], a, o, xl ? bx : b, xl ? hx : h, sb_of(tl));
+                const int ql = q_of(tl);
+                load_small_at<N, false>(sl, a, o, 0, d_at(tl), ql, 0, lane);
+                load_x_at<N>(bulk[par], a, o, x_at(tl), ql);
             }
 
             // LDS reads first (the Cm fragments of the inter-block term, the x
@@ -509,12 +561,24 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             if (t + 1 < T) stage_x<N>(sm, (t + 1) % 3, bulk[par ^ 1], o);
             __syncthreads();
         };
-        int t = 0;
-        for (; t + 1 < T; t += 2) {
-            step(t, 0, small[0]);
-            step(t + 1, 1, small[1]);
+        // steps [t0, t1) with the parity of each step known at compile time
+        auto run = [&](int t0, int t1) __attribute__((always_inline)) {
+            int t = t0;
+            if ((t & 1) && t < t1) {
+                step(t, 1, small[1]);
+                ++t;
+            }
+            for (; t + 1 < t1; t += 2) {
+                step(t, 0, small[0]);
+                step(t + 1, 1, small[1]);
+            }
+            if (t < t1) step(t, 0, small[0]);
+        };
+        run(0, nsub);
+        if (has_x) {
+            switch_to_segment();
+            run(nsub, T);
         }
-        if (t < T) step(t, 0, small[0]);
         __syncthreads();   // matches the output waves' final step
         // final state of the own sequence, or (the segment ran last) of the
         // further sequence after its last segment
@@ -532,17 +596,16 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         BulkBC<N> bulk[2];   // Bm, Cm of step t+1 (staged at the end of step t) and t+2
         {
             const int t1 = T > 1 ? 1 : 0;
-            const bool x1 = t1 >= nsub;
-            load_bc<N>(bulk[0], a, o, b, g, 0);
-            load_small<N, true>(small[0], a, o, b, h, g, 0, pq, lane);
-            load_small<N, true>(small[1], a, o, x1 ? bx : b, x1 ? hx : h, x1 ? gx : g, sb_of(t1), pq, lane);
+            load_bc_at<N>(bulk[0], a, o, b_at(0), q_of(0));
+            load_small_at<N, true>(small[0], a, o, g_at(0), d_at(0), q_of(0), pq, lane);
+            load_small_at<N, true>(small[1], a, o, g_at(t1), d_at(t1), q_of(t1), pq, lane);
             stage_bc<N>(sm, 0, bulk[0], o);
-            load_bc<N>(bulk[1], a, o, x1 ? bx : b, x1 ? gx : g, sb_of(t1));
+            load_bc_at<N>(bulk[1], a, o, b_at(t1), q_of(t1));
         }
         __syncthreads();
         const unsigned char *Mb[2] = {reinterpret_cast<const unsigned char *>(sm.Mm[0]),
                                       reinterpret_cast<const unsigned char *>(sm.Mm[1])};
-        auto step = [&](int t, int par, Small &sl) {
+        auto step = [&](int t, int par, Small &sl) __attribute__((always_inline)) {
             if (t < T) {
                 // decays and this wave's tiles of M for step t
                 const bool xs = t >= nsub;
@@ -591,13 +654,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                     lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * (ti + 1))), uint2{z, z});
                 }
                 const int tl = t + 2 < T ? t + 2 : T - 1;
-                const bool xl = tl >= nsub;
-                load_small<N, true>(sl, a, o, xl ? bx : b, xl ? hx : h, xl ? gx : g, sb_of(tl), pq, lane);
-                load_bc<N>(bulk[par], a, o, xl ? bx : b, xl ? gx : g, sb_of(tl));
+                const int ql = q_of(tl);
+                load_small_at<N, true>(sl, a, o, g_at(tl), d_at(tl), ql, pq, lane);
+                load_bc_at<N>(bulk[par], a, o, b_at(tl), ql);
             }
             if (t >= 1) {
                 // outputs of step t-1 (sub-block s)
-                const bool xo = t - 1 >= nsub;
                 const int s = sb_of(t - 1);
                 const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[(t - 1) % 3]);
                 const unsigned char *Mr = Mb[par ^ 1];
@@ -621,10 +683,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
-                const int64_t t0 = (int64_t)s * kSub;
-                const int q = sub_tokens(a, s);
-                const rsrc_t ry = rsrc(a.y + ((( xo ? bx : b) * a.L + t0) * a.H + (xo ? hx : h)) * kP,
-                                       (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
+                const int q = q_of(t - 1);
+                const rsrc_t ry = rsrc(a.y + x_at(t - 1), (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
                 const int ystep = (int)(16 * a.H * kP * 2);
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
