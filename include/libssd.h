@@ -80,7 +80,8 @@ typedef enum {
     SSD_ALGO_STAGED = 2,      /* bf16 matrix cores: block states, state pass, block outputs */
     SSD_ALGO_FUSED = 3,       /* bf16 matrix cores, one pass: states handed from block to block */
     SSD_ALGO_CHAIN = 4,       /* bf16 matrix cores, one workgroup per (batch, head) sequence */
-    SSD_ALGO_PIPE = 5         /* as CHAIN, eight waves in two roles (state / outputs) per sequence */
+    SSD_ALGO_PIPE = 5,        /* as CHAIN, eight waves in two roles (state / outputs) per sequence */
+    SSD_ALGO_PAIR = 6         /* as CHAIN, one workgroup per two adjacent heads sharing Bm / Cm */
 } ssd_algo;
 
 /* Human-readable name of a status code (static storage). */
@@ -134,8 +135,9 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
  * algorithm that does not cover the shape or dtype returns
  * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16 and
  * P == 64; SSD_ALGO_STAGED takes N in {64, 128, 256}, SSD_ALGO_FUSED,
- * SSD_ALGO_CHAIN and SSD_ALGO_PIPE N in {64, 128}).  SSD_ALGO_CHAIN and
- * SSD_ALGO_PIPE walk every (batch, head) sequence in 64-token steps whatever
+ * SSD_ALGO_CHAIN, SSD_ALGO_PIPE and SSD_ALGO_PAIR N in {64, 128}; SSD_ALGO_PAIR
+ * also needs H and H / G even).  SSD_ALGO_CHAIN, SSD_ALGO_PIPE and
+ * SSD_ALGO_PAIR walk every (batch, head) sequence in 64-token steps whatever
  * chunk_size is (the result is the same up to rounding); SSD_ALGO_AUTO picks
  * SSD_ALGO_PIPE when B * H >= 160.
  */

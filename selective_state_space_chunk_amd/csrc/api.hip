@@ -17,6 +17,8 @@ hipError_t launch_chain_scan(const ScanArgs &a, const Workspace &ws);
 bool chain_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
 bool pipe_supported(int64_t H, int64_t G, int64_t N);
+hipError_t launch_pair_scan(const ScanArgs &a, const Workspace &ws);
+bool pair_supported(int64_t H, int64_t G, int64_t N);
 }
 
 namespace {
@@ -109,14 +111,16 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
-        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE)
+        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE && algo != SSD_ALGO_PAIR)
         return SSD_ERR_UNSUPPORTED;
     const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
-    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN || algo == SSD_ALGO_PIPE) &&
+    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN || algo == SSD_ALGO_PIPE ||
+         algo == SSD_ALGO_PAIR) &&
         !mfma_ok)
         return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_CHAIN && !chain_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_PIPE && !pipe_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_PAIR && !pair_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && !fused_supported(H, G, N, Q)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && B * H * ((L + Q - 1) / Q) > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
 
@@ -162,6 +166,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         case SSD_ALGO_FUSED: e = launch_fused_scan(a, ws); break;
         case SSD_ALGO_CHAIN: e = launch_chain_scan(a, ws); break;
         case SSD_ALGO_PIPE: e = launch_pipe_scan(a, ws); break;
+        case SSD_ALGO_PAIR: e = launch_pair_scan(a, ws); break;
         default: return SSD_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

@@ -11,7 +11,12 @@ from gpu_util import TOL, announce, gpu_scan, oracle_scan, rel_err, to_device, t
 
 pytestmark = pytest.mark.gpu
 
-MFMA_ALGOS = ["reference", "staged", "fused", "chain", "pipe"]
+MFMA_ALGOS = ["reference", "staged", "fused", "chain", "pipe", "pair"]
+
+
+def covers(algo, H, G):
+    """The pair algorithm takes heads two at a time within one group."""
+    return algo != "pair" or (H % 2 == 0 and (H // G) % 2 == 0)
 
 # (name, B, L, H, P, N, G, chunk, dtype, init, regime, algos)
 SMALL = [
@@ -34,7 +39,7 @@ def test_small_shapes_match_oracle(case):
     d = si.make_scan_inputs(B, L, H, P, N, G, dtype=dtype, init=init, seed=1000 + L, regime=regime)
     y_ref, f_ref = oracle_scan(d)
     dd = to_device(d, dtype)
-    for algo in algos:
+    for algo in [a for a in algos if covers(a, H, G)]:
         announce(f"{name} B{B} L{L} H{H} P{P} N{N} G{G} Q{Q} {dtype} algo={algo}")
         y, fin = gpu_scan(dd, Q, algo=algo)
         ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
@@ -76,7 +81,7 @@ def test_chunk_size_independence_on_gpu():
     dd = to_device(d, "bf16")
     outs = []
     for Q in (64, 128, 256):
-        for algo in ("staged", "fused", "chain", "pipe"):
+        for algo in ("staged", "fused", "chain", "pipe", "pair"):
             announce(f"chunk independence Q{Q} algo={algo}")
             y, fin = gpu_scan(dd, Q, algo=algo)
             outs.append((to_np(y), to_np(fin)))
@@ -86,7 +91,7 @@ def test_chunk_size_independence_on_gpu():
         assert rel_err(y, outs[0][0]) <= 2e-2 and rel_err(fin, outs[0][1]) <= 2e-2
 
 
-@pytest.mark.parametrize("algo", ["reference", "staged", "fused", "chain", "pipe"])
+@pytest.mark.parametrize("algo", ["reference", "staged", "fused", "chain", "pipe", "pair"])
 def test_split_resume_on_gpu(algo):
     """Running the first k tokens, then the rest from the returned state,
     matches one run over the whole sequence."""
@@ -186,7 +191,7 @@ def test_nothing_is_read_past_the_sequence_end(N, Q):
     for name in ("x", "dt", "Bm", "Cm"):
         dd[name] = padded(dd[name])
         assert dd[name].is_contiguous()
-    algos = ["reference", "staged"] + (["fused", "chain", "pipe"] if N <= 128 else [])
+    algos = ["reference", "staged"] + (["fused", "chain", "pipe", "pair"] if N <= 128 else [])
     for algo in algos:
         announce(f"NaN past the end N{N} Q{Q} L{L} algo={algo}")
         y = torch.full_like(dd["x"], float("nan"))
@@ -222,3 +227,40 @@ def test_more_sequences_than_compute_units(case):
         ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
         print(f"    call {rep}: y err {ey:.3e}  final err {ef:.3e}", flush=True)
         assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+# Pairs of adjacent heads per workgroup: odd numbers of pairs, several batch
+# rows and groups, ragged and sub-block-short sequences, zero initial state.
+# (B, L, H, G, N, regime, init)
+PAIRS = [
+    (1, 64, 2, 1, 128, "default", True),
+    (3, 37, 6, 3, 128, "long_memory", True),
+    (2, 1000, 10, 1, 64, "long_memory", False),
+    (2, 4096 + 17, 4, 2, 128, "long_memory", True),
+    (1, 333, 18, 1, 128, "no_decay", True),
+]
+
+
+@pytest.mark.parametrize("case", PAIRS, ids=[f"B{c[0]}_L{c[1]}_H{c[2]}_G{c[3]}_N{c[4]}" for c in PAIRS])
+def test_pair_matches_oracle(case):
+    B, L, H, G, N, regime, init = case
+    d = si.make_scan_inputs(B, L, H, 64, N, G, dtype="bf16", init=init, seed=1300 + L + H, regime=regime)
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+    announce(f"pair B{B} L{L} H{H} G{G} N{N} {regime} algo=pair")
+    for rep in range(2):
+        y, fin = gpu_scan(dd, 256, algo="pair")
+        ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+        print(f"    call {rep}: y err {ey:.3e}  final err {ef:.3e}", flush=True)
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_pair_rejects_odd_head_counts():
+    import selective_state_space_chunk_amd as ssd
+    for H, G in ((3, 1), (6, 6)):
+        d = si.make_scan_inputs(1, 100, H, 64, 128, G, dtype="bf16", init=False, seed=7)
+        dd = to_device(d, "bf16")
+        announce(f"pair unsupported H{H} G{G}")
+        with pytest.raises(ssd.SSDError) as ei:
+            gpu_scan(dd, 256, algo="pair")
+        assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
