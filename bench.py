@@ -246,7 +246,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_fetch, "write_scale_bytes_per_kib": f_write, "kernels": {}}
     total = 0.0
-    for name in ("pipe_kernel", "seg_state_kernel", "chain_kernel", "scan_fused", "gram_kernel", "scan_mfma", "ref_"):
+    for name in ("pipe_kernel", "prep_kernel", "seg_state_kernel", "chain_kernel", "scan_fused", "gram_kernel", "scan_mfma", "ref_"):
         try:
             fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
             wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)
@@ -320,7 +320,7 @@ def main():
                    "init_state": bool(w.init), "parallelism": "single_gpu"},
         "kernel_ms": {"mean": kern_ms, "median": per[len(per) // 2], "p10": per[len(per) // 10],
                       "p90": per[(9 * len(per)) // 10]},
-        "roofline": {"bound": "hbm", "kernels": "gram_kernel + seg_state_kernel<128> + pipe_kernel<128> (one ssd_chunk_scan_fwd call)",
+        "roofline": {"bound": "hbm", "kernels": "prep_kernel<128> (segment states and gram tiles) + pipe_kernel<128> (one ssd_chunk_scan_fwd call)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic() if headline else None,
                      "algorithmic_bytes": byts, "algorithmic_flops": flops,

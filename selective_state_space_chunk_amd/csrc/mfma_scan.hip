@@ -39,6 +39,7 @@
 //   kOutput  the outputs of each block from the state entering it (read from
 //            the workspace, where the pass kernel put it).
 #include "common.h"
+#include "tile_ops.h"
 
 namespace ssd {
 namespace {
@@ -85,44 +86,13 @@ __device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
     jt = k - (it * (it + 1)) / 2;
 }
 
-// ---------------------------------------------------------------------------
-// Gram kernel: G[i][j] = Cm_i . Bm_j for every 64-token block and group, the
-// causal 16x16 tiles only (the others are never read), bf16.  Storage is in
-// matrix-core fragment order so that a wave reads a tile as one contiguous
-// 512-byte run: tile k (0..9, see tile_of) holds, for lane l = 16*lgrp + lrow,
-// G[16*it + lrow][16*jt + 4*lgrp + 0..3] at elements (64*k + l)*4 .. +3.
-// ---------------------------------------------------------------------------
+// Gram kernel: one workgroup per (sub-block, batch * group); see tile::gram_block.
 template <int N>
 __global__ __launch_bounds__(kThreads) void gram_kernel(const __bf16 *__restrict__ Bm,
                                                         const __bf16 *__restrict__ Cm,
                                                         __bf16 *__restrict__ gram, int64_t L,
                                                         int64_t G, int64_t nsb) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lrow = lane & 15, lgrp = lane >> 4;
-    const int64_t sbg = blockIdx.x, bg = blockIdx.y;
-    const int64_t b = bg / G, g = bg % G;
-    const int64_t t_base = sbg * kSub;
-    __bf16 *out = gram + (bg * nsb + sbg) * (int64_t)(kSub * kSub);
-    for (int k = wave; k < 10; k += 4) {
-        int it, jt;
-        tile_of(k, it, jt);
-        const int64_t tj = t_base + 16 * jt + lrow, ti = t_base + 16 * it + lrow;
-        const __bf16 *brow = Bm + ((b * L + tj) * G + g) * N;
-        const __bf16 *crow = Cm + ((b * L + ti) * G + g) * N;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < N / 32; ++ks) {
-            const int n0 = 32 * ks + 8 * lgrp;
-            bf16x8 ab = {}, bc = {};
-            if (tj < L) ab = *reinterpret_cast<const bf16x8 *>(brow + n0);
-            if (ti < L) bc = *reinterpret_cast<const bf16x8 *>(crow + n0);
-            acc = mfma(ab, bc, acc);          // rows j, column i
-        }
-        uint2 pk;
-        pk.x = pack2(acc[0], acc[1]);
-        pk.y = pack2(acc[2], acc[3]);
-        *reinterpret_cast<uint2 *>(out + (k * 64 + lane) * 4) = pk;
-    }
+    tile::gram_block<N>(Bm, Cm, gram, L, G, nsb, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -561,13 +561,13 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 // update, no outputs.  The main kernel combines these into each segment's
 // entering state: H_{q+1} = 2^(log2 decay_q) H_q + S_q.
 template <int N>
-__global__ __launch_bounds__(256, 1) void seg_state_kernel(Args a) {
+__device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     __shared__ __align__(16) __bf16 lds_x[2][kSub * kP];
     __shared__ __align__(16) __bf16 lds_bt[2][kSub * N];
     __shared__ __align__(16) WaveDecays lds_wd[4];
     using O = LaneOffs<N>;
     constexpr int NT = N / 16;
-    const int xe = (int)blockIdx.x % a.nextra, q = (int)blockIdx.x / a.nextra;
+    const int xe = blk % a.nextra, q = blk / a.nextra;
     const int64_t chain = a.nmain + xe;
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
@@ -669,6 +669,19 @@ __global__ __launch_bounds__(256, 1) void seg_state_kernel(Args a) {
     if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
 }
 
+// The work that must precede pipe_kernel when there are segments, in one
+// launch so that the two parts share the device: workgroups below nsegwg
+// compute segment states, the others one sub-block's gram tiles each.
+template <int N>
+__global__ __launch_bounds__(256) void prep_kernel(Args a, int nsegwg) {
+    if ((int)blockIdx.x < nsegwg) {
+        seg_state_block<N>(a, blockIdx.x);
+    } else {
+        const int64_t k = (int64_t)blockIdx.x - nsegwg;
+        gram_block<N>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb, threadIdx.x);
+    }
+}
+
 // Number of compute units of the current device (cached per device).
 int device_cus() {
     static int cached[64] = {0};
@@ -685,8 +698,7 @@ int device_cus() {
 template <int N>
 hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int64_t nsb = (sa.L + kSub - 1) / kSub;
-    hipError_t e = launch_gram(sa, ws, nsb);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     // One workgroup per compute unit when there are more sequences than
     // compute units (but fewer than twice as many): each workgroup runs one
     // sequence whole and then one segment of a remaining sequence, whose
@@ -714,10 +726,14 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
            sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, ws.ring,
            sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
     if (nextra > 0 && nseg > 1) {
-        seg_state_kernel<N><<<dim3((unsigned)(nextra * (nseg - 1))), 256, 0, sa.stream>>>(a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const int nsegwg = nextra * (nseg - 1);
+        prep_kernel<N><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 256, 0, sa.stream>>>(a, nsegwg);
+    } else {
+        e = launch_gram(sa, ws, nsb);
     }
+    if (e != hipSuccess) return e;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)nmain), kThreads, smem, sa.stream>>>(a);
     return hipGetLastError();
 }
