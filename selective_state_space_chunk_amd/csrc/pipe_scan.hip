@@ -556,17 +556,18 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 
 // The state that segment q of further sequence e produces from a zero state,
 // S = sum over its sub-blocks of the state update, and log2 of its total decay
-// (the sum of dt*A over the segment, in base-2 units).  Four waves, each
-// owning 16 rows p of the state, as the state waves of pipe_kernel; only the
-// update, no outputs.  The main kernel combines these into each segment's
-// entering state: H_{q+1} = 2^(log2 decay_q) H_q + S_q.
+// (the sum of dt*A over the segment, in base-2 units).  Eight waves: wave w
+// owns rows p = 16 (w % 4) .. +15 and the n-tiles of half w / 4 of the state,
+// with pipe_kernel's update step; no outputs.  The main kernel combines these
+// into each segment's entering state: H_{q+1} = 2^(log2 decay_q) H_q + S_q.
 template <int N>
 __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     __shared__ __align__(16) __bf16 lds_x[2][kSub * kP];
     __shared__ __align__(16) __bf16 lds_bt[2][kSub * N];
-    __shared__ __align__(16) WaveDecays lds_wd[4];
+    __shared__ __align__(16) float lds_w[8][kSub];
     using O = LaneOffs<N>;
-    constexpr int NT = N / 16;
+    constexpr int NT = N / 16, NH = NT / 2;   // n-tiles in all, per wave
+    constexpr int KB = N / 64;                // Bm chunks staged per thread
     const int xe = blk % a.nextra, q = blk / a.nextra;
     const int64_t chain = a.nmain + xe;
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
@@ -577,47 +578,49 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pq = wave & 3, nh = wave >> 2;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, wave, a.H, a.G);
-    WaveDecays &wd = lds_wd[wave];
+    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
+    float *wrow = lds_w[wave];
 
-    BulkX bx[2];
-    BulkBC<N> bb[2];   // only the Bm half is used
-    Small sl[2];
-    auto load = [&](int k, int slot) {
-        load_x<N>(bx[slot], a, o, b, h, s0 + k);
-        load_small<N, false>(sl[slot], a, o, b, h, g, s0 + k, 0, lane);
+    // thread (u = tid % 256, half nh) stages x chunk nh and Bm chunks nh*KB .. +KB-1 of u
+    uint4 xr[2], br[2][KB];
+    float dts[2];
+    auto load = [&](int k, int slot) __attribute__((always_inline)) {
         const int qn = sub_tokens(a, s0 + k);
         const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+        const rsrc_t rx = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(qn - 1) * a.H * kP + kP) * 2));
+        xr[slot] = ld16(rx, o.gx + nh * (int)(32 * a.H * kP * 2));
         const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, (int)(((int64_t)(qn - 1) * a.G * N + N) * 2));
         const int step = (int)((256 / O::CPR) * a.G * N * 2);
 #pragma unroll
-        for (int kk = 0; kk < N / 32; ++kk) bb[slot].b[kk] = ld16(rb, o.gb + kk * step);
+        for (int kk = 0; kk < KB; ++kk) br[slot][kk] = ld16(rb, o.gb + (nh * KB + kk) * step);
+        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
+        dts[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
     };
-    auto stage = [&](int slot) {
+    auto stage = [&](int slot) __attribute__((always_inline)) {
         unsigned char *Xb = reinterpret_cast<unsigned char *>(lds_x[slot]);
         unsigned char *Bb = reinterpret_cast<unsigned char *>(lds_bt[slot]);
+        lds_st<uint4>(Xb + o.sx + nh * 4096, xr[slot]);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) lds_st<uint4>(Xb + o.sx + k * 4096, bx[slot].x[k]);
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) lds_st<uint4>(Bb + o.sb + k * (256 / O::CPR) * O::RB, bb[slot].b[k]);
+        for (int kk = 0; kk < KB; ++kk) lds_st<uint4>(Bb + o.sb + (nh * KB + kk) * (256 / O::CPR) * O::RB, br[slot][kk]);
     };
     load(0, 0);
     load(len > 1 ? 1 : 0, 1);
     stage(0);
     __syncthreads();
 
-    f32x4 Hacc[NT];
+    f32x4 Hacc[NH];
 #pragma unroll
-    for (int u = 0; u < NT; ++u) Hacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NH; ++u) Hacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     float log2dec = 0.f;
-    auto step = [&](int k, int slot) {
+    auto step = [&](int k, int slot) __attribute__((always_inline)) {
         const unsigned char *Xb = reinterpret_cast<const unsigned char *>(lds_x[slot]);
         const unsigned char *Bb = reinterpret_cast<const unsigned char *>(lds_bt[slot]);
-        const float dt = sl[slot].dt;
+        const float dt = dts[slot];
         const float v = wave_scan(dt * Ah2);
         const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-        wd.w[lane] = ex2(lend - v) * dt;
+        wrow[lane] = ex2(lend - v) * dt;
         const float gam = ex2(lend);
         log2dec += lend;
         if (k + 2 < len) load(k + 2, slot);
@@ -629,11 +632,11 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
             xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
-        for (int u = 0; u < NT; ++u) Hacc[u] *= gam;
+        for (int u = 0; u < NH; ++u) Hacc[u] *= gam;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp]);
-            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp + 4]);
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&wrow[32 * ks + 8 * lgrp]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&wrow[32 * ks + 8 * lgrp + 4]);
             f32x4 x0, x1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -641,18 +644,16 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
                 x1[e] = (float)xf[ks][4 + e] * w1[e];
             }
             const bf16x8 xw = to_bf16x8(x0, x1);
+            bf16x8 bt[NH];
 #pragma unroll
-            for (int t0 = 0; t0 < NT; t0 += 4) {
-                bf16x8 bt[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const bf16x4 lo = tr4(Bb + o.bt[t0 + u] + ks * 32 * O::RB);
-                    const bf16x4 hi = tr4(Bb + o.bt[t0 + u] + ks * 32 * O::RB + 4 * O::RB);
-                    bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) Hacc[t0 + u] = mfma(bt[u], xw, Hacc[t0 + u]);
+            for (int u = 0; u < NH; ++u) {
+                const int bo = nh ? o.bt[NH + u] : o.bt[u];   // (no run-time index into o)
+                const bf16x4 lo = tr4(Bb + bo + ks * 32 * O::RB);
+                const bf16x4 hi = tr4(Bb + bo + ks * 32 * O::RB + 4 * O::RB);
+                bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+#pragma unroll
+            for (int u = 0; u < NH; ++u) Hacc[u] = mfma(bt[u], xw, Hacc[u]);
         }
         if (k + 1 < len) stage(slot ^ 1);
         __syncthreads();
@@ -663,9 +664,9 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
         step(k + 1, 1);
     }
     if (k < len) step(k, 0);
-    float *dst = seg_state<N>(a, xe, q) + (16 * wave + lrow) * N + 4 * lgrp;
+    float *dst = seg_state<N>(a, xe, q) + (16 * pq + lrow) * N + 4 * lgrp + 16 * nh * NH;
 #pragma unroll
-    for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
+    for (int u = 0; u < NH; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
     if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
 }
 
@@ -673,12 +674,13 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
 // launch so that the two parts share the device: workgroups below nsegwg
 // compute segment states, the others one sub-block's gram tiles each.
 template <int N>
-__global__ __launch_bounds__(256) void prep_kernel(Args a, int nsegwg) {
+__global__ __launch_bounds__(512) void prep_kernel(Args a, int nsegwg) {
     if ((int)blockIdx.x < nsegwg) {
         seg_state_block<N>(a, blockIdx.x);
     } else {
         const int64_t k = (int64_t)blockIdx.x - nsegwg;
-        gram_block<N>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb, threadIdx.x);
+        gram_block<N, 8>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb,
+                         threadIdx.x);
     }
 }
 
@@ -727,7 +729,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
            sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
     if (nextra > 0 && nseg > 1) {
         const int nsegwg = nextra * (nseg - 1);
-        prep_kernel<N><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 256, 0, sa.stream>>>(a, nsegwg);
+        prep_kernel<N><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 512, 0, sa.stream>>>(a, nsegwg);
     } else {
         e = launch_gram(sa, ws, nsb);
     }

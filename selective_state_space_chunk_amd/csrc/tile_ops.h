@@ -187,8 +187,8 @@ __device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, 
 // is in matrix-core fragment order so that a wave reads a tile as one
 // contiguous 512-byte run: tile k (0..9, see tile_of) holds, for lane
 // l = 16*lgrp + lrow, G[16*it + lrow][16*jt + 4*lgrp + 0..3] at elements
-// (64*k + l)*4 .. +3.  Called by the four waves of a 256-thread workgroup.
-template <int N>
+// (64*k + l)*4 .. +3.  Called by the NW waves of a workgroup.
+template <int N, int NW = 4>
 __device__ __forceinline__ void gram_block(const __bf16 *__restrict__ Bm, const __bf16 *__restrict__ Cm,
                                            __bf16 *__restrict__ gram, int64_t L, int64_t G, int64_t nsb,
                                            int64_t sbg, int64_t bg, int tid) {
@@ -197,7 +197,7 @@ __device__ __forceinline__ void gram_block(const __bf16 *__restrict__ Bm, const 
     const int64_t b = bg / G, g = bg % G;
     const int64_t t_base = sbg * kSub;
     __bf16 *out = gram + (bg * nsb + sbg) * (int64_t)(kSub * kSub);
-    for (int k = wave; k < 10; k += 4) {
+    for (int k = wave; k < 10; k += NW) {
         int it, jt;
         tile_of(k, it, jt);
         const int64_t tj = t_base + 16 * jt + lrow, ti = t_base + 16 * it + lrow;
