@@ -41,7 +41,7 @@ WORKLOAD_NAMES = {"m2_2p7b": "mamba2_2.7b_layer_ssd_chunk_scan", "m2_130m": "mam
                   "tiny_fp32": "tiny_fp32_ssd_chunk_scan", "long_n128": "long_sequence_n128_ssd_chunk_scan",
                   "long_n256": "long_sequence_n256_ssd_chunk_scan"}
 # the sources whose kernels run in one scan launch at this workload
-SCAN_SOURCES = ["pipe_scan.hip", "mfma_scan.hip", "api.hip", "common.h"]
+SCAN_SOURCES = ["pipe_scan.hip", "tile_ops.h", "mfma_scan.hip", "api.hip", "common.h"]
 
 
 def scan_sources_digest() -> str:
