@@ -138,8 +138,9 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
  * SSD_ALGO_CHAIN, SSD_ALGO_PIPE and SSD_ALGO_PAIR N in {64, 128}; SSD_ALGO_PAIR
  * also needs H and H / G even).  SSD_ALGO_CHAIN, SSD_ALGO_PIPE and
  * SSD_ALGO_PAIR walk every (batch, head) sequence in 64-token steps whatever
- * chunk_size is (the result is the same up to rounding); SSD_ALGO_AUTO picks
- * SSD_ALGO_PIPE when B * H >= 160.
+ * chunk_size is (the result is the same up to rounding).  SSD_ALGO_PIPE spreads
+ * few sequences over the device in time segments; SSD_ALGO_AUTO picks it
+ * wherever it covers the shape.
  */
 ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A,
                                    const void *Bm, const void *Cm, const float *D,

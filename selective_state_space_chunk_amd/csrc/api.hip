@@ -41,7 +41,11 @@ bool shape_supported(int64_t P, int64_t N, int64_t Q) {
 
 struct Layout {
     size_t states, decay, flags, counters, ring, gram, total;
+    size_t ring_floats;
 };
+
+// Segment states the workspace holds for the per-sequence scan.
+constexpr int64_t kSegStates = 256;
 
 // Most (batch, head) chains the hand-off flags cover; scans are limited to it.
 constexpr int64_t kMaxChains = 65535;
@@ -57,7 +61,12 @@ Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, 
     l.flags = off;    off = align_up(off + (size_t)kMaxChains * sizeof(unsigned));
     l.states = off;   off = align_up(off + (size_t)(B * nc * H * P * N) * sizeof(float));
     l.decay = off;    off = align_up(off + (size_t)(B * H * nc) * sizeof(float));
-    l.ring = off;     off = align_up(off + (size_t)(B * H * 2 * P * N) * sizeof(float));
+    // the ring also holds the segment states of the per-sequence matrix-core
+    // scan (P = 64, N <= 128): room for 256 of them, one per compute unit
+    const int64_t seg_floats = (P == 64 && (N == 64 || N == 128)) ? kSegStates * (P * N + 1) : 0;
+    const int64_t ring_floats = B * H * 2 * P * N > seg_floats ? B * H * 2 * P * N : seg_floats;
+    l.ring = off;     off = align_up(off + (size_t)ring_floats * sizeof(float));
+    l.ring_floats = (size_t)ring_floats;
     l.gram = off;     off = align_up(off + gram_bytes(B, L, G, Q));
     l.total = off;
     return l;
@@ -71,6 +80,7 @@ Workspace carve(void *base, const Layout &l) {
     w.flags = (unsigned *)(p + l.flags);
     w.counters = (unsigned *)(p + l.counters);
     w.ring = (float *)(p + l.ring);
+    w.ring_floats = l.ring_floats;
     w.gram = (void *)(p + l.gram);
     return w;
 }
@@ -149,10 +159,10 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
             algo = SSD_ALGO_REFERENCE;
         } else {
             const int64_t nc = (L + Q - 1) / Q;
-            // one workgroup per (batch, head) sequence when there are enough
-            // sequences to occupy the device; else one pass while chains of
-            // blocks are short and many; staged otherwise
-            if (pipe_supported(H, G, N) && B * H >= 160)
+            // per-sequence scan (spread over the device in time segments when
+            // sequences are few) wherever it covers the shape; else one pass
+            // while chains of blocks are short and many; staged otherwise
+            if (pipe_supported(H, G, N))
                 algo = SSD_ALGO_PIPE;
             else
                 algo = (nc <= 64 && fused_supported(H, G, N, Q) && B * H >= 64 && B * H * nc <= 0x7fffffff)

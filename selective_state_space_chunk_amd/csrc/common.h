@@ -74,7 +74,8 @@ struct Workspace {
     float *decay;       // [B, H, nc]          exp(sum of dt*A over the block)
     unsigned *flags;    // hand-off flags of the one-pass algorithm
     unsigned *counters; // ticket and completion counters of the one-pass algorithm
-    float *ring;        // [B*H, 2, P, N] states handed from block to block
+    float *ring;        // [B*H, 2, P, N] states handed from block to block, or segment states
+    size_t ring_floats; // floats in ring
     void *gram;         // [B*G, nsb, 64, 64] bf16 Cm.Bm^T of every 64-token block
 };
 

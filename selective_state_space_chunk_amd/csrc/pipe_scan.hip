@@ -63,7 +63,7 @@ struct Args {
     const __bf16 *gram;
     float *seg;              // segment states [nextra][nseg-1][P][N], then their log2 decays [nextra][nseg-1]
     int64_t L, H, G, nsb;
-    int nmain;               // workgroups of the main kernel, one own sequence each
+    int nmain;               // sequences run whole, one per workgroup (0: every sequence is cut)
     int nextra;              // further sequences, each cut into nseg segments of seglen sub-blocks;
     int nseg, seglen;        //   segment q of extra sequence e runs on workgroup q*nextra + e
 };
@@ -194,10 +194,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     constexpr int NT = N / 16;
     constexpr int KS = N / 32;
 
-    // this workgroup's own sequence (steps 0..nsub-1) and, after it, segment xq
-    // of a further sequence (steps nsub..T-1, sub-blocks seg0..seg0+xlen-1)
+    // this workgroup's own sequence (steps 0..nown-1; none when nmain is 0) and,
+    // after it, segment xq of a further sequence (steps nown..T-1, sub-blocks
+    // seg0..seg0+xlen-1)
     const int nsub = (int)((a.L + kSub - 1) / kSub);
-    const int64_t chain = xcd_chain(blockIdx.x, a.nmain);
+    const int nown = a.nmain > 0 ? nsub : 0;
+    const int64_t chain = a.nmain > 0 ? xcd_chain(blockIdx.x, a.nmain) : (int64_t)blockIdx.x % a.nextra;
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
@@ -212,9 +214,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const float Ahx2 = a.A[hx] * kLog2e, Dhx = a.D[hx];
     const int seg0 = xq * a.seglen;
     const int xlen = has_x ? (nsub - seg0 < a.seglen ? nsub - seg0 : a.seglen) : 0;
-    const int T = nsub + xlen;
+    const int T = nown + xlen;
     // sub-block of step tau, and of the step whose loads are issued at tau
-    auto sb_of = [&](int tau) { return tau < nsub ? tau : seg0 + (tau - nsub); };
+    auto sb_of = [&](int tau) { return tau < nown ? tau : seg0 + (tau - nown); };
     auto q_of = [&](int tau) {
         const int rem = (int)a.L - sb_of(tau) * kSub;
         return rem < kSub ? rem : kSub;
@@ -223,14 +225,14 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     // gram tiles: the own sequence's base, or the segment's base shifted so
     // that the step index addresses it directly
     const int64_t SX = kSub * a.H * kP, SD = kSub * a.H, SB = kSub * a.G * N, SG = kSub * kSub;
-    const int64_t xo0 = (b * a.L * a.H + h) * kP, xo1 = (bx * a.L * a.H + hx) * kP + (int64_t)(seg0 - nsub) * SX;
-    const int64_t do0 = b * a.L * a.H + h, do1 = bx * a.L * a.H + hx + (int64_t)(seg0 - nsub) * SD;
-    const int64_t bo0 = (b * a.L * a.G + g) * N, bo1 = (bx * a.L * a.G + gx) * N + (int64_t)(seg0 - nsub) * SB;
-    const int64_t go0 = (b * a.G + g) * a.nsb * SG, go1 = (bx * a.G + gx) * a.nsb * SG + (int64_t)(seg0 - nsub) * SG;
-    auto x_at = [&](int tau) { return (tau < nsub ? xo0 : xo1) + tau * SX; };
-    auto d_at = [&](int tau) { return (tau < nsub ? do0 : do1) + tau * SD; };
-    auto b_at = [&](int tau) { return (tau < nsub ? bo0 : bo1) + tau * SB; };
-    auto g_at = [&](int tau) { return (tau < nsub ? go0 : go1) + tau * SG; };
+    const int64_t xo0 = (b * a.L * a.H + h) * kP, xo1 = (bx * a.L * a.H + hx) * kP + (int64_t)(seg0 - nown) * SX;
+    const int64_t do0 = b * a.L * a.H + h, do1 = bx * a.L * a.H + hx + (int64_t)(seg0 - nown) * SD;
+    const int64_t bo0 = (b * a.L * a.G + g) * N, bo1 = (bx * a.L * a.G + gx) * N + (int64_t)(seg0 - nown) * SB;
+    const int64_t go0 = (b * a.G + g) * a.nsb * SG, go1 = (bx * a.G + gx) * a.nsb * SG + (int64_t)(seg0 - nown) * SG;
+    auto x_at = [&](int tau) { return (tau < nown ? xo0 : xo1) + tau * SX; };
+    auto d_at = [&](int tau) { return (tau < nown ? do0 : do1) + tau * SD; };
+    auto b_at = [&](int tau) { return (tau < nown ? bo0 : bo1) + tau * SB; };
+    auto g_at = [&](int tau) { return (tau < nown ? go0 : go1) + tau * SG; };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // in, from the initial state and the states and log2 decays of the
         // earlier segments (written by the segment-state kernel)
         auto switch_to_segment = [&]() __attribute__((always_inline)) {
-            if (a.final_state) {
+            if (a.final_state && nown > 0) {
                 float *dst = a.final_state + chain * (kP * N) + lane_off;
 #pragma unroll
                 for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[t % 3]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
             const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
-            const bool xs = t >= nsub;
+            const bool xs = t >= nown;
             const float Ah2 = xs ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
             const float dt = sl.dt;
@@ -399,10 +401,10 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             }
             if (t < t1) step(t, 0, small[0]);
         };
-        run(0, nsub);
+        run(0, nown);
         if (has_x) {
             switch_to_segment();
-            run(nsub, T);
+            run(nown, T);
         }
         __syncthreads();   // matches the output waves' final step
         // final state of the own sequence, or (the segment ran last) of the
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             {
                 // decays and this wave's tiles of M for step t (at t == T they
                 // are computed for nothing and never read)
-                const bool xs = t >= nsub;
+                const bool xs = t >= nown;
                 const float Ah2 = xs ? Ahx2 : Ah2v;
                 const float Dh = xs ? Dhx : Dhv;
                 const float dt = sl.dt;
@@ -701,10 +703,14 @@ template <int N>
 hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int64_t nsb = (sa.L + kSub - 1) / kSub;
     hipError_t e = hipSuccess;
-    // One workgroup per compute unit when there are more sequences than
-    // compute units (but fewer than twice as many): each workgroup runs one
-    // sequence whole and then one segment of a remaining sequence, whose
-    // entering state comes from the segment states of a first, shorter kernel.
+    // Sequences are spread over the compute units in time segments whose
+    // entering states come from the segment states of a first, shorter kernel:
+    //  - more sequences than compute units (but fewer than twice as many): one
+    //    workgroup per compute unit runs one sequence whole and then one
+    //    segment of a remaining sequence;
+    //  - at most half as many sequences as compute units: every sequence is
+    //    cut into segments, one workgroup per segment;
+    //  - otherwise one workgroup per sequence.
     const int64_t chains = sa.B * sa.H;
     const int cus = device_cus();
     int nmain = (int)chains, nextra = 0, nseg = 1, seglen = (int)nsb;
@@ -712,10 +718,21 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
         nmain = cus;
         nextra = (int)(chains - cus);
         nseg = cus / nextra;
+    } else if (cus > 0 && 2 * chains <= cus && nsb >= 2) {
+        nmain = 0;
+        nextra = (int)chains;
+        nseg = cus / nextra;
+    }
+    if (nextra > 0) {
+        // no more segment states than the workspace holds
+        const int64_t cap = (int64_t)(ws.ring_floats / ((size_t)kP * N + 1));
+        if ((int64_t)nextra * (nseg - 1) > cap) nseg = (int)(1 + cap / nextra);
         if (nseg > nsb) nseg = (int)nsb;
+        if (nseg < 1) nseg = 1;
         seglen = (int)((nsb + nseg - 1) / nseg);
         nseg = (int)((nsb + seglen - 1) / seglen);
     }
+    const int nwg = nmain > 0 ? nmain : nextra * nseg;
     const size_t smem = sizeof(PipeSmem<N>);
     auto kern = pipe_kernel<N>;
     static bool configured = false;
@@ -736,7 +753,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     if (e != hipSuccess) return e;
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    kern<<<dim3((unsigned)nmain), kThreads, smem, sa.stream>>>(a);
+    kern<<<dim3((unsigned)nwg), kThreads, smem, sa.stream>>>(a);
     return hipGetLastError();
 }
 

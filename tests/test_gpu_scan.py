@@ -264,3 +264,28 @@ def test_pair_rejects_odd_head_counts():
         with pytest.raises(ssd.SSDError) as ei:
             gpu_scan(dd, 256, algo="pair")
         assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+
+
+# At most half as many (batch, head) sequences as compute units: the pipe
+# algorithm cuts every sequence into time segments, one workgroup each, the
+# entering state of each from the segment states of a first kernel.
+# (B, H, L, N, regime, init)
+FEW_LONG = [
+    (1, 1, 64 * 300 + 7, 128, "long_memory", True),
+    (1, 2, 3000, 64, "default", False),
+    (2, 3, 5000, 128, "long_memory", True),
+]
+
+
+@pytest.mark.parametrize("case", FEW_LONG, ids=[f"B{c[0]}_H{c[1]}_L{c[2]}_N{c[3]}" for c in FEW_LONG])
+def test_few_long_sequences_are_cut_into_segments(case):
+    B, H, L, N, regime, init = case
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=init, seed=1700 + H + L, regime=regime)
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+    announce(f"segmented B{B} H{H} L{L} N{N} {regime} algo=pipe")
+    for rep in range(2):
+        y, fin = gpu_scan(dd, 256, algo="pipe")
+        ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+        print(f"    call {rep}: y err {ey:.3e}  final err {ef:.3e}", flush=True)
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
