@@ -120,8 +120,10 @@ __device__ __forceinline__ void load_small_at(Small &sl, const Args &a, const La
             sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
         }
     }
-    const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
-    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+    if constexpr (!kOut) {   // the output waves take their decays from the state waves
+        const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
+        sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+    }
 }
 
 template <int N>
@@ -241,6 +243,24 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
     const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
     WaveDecays &wd = sm.wd[wave];
+    // Lambda and dt of the sub-block of step tau for output wave pq, written by
+    // state wave pq one step ahead: two slots by the parity of tau, in output
+    // wave pq's decay record
+    auto out_lam = [&](int par) { return par ? sm.wd[4 + pq].w : sm.wd[4 + pq].lam; };
+    auto out_dt = [&](int par) { return par ? sm.wd[4 + pq].rdec : sm.wd[4 + pq].dt; };
+    // whole rows of y of step tau from YS[slot] to global memory (state waves;
+    // thread u = tid % 256: rows u/8 and u/8 + 32, chunk u%8)
+    const int ysr = ((tid & 255) >> 3) * 128 + ((((tid & 255) & 7) ^ (((tid & 255) >> 4) & 7)) * 16);
+    auto store_y = [&](int tau, int slot) __attribute__((always_inline)) {
+        const int q = tau >= 0 ? q_of(tau) : 0;
+        const rsrc_t ry = rsrc(a.y + x_at(tau), q > 0 ? (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2) : 0);
+        const unsigned char *Yr = reinterpret_cast<const unsigned char *>(sm.YS[slot]);
+        const int step = (int)(32 * a.H * kP * 2);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lds_ld<uint4>(Yr + ysr + k * 4096)), ry,
+                                                   o.gx + k * step, 0, 0);
+    };
 
     Small small[2];
 
@@ -258,6 +278,10 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             load_small_at<N, false>(small[1], a, o, 0, d_at(t1), q_of(t1), 0, lane);
             stage_x<N>(sm, 0, bulk[0], o);
             load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
+            // the output partner's decays of step 0
+            const float d0 = small[0].dt;
+            out_lam(0)[lane] = wave_scan(d0 * (nown > 0 ? Ah2v : Ahx2));
+            out_dt(0)[lane] = d0;
         }
         __syncthreads();
         f32x4 Hacc[NT];
@@ -308,6 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             wd.w[lane] = ex2(lend - v) * dt;
             wd.rdec[lane] = ex2(v);
             const float gam = ex2(lend);
+            // the output partner's decays of step t+1
+            {
+                const float d1 = small[par ^ 1].dt;
+                out_lam(par ^ 1)[lane] = wave_scan(d1 * (t + 1 >= nown ? Ahx2 : Ah2v));
+                out_dt(par ^ 1)[lane] = d1;
+            }
             // dt of step t+2 into the slot just read; x of step t+2
             {
                 const int tl = t + 2 < T ? t + 2 : T - 1;
@@ -315,6 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 load_small_at<N, false>(sl, a, o, 0, d_at(tl), ql, 0, lane);
                 load_x_at<N>(bulk[par], a, o, x_at(tl), ql);
             }
+            // the whole rows of y of step t-2 (written to YS by the output waves in step t-1)
+            store_y(t - 2, par ^ 1);
 
             // LDS reads first (the Cm fragments of the inter-block term, the x
             // fragments and weights of the update); the Bm fragments are read
@@ -406,7 +438,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             switch_to_segment();
             run(nown, T);
         }
+        store_y(T - 2, (T - 1) & 1);
         __syncthreads();   // matches the output waves' final step
+        store_y(T - 1, T & 1);
         // final state of the own sequence, or (the segment ran last) of the
         // further sequence after its last segment
         if (a.final_state && (!has_x || xq == a.nseg - 1)) {
@@ -433,20 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         const unsigned char *Mb[2] = {reinterpret_cast<const unsigned char *>(sm.Mm[0]),
                                       reinterpret_cast<const unsigned char *>(sm.Mm[1])};
         // this lane's 8 bytes of the y tile (rows 16it + lrow, columns 16pq + 4lgrp..+3)
-        // and its two 16-byte chunks of whole rows (rows u/8 and u/8 + 32, chunk u%8)
         const int ysw = lrow * 128 + (((2 * pq + (lgrp >> 1)) ^ ((lrow >> 1) & 7)) * 16) + (lgrp & 1) * 8;
-        const int ysr = ((tid & 255) >> 3) * 128 + ((((tid & 255) & 7) ^ (((tid & 255) >> 4) & 7)) * 16);
-        // whole rows of y of step tau from YS[slot] to global memory
-        auto store_y = [&](int tau, int slot) __attribute__((always_inline)) {
-            const int q = tau >= 0 ? q_of(tau) : 0;
-            const rsrc_t ry = rsrc(a.y + x_at(tau), q > 0 ? (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2) : 0);
-            const unsigned char *Yr = reinterpret_cast<const unsigned char *>(sm.YS[slot]);
-            const int step = (int)(32 * a.H * kP * 2);
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lds_ld<uint4>(Yr + ysr + k * 4096)), ry,
-                                                       o.gx + k * step, 0, 0);
-        };
         // Every step issues the same global loads and stores (loads past the
         // last sub-block repeat it, stores before the first output are
         // masked), so that the wait counts the compiler derives at the loop
@@ -456,12 +477,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 // decays and this wave's tiles of M for step t (at t == T they
                 // are computed for nothing and never read)
                 const bool xs = t >= nown;
-                const float Ah2 = xs ? Ahx2 : Ah2v;
                 const float Dh = xs ? Dhx : Dhv;
-                const float dt = sl.dt;
-                const float v = wave_scan(dt * Ah2);
-                wd.lam[lane] = v;
-                wd.dt[lane] = dt;
+                const float *lam = out_lam(par), *dts = out_dt(par);   // from state wave pq
                 uint2 mt[3];
 #pragma unroll
                 for (int m = 0; m < 3; ++m) {
@@ -469,9 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                     int ti, tj;
                     tile_of(k, ti, tj);
                     const int i = 16 * ti + lrow, j0 = 16 * tj + 4 * lgrp;
-                    const float li = wd.lam[i];
-                    const f32x4 lj = *reinterpret_cast<const f32x4 *>(&wd.lam[j0]);
-                    const f32x4 dj = *reinterpret_cast<const f32x4 *>(&wd.dt[j0]);
+                    const float li = lam[i];
+                    const f32x4 lj = *reinterpret_cast<const f32x4 *>(&lam[j0]);
+                    const f32x4 dj = *reinterpret_cast<const f32x4 *>(&dts[j0]);
                     const uint32_t gw[2] = {sl.g[m].x, sl.g[m].y};
                     float mv[4];
 #pragma unroll
@@ -530,12 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
                         if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
-                // y of step t-1 into YS; the whole rows of step t-2 out
+                // y of step t-1 into YS (stored to global memory by the state waves in step t+1)
                 unsigned char *Yw = reinterpret_cast<unsigned char *>(sm.YS[par]);
 #pragma unroll
                 for (int it = 0; it < 4; ++it)
                     lds_st<uint2>(Yw + ysw + it * 2048, uint2{pack2(Y[it][0], Y[it][1]), pack2(Y[it][2], Y[it][3])});
-                store_y(t - 2, par ^ 1);
             }
             if (t + 1 < T) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
             __syncthreads();
@@ -551,8 +567,6 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             step(t + 1, 1, small[1]);
         }
         if (t <= T) step(t, 0, small[0]);
-        // the last sub-block's rows, written to YS in step T
-        store_y(T - 1, T & 1);
     }
 }
 
