@@ -39,14 +39,13 @@ constexpr int kThreads = 512;
 
 template <int N>
 struct PipeSmem {
-    __bf16 X[3][kSub * kP];        // x [j][p] of sub-blocks t-1, t, t+1 (by t % 3), chunks swizzled (xsw)
+    __bf16 X[2][kSub * kP];        // x [j][p] (by t % 2), chunks swizzled (xsw)
     __bf16 Bt[2][kSub * N];        // Bm [j][n] (by t % 2), chunks swizzled (bsw)
     __bf16 Ct[2][kSub * N];        // Cm [i][n] (by t % 2), chunks swizzled (csw)
     __bf16 Mm[2][kSub * kSub];     // masked decay matrix [i][j] (by t % 2), chunks swizzled (msw)
-    f32x4 YI[2][4][4][64];         // inter-block term, [parity][row group][token tile][lane]
     WaveDecays wd[8];
     // y on its way to global memory as whole 128-byte rows: written by the
-    // four output waves (16 columns each) in one step, stored in the next
+    // four compute waves (16 columns each) in one step, stored in the next
     // (by t % 2); chunk c of row r at c ^ ((r >> 1) & 7)
     __bf16 YS[2][kSub * kP];
 };
@@ -120,10 +119,8 @@ __device__ __forceinline__ void load_small_at(Small &sl, const Args &a, const La
             sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
         }
     }
-    if constexpr (!kOut) {   // the output waves take their decays from the state waves
-        const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
-        sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
-    }
+    const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
+    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
 }
 
 template <int N>
@@ -239,16 +236,11 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pq = wave & 3;
-    const bool state_wave = wave < 4;
+    const bool compute_wave = wave < 4;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
     const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
     WaveDecays &wd = sm.wd[wave];
-    // Lambda and dt of the sub-block of step tau for output wave pq, written by
-    // state wave pq one step ahead: two slots by the parity of tau, in output
-    // wave pq's decay record
-    auto out_lam = [&](int par) { return par ? sm.wd[4 + pq].w : sm.wd[4 + pq].lam; };
-    auto out_dt = [&](int par) { return par ? sm.wd[4 + pq].rdec : sm.wd[4 + pq].dt; };
-    // whole rows of y of step tau from YS[slot] to global memory (state waves;
+    // whole rows of y of step tau from YS[slot] to global memory (compute waves;
     // thread u = tid % 256: rows u/8 and u/8 + 32, chunk u%8)
     const int ysr = ((tid & 255) >> 3) * 128 + ((((tid & 255) & 7) ^ (((tid & 255) >> 4) & 7)) * 16);
     auto store_y = [&](int tau, int slot) __attribute__((always_inline)) {
@@ -264,10 +256,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 
     Small small[2];
 
-    if (state_wave) {
+    if (compute_wave) {
         // ------------------------------------------------------------------
-        // state waves: rows p = 16pq..16pq+15 of H, held transposed (rows n,
-        // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow
+        // compute waves: rows p = 16pq..16pq+15 of H, held transposed (rows n,
+        // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow.  The
+        // outputs of sub-block t: lane holds token i = 16it + lrow,
+        // p = 16pq + 4lgrp + 0..3.
         // prologue: x of sub-block 0 staged; x of sub-block 1 and dt of
         // sub-blocks 0 and 1 in flight
         BulkX bulk[2];   // x of step t+1 (staged at the end of step t) and t+2 (in flight)
@@ -278,23 +272,19 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             load_small_at<N, false>(small[1], a, o, 0, d_at(t1), q_of(t1), 0, lane);
             stage_x<N>(sm, 0, bulk[0], o);
             load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
-            // the output partner's decays of step 0
-            const float d0 = small[0].dt;
-            out_lam(0)[lane] = wave_scan(d0 * (nown > 0 ? Ah2v : Ahx2));
-            out_dt(0)[lane] = d0;
         }
-        __syncthreads();
         f32x4 Hacc[NT];
+        const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
         {
             const rsrc_t ri = rsrc(a.init ? (const void *)(a.init + chain * (kP * N)) : (const void *)a.x,
                                    a.init ? kP * N * 4 : 0);
-            const int lane_off0 = (16 * pq + lrow) * N + 4 * lgrp;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                Hacc[t] = __builtin_bit_cast(f32x4,
-                                             __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off0 + 16 * t) * 4, 0, 0));
+            for (int u = 0; u < NT; ++u)
+                Hacc[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off + 16 * u) * 4, 0, 0));
         }
-        const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
+        __syncthreads();
+        // this lane's 8 bytes of the y tile (rows 16it + lrow, columns 16pq + 4lgrp..+3)
+        const int ysw = lrow * 128 + (((2 * pq + (lgrp >> 1)) ^ ((lrow >> 1) & 7)) * 16) + (lgrp & 1) * 8;
         // own sequence done: its final state out; the segment's entering state
         // in, from the initial state and the states and log2 decays of the
         // earlier segments (written by the segment-state kernel)
@@ -320,11 +310,11 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             }
         };
         auto step = [&](int t, int par, Small &sl) __attribute__((always_inline)) {
-            const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[t % 3]);
+            const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[par]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
             const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
-            const bool xs = t >= nown;
-            const float Ah2 = xs ? Ahx2 : Ah2v;
+            const unsigned char *Mr = reinterpret_cast<const unsigned char *>(sm.Mm[par]);
+            const float Ah2 = t >= nown ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
             const float dt = sl.dt;
             const float v = wave_scan(dt * Ah2);
@@ -332,12 +322,6 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             wd.w[lane] = ex2(lend - v) * dt;
             wd.rdec[lane] = ex2(v);
             const float gam = ex2(lend);
-            // the output partner's decays of step t+1
-            {
-                const float d1 = small[par ^ 1].dt;
-                out_lam(par ^ 1)[lane] = wave_scan(d1 * (t + 1 >= nown ? Ahx2 : Ah2v));
-                out_dt(par ^ 1)[lane] = d1;
-            }
             // dt of step t+2 into the slot just read; x of step t+2
             {
                 const int tl = t + 2 < T ? t + 2 : T - 1;
@@ -345,33 +329,35 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 load_small_at<N, false>(sl, a, o, 0, d_at(tl), ql, 0, lane);
                 load_x_at<N>(bulk[par], a, o, x_at(tl), ql);
             }
-            // the whole rows of y of step t-2 (written to YS by the output waves in step t-1)
-            store_y(t - 2, par ^ 1);
+            // the whole rows of y of step t-1 (written to YS by the four compute waves in step t-1)
+            store_y(t - 1, par ^ 1);
 
-            // LDS reads first (the Cm fragments of the inter-block term, the x
-            // fragments and weights of the update); the Bm fragments are read
-            // while the first products run
-            bf16x8 cf[KS][4];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            // LDS reads, each a k-step ahead of the products that use them
+            auto read_cf = [&](int ks, bf16x8 (&cf)[4]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
                     const bf16x4 c0 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][0] ^ csw_tile_bytes<N>(it)));
                     const bf16x4 c1 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][1] ^ csw_tile_bytes<N>(it)));
-                    cf[ks][it] = bf16x8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                    cf[it] = bf16x8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                 }
+            };
+            // Bm fragments of the update, in groups of four n-tiles (k-step ks, tiles 4v..4v+3)
+            auto read_bt = [&](int ks, int v4, bf16x8 (&bt)[4]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bf16x4 lo = tr4(Bb + o.bt[4 * v4 + u] + ks * 32 * O::RB);
+                    const bf16x4 hi = tr4(Bb + o.bt[4 * v4 + u] + ks * 32 * O::RB + 4 * O::RB);
+                    bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            };
+            bf16x8 cf[2][4];
+            read_cf(0, cf[0]);
             bf16x8 xf[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
                 const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
                 xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-            f32x4 wv[2][2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                wv[ks][0] = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp]);
-                wv[ks][1] = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp + 4]);
             }
             const f32x4 rd = {wd.rdec[lrow], wd.rdec[16 + lrow], wd.rdec[32 + lrow], wd.rdec[48 + lrow]};
             __builtin_amdgcn_sched_barrier(0);
@@ -380,44 +366,69 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             f32x4 Y[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it) Y[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 bt[2][NT];
+            bf16x8 mf[4][2];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) {
+                    read_cf(ks + 1, cf[(ks + 1) & 1]);
+                } else {
+#pragma unroll
+                    for (int it = 0; it < 4; ++it)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+                            if (!(kk == 1 && it < 2)) mf[it][kk] = lds_ld<bf16x8>(Mr + o.mm[kk] + it * 2048);
+                }
                 const bf16x8 ah = to_bf16x8(Hacc[2 * ks], Hacc[2 * ks + 1]);
 #pragma unroll
-                for (int it = 0; it < 4; ++it) Y[it] = mfma(ah, cf[ks][it], Y[it]);
-                // Bm fragments of k-step kb = 2ks/KS (half of them after each half of the products)
-                if (ks == KS / 2 - 1 || ks == KS - 1) {
-                    const int kb = ks == KS - 1 ? 1 : 0;
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < NT; ++u) {
-                        const bf16x4 lo = tr4(Bb + o.bt[u] + kb * 32 * O::RB);
-                        const bf16x4 hi = tr4(Bb + o.bt[u] + kb * 32 * O::RB + 4 * O::RB);
-                        bt[kb][u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int it = 0; it < 4; ++it) Y[it] = mfma(ah, cf[ks & 1][it], Y[it]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            constexpr int NG = NT / 4;   // groups of four n-tiles
+            bf16x8 bt[2][4];
+            read_bt(0, 0, bt[0]);
+            // x scaled by the decay weights: the k-operand of the update
+            bf16x8 xw[2];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) sm.YI[par][pq][it][lane] = Y[it] * rd[it];
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&wd.w[32 * ks + 8 * lgrp + 4]);
+                f32x4 x0, x1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] = (float)xf[ks][e] * w0[e];
+                    x1[e] = (float)xf[ks][4 + e] * w1[e];
+                }
+                xw[ks] = to_bf16x8(x0, x1);
+            }
+            // plus the masked intra-block product (D x_i on the diagonal); y of
+            // sub-block t into YS
+#pragma unroll
+            for (int it = 0; it < 4; ++it) Y[it] *= rd[it];
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
+            {
+                unsigned char *Yw = reinterpret_cast<unsigned char *>(sm.YS[par]);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    lds_st<uint2>(Yw + ysw + it * 2048, uint2{pack2(Y[it][0], Y[it][1]), pack2(Y[it][2], Y[it][3])});
+            }
+            __builtin_amdgcn_sched_barrier(0);
 
             // state update over sub-block t: H <- exp(Lambda_63) H + sum_j Bm_j (outer) (w_j x_j)
 #pragma unroll
             for (int u = 0; u < NT; ++u) Hacc[u] *= gam;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f32x4 x0, x1;
+            for (int r = 0; r < 2 * NG; ++r) {
+                const int ks = r / NG, v4 = r % NG;
+                if (r + 1 < 2 * NG) read_bt((r + 1) / NG, (r + 1) % NG, bt[(r + 1) & 1]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x0[e] = (float)xf[ks][e] * wv[ks][0][e];
-                    x1[e] = (float)xf[ks][4 + e] * wv[ks][1][e];
-                }
-                const bf16x8 xw = to_bf16x8(x0, x1);
-#pragma unroll
-                for (int u = 0; u < NT; ++u) Hacc[u] = mfma(bt[ks][u], xw, Hacc[u]);
+                for (int u = 0; u < 4; ++u) Hacc[4 * v4 + u] = mfma(bt[r & 1][u], xw[ks], Hacc[4 * v4 + u]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (t + 1 < T) stage_x<N>(sm, (t + 1) % 3, bulk[par ^ 1], o);
+            if (t + 1 < T) stage_x<N>(sm, par ^ 1, bulk[par ^ 1], o);
             __syncthreads();
         };
         // steps [t0, t1) with the parity of each step known at compile time
@@ -438,9 +449,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             switch_to_segment();
             run(nown, T);
         }
-        store_y(T - 2, (T - 1) & 1);
-        __syncthreads();   // matches the output waves' final step
-        store_y(T - 1, T & 1);
+        __syncthreads();   // matches the prep waves' final barrier
+        store_y(T - 1, (T - 1) & 1);
         // final state of the own sequence, or (the segment ran last) of the
         // further sequence after its last segment
         if (a.final_state && (!has_x || xq == a.nseg - 1)) {
@@ -450,123 +460,99 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         }
     } else {
         // ------------------------------------------------------------------
-        // output waves: tiles of M for sub-block t, outputs of sub-block t-1
-        // (lane holds token i = 16it + lrow, p = 16pq + 4lgrp + 0..3)
-        // prologue: Bm, Cm of sub-block 0 staged; those of sub-block 1 and dt
-        // and G tiles of sub-blocks 0 and 1 in flight
+        // prep waves: in step t the masked decay matrix of sub-block t+1 (this
+        // wave's tiles, from its gram tiles and a prefix scan of dt*A) and its
+        // Bm, Cm into LDS
         BulkBC<N> bulk[2];   // Bm, Cm of step t+1 (staged at the end of step t) and t+2
+        // decays and this wave's tiles of the masked matrix of the sub-block
+        // of step tau, from sl, into Mm[slot]
+        auto build_m = [&](int tau, const Small &sl, int slot) __attribute__((always_inline)) {
+            const bool xs = tau >= nown;
+            const float Ah2 = xs ? Ahx2 : Ah2v;
+            const float Dh = xs ? Dhx : Dhv;
+            wd.lam[lane] = wave_scan(sl.dt * Ah2);
+            wd.dt[lane] = sl.dt;
+            uint2 mt[3];
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int k = pq + 4 * m < 10 ? pq + 4 * m : 9;
+                int ti, tj;
+                tile_of(k, ti, tj);
+                const int i = 16 * ti + lrow, j0 = 16 * tj + 4 * lgrp;
+                const float li = wd.lam[i];
+                const f32x4 lj = *reinterpret_cast<const f32x4 *>(&wd.lam[j0]);
+                const f32x4 dj = *reinterpret_cast<const f32x4 *>(&wd.dt[j0]);
+                const uint32_t gw[2] = {sl.g[m].x, sl.g[m].y};
+                float mv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = (e & 1) ? hi_bf16(gw[e >> 1]) : lo_bf16(gw[e >> 1]);
+                    const float d = j0 + e <= i ? li - lj[e] : -__builtin_inff();
+                    // the skip term D x_i rides on the diagonal
+                    mv[e] = __builtin_fmaf(gv * ex2(d), dj[e], j0 + e == i ? Dh : 0.f);
+                }
+                mt[m] = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
+            }
+            unsigned char *Mw = reinterpret_cast<unsigned char *>(sm.Mm[slot]);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int k = pq + 4 * m;
+                if (k < 10) {
+                    int ti, tj;
+                    tile_of(k, ti, tj);
+                    lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * tj)), mt[m]);
+                }
+            }
+            if (pq >= 2) {
+                // the tiles above the diagonal that the products read: (0,1) and (2,3)
+                const int ti = pq == 2 ? 0 : 2;
+                uint32_t z = 0;
+                asm volatile("" : "+v"(z));
+                lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * (ti + 1))), uint2{z, z});
+            }
+        };
+        // prologue: Bm, Cm of sub-block 0 staged and its masked matrix built;
+        // Bm, Cm of sub-block 1 and the dt and G tiles of sub-blocks 1 and 2 in flight
         {
-            const int t1 = T > 1 ? 1 : 0;
+            const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1;
             load_bc_at<N>(bulk[0], a, o, b_at(0), q_of(0));
             load_small_at<N, true>(small[0], a, o, g_at(0), d_at(0), q_of(0), pq, lane);
             load_small_at<N, true>(small[1], a, o, g_at(t1), d_at(t1), q_of(t1), pq, lane);
             stage_bc<N>(sm, 0, bulk[0], o);
             load_bc_at<N>(bulk[1], a, o, b_at(t1), q_of(t1));
+            build_m(0, small[0], 0);
+            load_small_at<N, true>(small[0], a, o, g_at(t2), d_at(t2), q_of(t2), pq, lane);
         }
         __syncthreads();
-        const unsigned char *Mb[2] = {reinterpret_cast<const unsigned char *>(sm.Mm[0]),
-                                      reinterpret_cast<const unsigned char *>(sm.Mm[1])};
-        // this lane's 8 bytes of the y tile (rows 16it + lrow, columns 16pq + 4lgrp..+3)
-        const int ysw = lrow * 128 + (((2 * pq + (lgrp >> 1)) ^ ((lrow >> 1) & 7)) * 16) + (lgrp & 1) * 8;
-        // Every step issues the same global loads and stores (loads past the
-        // last sub-block repeat it, stores before the first output are
-        // masked), so that the wait counts the compiler derives at the loop
-        // head are those of the steady state.
-        auto step = [&](int t, int par, Small &sl) __attribute__((always_inline)) {
+        // Every step issues the same global loads (loads past the last
+        // sub-block repeat it), so that the wait counts the compiler derives
+        // at the loop head are those of the steady state.
+        auto step = [&](int t, int par) __attribute__((always_inline)) {
+            // sub-block t+1 (its dt and G tiles were loaded in step t-1), then
+            // the dt and G tiles of t+3 into the same slot
+            build_m(t + 1, small[par ^ 1], par ^ 1);
             {
-                // decays and this wave's tiles of M for step t (at t == T they
-                // are computed for nothing and never read)
-                const bool xs = t >= nown;
-                const float Dh = xs ? Dhx : Dhv;
-                const float *lam = out_lam(par), *dts = out_dt(par);   // from state wave pq
-                uint2 mt[3];
-#pragma unroll
-                for (int m = 0; m < 3; ++m) {
-                    const int k = pq + 4 * m < 10 ? pq + 4 * m : 9;
-                    int ti, tj;
-                    tile_of(k, ti, tj);
-                    const int i = 16 * ti + lrow, j0 = 16 * tj + 4 * lgrp;
-                    const float li = lam[i];
-                    const f32x4 lj = *reinterpret_cast<const f32x4 *>(&lam[j0]);
-                    const f32x4 dj = *reinterpret_cast<const f32x4 *>(&dts[j0]);
-                    const uint32_t gw[2] = {sl.g[m].x, sl.g[m].y};
-                    float mv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gv = (e & 1) ? hi_bf16(gw[e >> 1]) : lo_bf16(gw[e >> 1]);
-                        const float d = j0 + e <= i ? li - lj[e] : -__builtin_inff();
-                        // the skip term D x_i rides on the diagonal
-                        mv[e] = __builtin_fmaf(gv * ex2(d), dj[e], j0 + e == i ? Dh : 0.f);
-                    }
-                    mt[m] = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
-                }
-                unsigned char *Mw = reinterpret_cast<unsigned char *>(sm.Mm[par]);
-#pragma unroll
-                for (int m = 0; m < 3; ++m) {
-                    const int k = pq + 4 * m;
-                    if (k < 10) {
-                        int ti, tj;
-                        tile_of(k, ti, tj);
-                        lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * tj)), mt[m]);
-                    }
-                }
-                if (pq >= 2) {
-                    // the tiles above the diagonal that the products read: (0,1) and (2,3)
-                    const int ti = pq == 2 ? 0 : 2;
-                    uint32_t z = 0;
-                    asm volatile("" : "+v"(z));
-                    lds_st<uint2>(Mw + 16 * ti * 128 + (o.mw ^ (32 * (ti + 1))), uint2{z, z});
-                }
-                const int tl = t + 2 < T ? t + 2 : T - 1;
-                const int ql = q_of(tl);
-                load_small_at<N, true>(sl, a, o, g_at(tl), d_at(tl), ql, pq, lane);
-                load_bc_at<N>(bulk[par], a, o, b_at(tl), ql);
+                const int tl = t + 3 < T ? t + 3 : T - 1;
+                load_small_at<N, true>(small[par ^ 1], a, o, g_at(tl), d_at(tl), q_of(tl), pq, lane);
             }
             {
-                // outputs of step t-1 (at t == 0 computed from stale LDS, with
-                // every store masked)
-                const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[(t + 2) % 3]);
-                const unsigned char *Mr = Mb[par ^ 1];
-                f32x4 Y[4];
-#pragma unroll
-                for (int it = 0; it < 4; ++it) Y[it] = sm.YI[par ^ 1][pq][it][lane];
-                bf16x8 xf[2], mf[4][2];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
-                    const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
-                    xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        if (!(ks == 1 && it < 2)) mf[it][ks] = lds_ld<bf16x8>(Mr + o.mm[ks] + it * 2048);
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        if (!(ks == 1 && it < 2)) Y[it] = mfma(xf[ks], mf[it][ks], Y[it]);
-                // y of step t-1 into YS (stored to global memory by the state waves in step t+1)
-                unsigned char *Yw = reinterpret_cast<unsigned char *>(sm.YS[par]);
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    lds_st<uint2>(Yw + ysw + it * 2048, uint2{pack2(Y[it][0], Y[it][1]), pack2(Y[it][2], Y[it][3])});
+                const int tl = t + 2 < T ? t + 2 : T - 1;
+                load_bc_at<N>(bulk[par], a, o, b_at(tl), q_of(tl));
             }
             if (t + 1 < T) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
             __syncthreads();
         };
-        // steps 0..T (step T only finishes the outputs of the last sub-block);
-        // the first two outside the loop, so that the loop is entered in the
-        // steady state
-        step(0, 0, small[0]);
-        step(1, 1, small[1]);
+        // steps 0..T-1, the first two outside the loop so that the loop is
+        // entered in the steady state
+        step(0, 0);
+        if (T > 1) step(1, 1);
         int t = 2;
-        for (; t + 1 <= T; t += 2) {
-            step(t, 0, small[0]);
-            step(t + 1, 1, small[1]);
+        for (; t + 1 < T; t += 2) {
+            step(t, 0);
+            step(t + 1, 1);
         }
-        if (t <= T) step(t, 0, small[0]);
+        if (t < T) step(t, 0);
+        __syncthreads();   // matches the compute waves' final barrier
     }
 }
 
