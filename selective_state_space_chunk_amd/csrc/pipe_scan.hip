@@ -262,16 +262,18 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow.  The
         // outputs of sub-block t: lane holds token i = 16it + lrow,
         // p = 16pq + 4lgrp + 0..3.
-        // prologue: x of sub-block 0 staged; x of sub-block 1 and dt of
-        // sub-blocks 0 and 1 in flight
-        BulkX bulk[2];   // x of step t+1 (staged at the end of step t) and t+2 (in flight)
+        // prologue: x of sub-block 0 staged; x of sub-blocks 1 and 2 and dt
+        // of sub-blocks 0 and 1 in flight.  x is loaded three steps ahead:
+        // during step t, bulk[0..2] hold x of steps t+1..t+3.
+        BulkX bulk[3];
         {
-            const int t1 = T > 1 ? 1 : 0;
+            const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1;
             load_x_at<N>(bulk[0], a, o, x_at(0), q_of(0));
             load_small_at<N, false>(small[0], a, o, 0, d_at(0), q_of(0), 0, lane);
             load_small_at<N, false>(small[1], a, o, 0, d_at(t1), q_of(t1), 0, lane);
             stage_x<N>(sm, 0, bulk[0], o);
-            load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
+            load_x_at<N>(bulk[0], a, o, x_at(t1), q_of(t1));
+            load_x_at<N>(bulk[1], a, o, x_at(t2), q_of(t2));
         }
         f32x4 Hacc[NT];
         const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
@@ -322,12 +324,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             wd.w[lane] = ex2(lend - v) * dt;
             wd.rdec[lane] = ex2(v);
             const float gam = ex2(lend);
-            // dt of step t+2 into the slot just read; x of step t+2
+            // dt of step t+2 into the slot just read; x of step t+3
             {
                 const int tl = t + 2 < T ? t + 2 : T - 1;
-                const int ql = q_of(tl);
-                load_small_at<N, false>(sl, a, o, 0, d_at(tl), ql, 0, lane);
-                load_x_at<N>(bulk[par], a, o, x_at(tl), ql);
+                const int tx = t + 3 < T ? t + 3 : T - 1;
+                load_small_at<N, false>(sl, a, o, 0, d_at(tl), q_of(tl), 0, lane);
+                load_x_at<N>(bulk[2], a, o, x_at(tx), q_of(tx));
             }
             // the whole rows of y of step t-1 (written to YS by the four compute waves in step t-1)
             store_y(t - 1, par ^ 1);
@@ -428,7 +430,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 for (int u = 0; u < 4; ++u) Hacc[4 * v4 + u] = mfma(bt[r & 1][u], xw[ks], Hacc[4 * v4 + u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (t + 1 < T) stage_x<N>(sm, par ^ 1, bulk[par ^ 1], o);
+            if (t + 1 < T) stage_x<N>(sm, par ^ 1, bulk[0], o);
+            bulk[0] = bulk[1];
+            bulk[1] = bulk[2];
             __syncthreads();
         };
         // steps [t0, t1) with the parity of each step known at compile time
@@ -558,18 +562,38 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 
 // The state that segment q of further sequence e produces from a zero state,
 // S = sum over its sub-blocks of the state update, and log2 of its total decay
-// (the sum of dt*A over the segment, in base-2 units).  Eight waves: wave w
-// owns rows p = 16 (w % 4) .. +15 and the n-tiles of half w / 4 of the state,
-// with pipe_kernel's update step; no outputs.  The main kernel combines these
-// into each segment's entering state: H_{q+1} = 2^(log2 decay_q) H_q + S_q.
+// (the sum of dt*A over the segment, in base-2 units).  The main kernel
+// combines these into each segment's entering state:
+// H_{q+1} = 2^(log2 decay_q) H_q + S_q.
+//
+// A step takes a pair of sub-blocks (a, b) as one 128-token update:
+// H <- 2^(l_a + l_b) H + sum_j Bm_j (w_j x_j), w_j = 2^(Lambda_end - Lambda_j) dt_j,
+// with Lambda the running sum of dt*A (log2 units) over the pair and l_c the
+// total of sub-block c.
+//  - Wave 0 alone loads dt (a row of one float per token touches 64 cache
+//    lines per sub-block, so it is loaded once per workgroup), three steps
+//    ahead, and two steps ahead scans it into the pair's weights and decay,
+//    published through a three-slot LDS ring.
+//  - The weights are applied to x as it is staged (each x element is
+//    multiplied once), so the matrix-core operands come straight from LDS.
+//  - The eight waves form two groups, group c taking sub-block c of every
+//    pair into a partial state of its own (the two add up to S at the end);
+//    in a group, wave (nq, pp) holds n-tiles nq*NT/2 .. +NT/2-1 and p-tiles
+//    2pp, 2pp+1, so each fragment read from LDS serves two waves.
+// Register slot s % 2 holds the pair of step s from its load (issued in step
+// s - 2) until it is staged to LDS slot s % 2 at the end of step s - 1.  A
+// pair that runs past the segment's end gets dt = 0 for its missing
+// sub-block: weight 0, decay 1.
 template <int N>
 __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
-    __shared__ __align__(16) __bf16 lds_x[2][kSub * kP];
-    __shared__ __align__(16) __bf16 lds_bt[2][kSub * N];
-    __shared__ __align__(16) float lds_w[8][kSub];
+    __shared__ __align__(16) __bf16 lds_x[2][2][kSub * kP];
+    __shared__ __align__(16) __bf16 lds_bt[2][2][kSub * N];
+    __shared__ __align__(16) float lds_w[3][2][kSub];
+    __shared__ float lds_l[3];
     using O = LaneOffs<N>;
-    constexpr int NT = N / 16, NH = NT / 2;   // n-tiles in all, per wave
-    constexpr int KB = N / 64;                // Bm chunks staged per thread
+    constexpr int NT = N / 16, NTW = NT / 2;  // n-tiles in all, per wave
+    constexpr int KB = N / 64;                // Bm chunks staged per thread and sub-block
+    static_assert(sizeof(lds_bt) >= 4 * NTW * 2 * 64 * sizeof(f32x4), "reduction room");
     const int xe = blk % a.nextra, q = blk / a.nextra;
     const int64_t chain = a.nmain + xe;
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
@@ -577,99 +601,171 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
     const float Ah2 = a.A[h] * kLog2e;
     const int s0 = q * a.seglen, len = a.seglen;   // segments before the last are full and inside the sequence
+    const int nsteps = (len + 1) / 2;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pq = wave & 3, nh = wave >> 2;
+    const int grp = wave >> 2, wq = wave & 3, nq = wq & 1, pp = wq >> 1;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
-    float *wrow = lds_w[wave];
+    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G);
+    const int xtr1 = lane_offsets<N>(tid, 2 * pp + 1, a.H, a.G).xtr;   // second p-tile
+    // staging: thread (u = tid % 256, half nh) stages x chunk nh (token
+    // u / 8 + 32 nh) and Bm chunks nh*KB .. +KB-1 of u, of each sub-block
+    const int nh = tid >> 8;
+    const int my_token = ((tid & 255) >> 3) + 32 * nh;
 
-    // thread (u = tid % 256, half nh) stages x chunk nh and Bm chunks nh*KB .. +KB-1 of u
-    uint4 xr[2], br[2][KB];
-    float dts[2];
-    auto load = [&](int k, int slot) __attribute__((always_inline)) {
-        const int qn = sub_tokens(a, s0 + k);
-        const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
-        const rsrc_t rx = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(qn - 1) * a.H * kP + kP) * 2));
-        xr[slot] = ld16(rx, o.gx + nh * (int)(32 * a.H * kP * 2));
-        const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, (int)(((int64_t)(qn - 1) * a.G * N + N) * 2));
-        const int step = (int)((256 / O::CPR) * a.G * N * 2);
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) br[slot][kk] = ld16(rb, o.gb + (nh * KB + kk) * step);
-        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
-        dts[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+    auto sub_at = [&](int st, int c) __attribute__((always_inline)) {
+        const int k = 2 * st + c;
+        return k < len ? k : len - 1;
     };
-    auto stage = [&](int slot) __attribute__((always_inline)) {
-        unsigned char *Xb = reinterpret_cast<unsigned char *>(lds_x[slot]);
-        unsigned char *Bb = reinterpret_cast<unsigned char *>(lds_bt[slot]);
-        lds_st<uint4>(Xb + o.sx + nh * 4096, xr[slot]);
+    uint4 xr[2][2], br[2][2][KB];
+    auto load = [&](int st, int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk) lds_st<uint4>(Bb + o.sb + (nh * KB + kk) * (256 / O::CPR) * O::RB, br[slot][kk]);
-    };
-    load(0, 0);
-    load(len > 1 ? 1 : 0, 1);
-    stage(0);
-    __syncthreads();
-
-    f32x4 Hacc[NH];
+        for (int c = 0; c < 2; ++c) {
+            const int k = sub_at(st, c);
+            const int qn = sub_tokens(a, s0 + k);
+            const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+            const rsrc_t rx = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(qn - 1) * a.H * kP + kP) * 2));
+            xr[slot][c] = ld16(rx, o.gx + nh * (int)(32 * a.H * kP * 2));
+            const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, (int)(((int64_t)(qn - 1) * a.G * N + N) * 2));
+            const int step = (int)((256 / O::CPR) * a.G * N * 2);
 #pragma unroll
-    for (int u = 0; u < NH; ++u) Hacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float log2dec = 0.f;
-    auto step = [&](int k, int slot) __attribute__((always_inline)) {
-        const unsigned char *Xb = reinterpret_cast<const unsigned char *>(lds_x[slot]);
-        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(lds_bt[slot]);
-        const float dt = dts[slot];
-        const float v = wave_scan(dt * Ah2);
-        const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-        wrow[lane] = ex2(lend - v) * dt;
-        const float gam = ex2(lend);
-        log2dec += lend;
-        if (k + 2 < len) load(k + 2, slot);
-        bf16x8 xf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
-            const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
-            xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            for (int kk = 0; kk < KB; ++kk) br[slot][c][kk] = ld16(rb, o.gb + (nh * KB + kk) * step);
         }
+    };
+    // wave 0: dt of the pair of step st (lane = token) into register slot `slot`
+    float dts[2][2];
+    auto load_dt = [&](int st, int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NH; ++u) Hacc[u] *= gam;
+        for (int c = 0; c < 2; ++c) {
+            const int k = sub_at(st, c);
+            const int qn = sub_tokens(a, s0 + k);
+            const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+            const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
+            dts[slot][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+        }
+    };
+    // wave 0: weights and log2 decay of the pair of step st into ring slot st % 3
+    auto weights = [&](int st, int slot) __attribute__((always_inline)) {
+        const float dta = dts[slot][0];
+        const float dtb = 2 * st + 1 < len ? dts[slot][1] : 0.f;
+        const float va = wave_scan(dta * Ah2), vb = wave_scan(dtb * Ah2);
+        const float la = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), 63));
+        const float lb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), 63));
+        const int r = st % 3;
+        lds_w[r][0][lane] = ex2(la + lb - va) * dta;
+        lds_w[r][1][lane] = ex2(lb - vb) * dtb;
+        if (lane == 0) lds_l[r] = la + lb;
+    };
+    // x of the pair of step st (register slot `slot`) times its weights, and
+    // Bm, into LDS slot `slot`
+    auto stage = [&](int st, int slot) __attribute__((always_inline)) {
+        const int r = st % 3;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&wrow[32 * ks + 8 * lgrp]);
-            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&wrow[32 * ks + 8 * lgrp + 4]);
+        for (int c = 0; c < 2; ++c) {
+            unsigned char *Xb = reinterpret_cast<unsigned char *>(lds_x[slot][c]);
+            unsigned char *Bb = reinterpret_cast<unsigned char *>(lds_bt[slot][c]);
+            const float w = lds_w[r][c][my_token];
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, xr[slot][c]);
             f32x4 x0, x1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x0[e] = (float)xf[ks][e] * w0[e];
-                x1[e] = (float)xf[ks][4 + e] * w1[e];
+                x0[e] = (float)xv[e] * w;
+                x1[e] = (float)xv[4 + e] * w;
             }
-            const bf16x8 xw = to_bf16x8(x0, x1);
-            bf16x8 bt[NH];
+            lds_st<bf16x8>(Xb + o.sx + nh * 4096, to_bf16x8(x0, x1));
 #pragma unroll
-            for (int u = 0; u < NH; ++u) {
-                const int bo = nh ? o.bt[NH + u] : o.bt[u];   // (no run-time index into o)
-                const bf16x4 lo = tr4(Bb + bo + ks * 32 * O::RB);
-                const bf16x4 hi = tr4(Bb + bo + ks * 32 * O::RB + 4 * O::RB);
-                bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-#pragma unroll
-            for (int u = 0; u < NH; ++u) Hacc[u] = mfma(bt[u], xw, Hacc[u]);
+            for (int kk = 0; kk < KB; ++kk)
+                lds_st<uint4>(Bb + o.sb + (nh * KB + kk) * (256 / O::CPR) * O::RB, br[slot][c][kk]);
         }
-        if (k + 1 < len) stage(slot ^ 1);
+    };
+
+    // prologue: pairs 0 and 1 loaded, weights of pairs 0 and 1, dt of pair 2
+    // in flight, pair 0 staged
+    load(0, 0);
+    load(nsteps > 1 ? 1 : 0, 1);
+    if (wave == 0) {
+        load_dt(0, 0);
+        load_dt(1, 1);
+        weights(0, 0);
+        load_dt(2, 0);
+        weights(1, 1);
+    }
+    __syncthreads();
+    stage(0, 0);
+    __syncthreads();
+
+    f32x4 Hacc[NTW][2];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) Hacc[u][0] = Hacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float log2dec = 0.f;
+    auto step = [&](int st, int par) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float lpair = lds_l[st % 3];
+        log2dec += lpair;
+        // the pair of step st+2 into the register slot staged at the end of the last step
+        load(st + 2 < nsteps ? st + 2 : nsteps - 1, par);
+        if (wave == 0) {
+            load_dt(st + 3, par ^ 1);   // the slot whose pair (st+1) was scanned in the last step
+            weights(st + 2, par);
+        }
+        const float gam = ex2(lpair);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            Hacc[u][0] *= gam;
+            Hacc[u][1] *= gam;
+        }
+        const unsigned char *Xb = reinterpret_cast<const unsigned char *>(lds_x[par][grp]);
+        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(lds_bt[par][grp]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 xw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int xo = (j ? xtr1 : o.xtr) + ks * 4096;
+                const bf16x4 lo = tr4(Xb + xo), hi = tr4(Xb + xo + 512);
+                xw[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int u = 0; u < NTW; ++u) {
+                const int bo = nq ? o.bt[NTW + u] : o.bt[u];   // (no run-time index into o)
+                const bf16x4 blo = tr4(Bb + bo + ks * 32 * O::RB);
+                const bf16x4 bhi = tr4(Bb + bo + ks * 32 * O::RB + 4 * O::RB);
+                const bf16x8 bt = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+                Hacc[u][0] = mfma(bt, xw[0], Hacc[u][0]);
+                Hacc[u][1] = mfma(bt, xw[1], Hacc[u][1]);
+            }
+        }
+        // unconditional (clamped) loads and stages: the same memory operations
+        // in every step, so that the wait counts need not cover a shorter path
+        stage(st + 1, par ^ 1);
         __syncthreads();
     };
-    int k = 0;
-    for (; k + 1 < len; k += 2) {
-        step(k, 0);
-        step(k + 1, 1);
+    int st = 0;
+    for (; st + 1 < nsteps; st += 2) {
+        step(st, 0);
+        step(st + 1, 1);
     }
-    if (k < len) step(k, 0);
-    float *dst = seg_state<N>(a, xe, q) + (16 * pq + lrow) * N + 4 * lgrp + 16 * nh * NH;
+    if (st < nsteps) step(st, 0);
+    // S = group 0's partial + group 1's (passed through LDS, free after the last barrier)
+    f32x4 *red = reinterpret_cast<f32x4 *>(&lds_bt[0][0][0]) + (wq * NTW * 2) * 64 + lane;
+    if (grp == 1) {
 #pragma unroll
-    for (int u = 0; u < NH; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u) = Hacc[u];
-    if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
+        for (int u = 0; u < NTW; ++u) {
+            red[(2 * u) * 64] = Hacc[u][0];
+            red[(2 * u + 1) * 64] = Hacc[u][1];
+        }
+    }
+    __syncthreads();
+    if (grp == 0) {
+        float *dst = seg_state<N>(a, xe, q) + (32 * pp + lrow) * N + 16 * NTW * nq + 4 * lgrp;
+#pragma unroll
+        for (int u = 0; u < NTW; ++u)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<f32x4 *>(dst + 16 * j * N + 16 * u) = Hacc[u][j] + red[(2 * u + j) * 64];
+        if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
+    }
 }
 
 // The work that must precede pipe_kernel when there are segments, in one

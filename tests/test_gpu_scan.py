@@ -274,6 +274,9 @@ FEW_LONG = [
     (1, 1, 64 * 300 + 7, 128, "long_memory", True),
     (1, 2, 3000, 64, "default", False),
     (2, 3, 5000, 128, "long_memory", True),
+    # 767 sub-blocks over 256 workgroups: segments of 3 sub-blocks (a pair and
+    # a lone one), the last ragged
+    (1, 1, 767 * 64 - 5, 64, "default", True),
 ]
 
 
