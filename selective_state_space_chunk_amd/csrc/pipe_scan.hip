@@ -48,6 +48,10 @@ struct PipeSmem {
     // four compute waves (16 columns each) in one step, stored in the next
     // (by t % 2); chunk c of row r at c ^ ((r >> 1) & 7)
     __bf16 YS[2][kSub * kP];
+    // dt of the sub-block of step s (token j at [s % 4][j], 0 past the end):
+    // loaded four steps ahead and written two steps ahead by the compute
+    // waves, a quarter of the tokens each; read by all eight waves
+    float dts[4][kSub];
 };
 
 
@@ -108,46 +112,22 @@ __device__ __forceinline__ void load_bc_at(BulkBC<N> &sl, const Args &a, const L
         sl.c[k] = ld16(rc, o.gb + k * step);
     }
 }
-template <int N, bool kOut>
-__device__ __forceinline__ void load_small_at(Small &sl, const Args &a, const LaneOffs<N> &o, int64_t go, int64_t dof,
-                                              int q, int ow, int lane) {
-    if constexpr (kOut) {
-        const rsrc_t rg = rsrc(a.gram + go, q > 0 ? kSub * kSub * 2 : 0);
+// This wave's gram tiles of one sub-block (tiles ow, ow+4, ow+8).
+__device__ __forceinline__ void load_g_at(uint2 (&g)[3], const Args &a, int64_t go, int q, int ow, int lane) {
+    const rsrc_t rg = rsrc(a.gram + go, q > 0 ? kSub * kSub * 2 : 0);
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            const int k = ow + 4 * m < 10 ? ow + 4 * m : 9;   // waves with two tiles load their last twice
-            sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
-        }
+    for (int m = 0; m < 3; ++m) {
+        const int k = ow + 4 * m < 10 ? ow + 4 * m : 9;   // waves with two tiles load their last twice
+        g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
     }
+}
+// dt of one token of a sub-block (element offset dof of its first row; token
+// offset gdq in bytes), 0 past its q tokens.
+__device__ __forceinline__ float load_dt_at(const Args &a, int64_t dof, int q, int gdq) {
     const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
-    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, gdq, 0, 0));
 }
 
-template <int N>
-__device__ __forceinline__ void load_x(BulkX &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t h, int sb) {
-    const int q = sub_tokens(a, sb);
-    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
-    const rsrc_t r = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
-    const int step = (int)(32 * a.H * kP * 2);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) sl.x[k] = ld16(r, o.gx + k * step);
-}
-template <int N>
-__device__ __forceinline__ void load_bc(BulkBC<N> &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t g,
-                                        int sb) {
-    using O = LaneOffs<N>;
-    const int q = sub_tokens(a, sb);
-    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
-    const int bytes = (int)(((int64_t)(q - 1) * a.G * N + N) * 2);
-    const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, bytes);
-    const rsrc_t rc = rsrc(a.Cm + (row0 * a.G + g) * N, bytes);
-    const int step = (int)((256 / O::CPR) * a.G * N * 2);
-#pragma unroll
-    for (int k = 0; k < N / 32; ++k) {
-        sl.b[k] = ld16(rb, o.gb + k * step);
-        sl.c[k] = ld16(rc, o.gb + k * step);
-    }
-}
 template <int N>
 __device__ __forceinline__ void stage_x(PipeSmem<N> &sm, int xbuf, const BulkX &sl, const LaneOffs<N> &o) {
     unsigned char *Xb = reinterpret_cast<unsigned char *>(sm.X[xbuf]);
@@ -166,24 +146,17 @@ __device__ __forceinline__ void stage_bc(PipeSmem<N> &sm, int par, const BulkBC<
     }
 }
 
-// dt of sub-block sb (lane = token) and, for output waves, their G tiles.
-template <int N, bool kOut>
-__device__ __forceinline__ void load_small(Small &sl, const Args &a, const LaneOffs<N> &o, int64_t b, int64_t h,
-                                           int64_t g, int sb, int ow, int lane) {
-    const int q = sub_tokens(a, sb);
-    const int64_t row0 = b * a.L + (int64_t)sb * kSub;
-    if constexpr (kOut) {
-        const rsrc_t rg = rsrc(a.gram + ((b * a.G + g) * a.nsb + sb) * (int64_t)(kSub * kSub), kSub * kSub * 2);
-#pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            const int k = ow + 4 * m < 10 ? ow + 4 * m : 9;   // waves with two tiles load their last twice
-            sl.g[m] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, (k * 64 + lane) * 8, 0, 0));
-        }
-    }
-    const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(q - 1) * a.H + 1) * 4));
-    sl.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
-}
 
+
+// Waits for the loads of the state held in H.  Without it the state enters a
+// step loop with its loads in flight on that path, and the wait counts the
+// compiler derives for the loop (one set for every path in) then make each
+// step wait for the latest x loads where it first reads the state.
+template <int NT>
+__device__ __forceinline__ void settle(f32x4 (&H)[NT]) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) asm volatile("" ::"v"(H[u]));
+}
 
 template <int N>
 __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
@@ -254,7 +227,19 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                                                    o.gx + k * step, 0, 0);
     };
 
-    Small small[2];
+    // compute wave pq loads dt of tokens 16pq .. 16pq+15 (four lanes each)
+    const int dq_tok = 16 * pq + (lane & 15);
+    const int gdq = dq_tok * (int)(a.H * 4);
+    if (compute_wave) {
+        const int t1 = T > 1 ? 1 : 0;
+        const float d0 = load_dt_at(a, d_at(0), q_of(0), gdq);
+        const float d1 = load_dt_at(a, d_at(t1), q_of(t1), gdq);
+        if (lane < 16) {
+            sm.dts[0][dq_tok] = d0;
+            sm.dts[1][dq_tok] = d1;
+        }
+    }
+    __syncthreads();
 
     if (compute_wave) {
         // ------------------------------------------------------------------
@@ -262,18 +247,22 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow.  The
         // outputs of sub-block t: lane holds token i = 16it + lrow,
         // p = 16pq + 4lgrp + 0..3.
-        // prologue: x of sub-block 0 staged; x of sub-blocks 1 and 2 and dt
-        // of sub-blocks 0 and 1 in flight.  x is loaded three steps ahead:
-        // during step t, bulk[0..2] hold x of steps t+1..t+3.
-        BulkX bulk[3];
+        // prologue: x of sub-block 0 staged; x of sub-blocks 1 and 2 and this
+        // wave's dt quarters of sub-blocks 2 and 3 in flight.  bulk[s % 2]
+        // holds x of step s from its load (issued at the end of step s-3)
+        // until it is staged at the end of step s-1; dq[t % 2] holds the dt
+        // quarter of step t+2 (loaded in step t-2), written to LDS in step t
+        // and replaced by that of t+4.
+        BulkX bulk[2];
+        float dq[2];
         {
-            const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1;
+            const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1, t3 = T > 3 ? 3 : T - 1;
             load_x_at<N>(bulk[0], a, o, x_at(0), q_of(0));
-            load_small_at<N, false>(small[0], a, o, 0, d_at(0), q_of(0), 0, lane);
-            load_small_at<N, false>(small[1], a, o, 0, d_at(t1), q_of(t1), 0, lane);
+            dq[0] = load_dt_at(a, d_at(t2), q_of(t2), gdq);
+            dq[1] = load_dt_at(a, d_at(t3), q_of(t3), gdq);
             stage_x<N>(sm, 0, bulk[0], o);
-            load_x_at<N>(bulk[0], a, o, x_at(t1), q_of(t1));
-            load_x_at<N>(bulk[1], a, o, x_at(t2), q_of(t2));
+            load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
+            load_x_at<N>(bulk[0], a, o, x_at(t2), q_of(t2));
         }
         f32x4 Hacc[NT];
         const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
@@ -283,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 #pragma unroll
             for (int u = 0; u < NT; ++u)
                 Hacc[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, (lane_off + 16 * u) * 4, 0, 0));
+            settle(Hacc);
         }
         __syncthreads();
         // this lane's 8 bytes of the y tile (rows 16it + lrow, columns 16pq + 4lgrp..+3)
@@ -310,26 +300,27 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 #pragma unroll
                 for (int u = 0; u < NT; ++u) Hacc[u] = gq * Hacc[u] + *reinterpret_cast<const f32x4 *>(sq + 16 * u);
             }
+            settle(Hacc);
         };
-        auto step = [&](int t, int par, Small &sl) __attribute__((always_inline)) {
+        auto step = [&](int t, int par) __attribute__((always_inline)) {
             const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[par]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
             const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
             const unsigned char *Mr = reinterpret_cast<const unsigned char *>(sm.Mm[par]);
             const float Ah2 = t >= nown ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
-            const float dt = sl.dt;
+            const float dt = sm.dts[t & 3][lane];
             const float v = wave_scan(dt * Ah2);
             const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
             wd.w[lane] = ex2(lend - v) * dt;
             wd.rdec[lane] = ex2(v);
             const float gam = ex2(lend);
-            // dt of step t+2 into the slot just read; x of step t+3
+            // this wave's dt quarter of step t+2 into LDS, that of t+4 into
+            // its register
             {
-                const int tl = t + 2 < T ? t + 2 : T - 1;
-                const int tx = t + 3 < T ? t + 3 : T - 1;
-                load_small_at<N, false>(sl, a, o, 0, d_at(tl), q_of(tl), 0, lane);
-                load_x_at<N>(bulk[2], a, o, x_at(tx), q_of(tx));
+                if (lane < 16) sm.dts[(t + 2) & 3][dq_tok] = dq[par];
+                const int td = t + 4 < T ? t + 4 : T - 1;
+                dq[par] = load_dt_at(a, d_at(td), q_of(td), gdq);
             }
             // the whole rows of y of step t-1 (written to YS by the four compute waves in step t-1)
             store_y(t - 1, par ^ 1);
@@ -430,23 +421,29 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 for (int u = 0; u < 4; ++u) Hacc[4 * v4 + u] = mfma(bt[r & 1][u], xw[ks], Hacc[4 * v4 + u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (t + 1 < T) stage_x<N>(sm, par ^ 1, bulk[0], o);
-            bulk[0] = bulk[1];
-            bulk[1] = bulk[2];
+            // x of step t+1 into LDS, and x of step t+3 into its registers.
+            // Unconditional: a conditional stage leaves its loads unwaited on
+            // one path, and the loop head then waits for them on every path
+            // (the last step stages into a slot nobody reads).
+            stage_x<N>(sm, par ^ 1, bulk[par ^ 1], o);
+            {
+                const int tx = t + 3 < T ? t + 3 : T - 1;
+                load_x_at<N>(bulk[par ^ 1], a, o, x_at(tx), q_of(tx));
+            }
             __syncthreads();
         };
         // steps [t0, t1) with the parity of each step known at compile time
         auto run = [&](int t0, int t1) __attribute__((always_inline)) {
             int t = t0;
             if ((t & 1) && t < t1) {
-                step(t, 1, small[1]);
+                step(t, 1);
                 ++t;
             }
             for (; t + 1 < t1; t += 2) {
-                step(t, 0, small[0]);
-                step(t + 1, 1, small[1]);
+                step(t, 0);
+                step(t + 1, 1);
             }
-            if (t < t1) step(t, 0, small[0]);
+            if (t < t1) step(t, 0);
         };
         run(0, nown);
         if (has_x) {
@@ -470,12 +467,12 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         BulkBC<N> bulk[2];   // Bm, Cm of step t+1 (staged at the end of step t) and t+2
         // decays and this wave's tiles of the masked matrix of the sub-block
         // of step tau, from sl, into Mm[slot]
-        auto build_m = [&](int tau, const Small &sl, int slot) __attribute__((always_inline)) {
+        auto build_m = [&](int tau, const uint2 (&gt)[3], int slot) __attribute__((always_inline)) {
             const bool xs = tau >= nown;
             const float Ah2 = xs ? Ahx2 : Ah2v;
             const float Dh = xs ? Dhx : Dhv;
-            wd.lam[lane] = wave_scan(sl.dt * Ah2);
-            wd.dt[lane] = sl.dt;
+            const float *dtrow = sm.dts[tau & 3];
+            wd.lam[lane] = wave_scan(dtrow[lane] * Ah2);
             uint2 mt[3];
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
@@ -485,8 +482,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 const int i = 16 * ti + lrow, j0 = 16 * tj + 4 * lgrp;
                 const float li = wd.lam[i];
                 const f32x4 lj = *reinterpret_cast<const f32x4 *>(&wd.lam[j0]);
-                const f32x4 dj = *reinterpret_cast<const f32x4 *>(&wd.dt[j0]);
-                const uint32_t gw[2] = {sl.g[m].x, sl.g[m].y};
+                const f32x4 dj = *reinterpret_cast<const f32x4 *>(&dtrow[j0]);
+                const uint32_t gw[2] = {gt[m].x, gt[m].y};
                 float mv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -516,41 +513,40 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             }
         };
         // prologue: Bm, Cm of sub-block 0 staged and its masked matrix built;
-        // Bm, Cm of sub-block 1 and the dt and G tiles of sub-blocks 1 and 2 in flight
+        // the G tiles of sub-blocks 1 and 2 and Bm, Cm of sub-block 1 in
+        // flight, issued in the order a step issues them (G tiles, then Bm,
+        // Cm), so that the loop is entered with the loads of its steady state
+        uint2 gt[2][3];
         {
             const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1;
+            load_g_at(gt[0], a, g_at(0), q_of(0), pq, lane);
+            load_g_at(gt[1], a, g_at(t1), q_of(t1), pq, lane);
             load_bc_at<N>(bulk[0], a, o, b_at(0), q_of(0));
-            load_small_at<N, true>(small[0], a, o, g_at(0), d_at(0), q_of(0), pq, lane);
-            load_small_at<N, true>(small[1], a, o, g_at(t1), d_at(t1), q_of(t1), pq, lane);
             stage_bc<N>(sm, 0, bulk[0], o);
+            build_m(0, gt[0], 0);
+            load_g_at(gt[0], a, g_at(t2), q_of(t2), pq, lane);
             load_bc_at<N>(bulk[1], a, o, b_at(t1), q_of(t1));
-            build_m(0, small[0], 0);
-            load_small_at<N, true>(small[0], a, o, g_at(t2), d_at(t2), q_of(t2), pq, lane);
         }
         __syncthreads();
         // Every step issues the same global loads (loads past the last
         // sub-block repeat it), so that the wait counts the compiler derives
         // at the loop head are those of the steady state.
         auto step = [&](int t, int par) __attribute__((always_inline)) {
-            // sub-block t+1 (its dt and G tiles were loaded in step t-1), then
-            // the dt and G tiles of t+3 into the same slot
-            build_m(t + 1, small[par ^ 1], par ^ 1);
+            // sub-block t+1 (its G tiles were loaded in step t-1, its dt is in
+            // LDS), then the G tiles of t+3 into the same slot
+            build_m(t + 1, gt[par ^ 1], par ^ 1);
             {
                 const int tl = t + 3 < T ? t + 3 : T - 1;
-                load_small_at<N, true>(small[par ^ 1], a, o, g_at(tl), d_at(tl), q_of(tl), pq, lane);
+                load_g_at(gt[par ^ 1], a, g_at(tl), q_of(tl), pq, lane);
             }
             {
                 const int tl = t + 2 < T ? t + 2 : T - 1;
                 load_bc_at<N>(bulk[par], a, o, b_at(tl), q_of(tl));
             }
-            if (t + 1 < T) stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);
+            stage_bc<N>(sm, par ^ 1, bulk[par ^ 1], o);   // unconditional, as stage_x
             __syncthreads();
         };
-        // steps 0..T-1, the first two outside the loop so that the loop is
-        // entered in the steady state
-        step(0, 0);
-        if (T > 1) step(1, 1);
-        int t = 2;
+        int t = 0;
         for (; t + 1 < T; t += 2) {
             step(t, 0);
             step(t + 1, 1);
