@@ -17,7 +17,10 @@ Measurement helpers (used to produce the files under profiles/):
       for scaling the FETCH_SIZE / WRITE_SIZE counters);
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --copy-mb MB
       turns four `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE` output folders into
-      profiles/traffic_m2_2p7b.json (HBM bytes per scan launch).
+      profiles/traffic_m2_2p7b.json (HBM bytes per scan launch);
+  python bench.py --summarize-mfma DIR [--cus 256] [--xcds 8]
+      per-kernel matrix-core utilisation from a `rocprofv3 --pmc
+      SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` output folder.
 """
 from __future__ import annotations
 
@@ -192,9 +195,44 @@ def cpu_baseline(w, budget_s=15.0):
         el += time.perf_counter() - t0
         reps += 1
     return {"value": reps * n * w.L / el / w.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 token-by-token recurrence over {n} of the {chains} (batch, head) "
                       f"sequences of L={w.L} tokens, {reps} run(s), {el:.1f} s on {threads} threads; "
                       f"tokens/s = runs*sequences*L/s / H"}
+
+
+def copy_bandwidth(device, mb=512, reps=10):
+    """Measured device-copy bandwidth (GB/s, bytes read + written) of a plain
+    `mb`-megabyte copy, median of `reps` event-timed launches: the practical
+    ceiling the scan's achieved bandwidth is also reported against."""
+    import torch
+    n = int(mb * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize(device)
+    times = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize(device)
+        times.append(s.elapsed_time(e))
+    times.sort()
+    return 2 * n * 4 / (times[len(times) // 2] * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def scan_traffic():
@@ -237,6 +275,27 @@ def _pmc_kib(folder, counter, match):
     return sum(vals.values()) / len(vals), len(vals)
 
 
+def summarize_mfma(folder, cus, xcds):
+    """Per-kernel matrix-core utilisation from a rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: busy cycles (summed over
+    all SIMDs: 16 per 16x16x32 bf16 instruction) over (active cycles x compute
+    units x 4 SIMDs), averaged over dispatches.  GRBM_GUI_ACTIVE comes summed
+    over the XCDs, so it is divided by their number."""
+    rows = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                d = rows.setdefault((row["Kernel_Name"], row["Dispatch_Id"]), {})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (name, _), d in rows.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("GRBM_GUI_ACTIVE"):
+            active = d["GRBM_GUI_ACTIVE"] / xcds
+            per.setdefault(name, []).append(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * cus * 4))
+    out = {n: {"dispatches": len(v), "mfma_util": sum(v) / len(v)} for n, v in per.items()}
+    print(json.dumps(out, indent=1))
+
+
 def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb):
     copy_bytes = int(copy_mb * 1e6) // 4 * 4
     cf, _ = _pmc_kib(copy_fetch_dir, "FETCH_SIZE", "copy")
@@ -274,12 +333,18 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--copy-mb", type=float, default=512.0)
+    ap.add_argument("--summarize-mfma", default=None, metavar="DIR")
+    ap.add_argument("--cus", type=int, default=256)
+    ap.add_argument("--xcds", type=int, default=8)
     ap.add_argument("--workload", default="m2_2p7b",
                     help="scan workload to time (m2_2p7b is the headline; tiny_fp32, m2_130m, long_n128, "
                          "long_n256 are the other scan shapes)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.copy_mb)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.cus, args.xcds)
         return
     if args.calibrate_copy is not None:
         calibrate_copy(args.calibrate_copy, args.steps)
@@ -326,6 +391,9 @@ def main():
                      "algorithmic_bytes": byts, "algorithmic_flops": flops,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    copy_gbs = copy_bandwidth(device)
+    out["roofline"]["copy_gbs"] = copy_gbs
+    out["roofline"]["frac_of_copy"] = achieved / copy_gbs
     if not headline:
         del out["roofline"]["kernels"]
     if not args.no_decode:
@@ -339,6 +407,7 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": sb / (smean * 1e-3) / 1e9,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
                                       "algorithmic_bytes": sb}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
