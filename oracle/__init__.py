@@ -11,6 +11,9 @@ Forms:
 * ``step`` -- one decode token, the same update applied once, in C.
 * ``quadratic`` / ``chunked`` -- numpy fp64 matrix and block-decomposition
   forms (``forms.py``), used to pin the recurrence.
+* ``recurrence_bwd`` -- gradients of the scan: the adjoint of the recurrence,
+  run backwards in time (``backward.py``, numpy), pinned by finite
+  differences of ``recurrence``, exact adjointness and closed forms.
 
 Every function takes float64 arrays (the values the GPU receives, widened
 exactly) and returns float64 arrays.
@@ -25,6 +28,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from .forms import chunked, decay_mask, quadratic  # noqa: F401
+from .backward import recurrence_bwd  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
