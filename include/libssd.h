@@ -165,6 +165,53 @@ ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_byte
                                           int64_t N, int64_t chunk_size, hipStream_t stream);
 
 /*
+ * Bytes of device workspace ssd_chunk_scan_bwd needs for this shape: the
+ * state entering every 64-token sub-block and the gradient of the state
+ * leaving it, and per-head partial gradients of Bm and Cm (four float32
+ * arrays of B*H*ceil(L/64)*64*N), plus per-sub-block parts of dA and dD.
+ * Returns 0 when the backward does not cover the shape or dtype.  No
+ * zero-filling is needed; calls sharing a workspace must be ordered on one
+ * stream.
+ */
+size_t ssd_chunk_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                         int64_t N, int64_t chunk_size, ssd_dtype dtype);
+
+/*
+ * Chunked SSD scan, backward: the gradients of the scalar
+ *     <dy, y> + <dfinal, final_state>
+ * with respect to every input of ssd_chunk_scan_fwd, i.e. the adjoint of the
+ * recurrence of the "Mamba-2" note (section "writing the SSM as a matrix")
+ * evaluated block by block as in the block decomposition of the "Mamba-2
+ * model walkthrough" (section 6.1).  The forward states are recomputed, not
+ * taken from a forward call.
+ *
+ *   x, dt, A, Bm, Cm, D, init_state   as for ssd_chunk_scan_fwd (init_state nullable)
+ *   dy       [B, L, H, P]   dtype    gradient of y
+ *   dfinal   [B, H, P, N]   float32  gradient of the final state, or NULL for zeros
+ *   dx       [B, L, H, P]   dtype    written
+ *   ddt      [B, L, H]      float32  written
+ *   dA       [H]            float32  written (summed over batch rows and tokens)
+ *   dBm      [B, L, G, N]   dtype    written (summed over the heads of each group)
+ *   dCm      [B, L, G, N]   dtype    written (summed over the heads of each group)
+ *   dD       [H]            float32  written
+ *   dinit    [B, H, P, N]   float32  gradient of init_state, or NULL to skip
+ *   workspace  device memory of at least ssd_chunk_scan_bwd_workspace_size(...) bytes
+ *
+ * Supported: dtype SSD_DTYPE_BF16, P == 64, N == 64 or 128, chunk_size as for
+ * the forward (the result does not depend on it beyond rounding); anything
+ * else returns SSD_ERR_UNSUPPORTED.  Products run on the matrix cores with
+ * bfloat16 operands and float32 accumulation.  Outputs must not alias inputs.
+ * Errors as for ssd_chunk_scan_fwd.  L == 0 or B == 0 writes dA = dD = 0 and
+ * dinit = dfinal (or zeros).
+ */
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm,
+                              const void *Cm, const float *D, const float *init_state, const void *dy,
+                              const float *dfinal, void *dx, float *ddt, float *dA, void *dBm, void *dCm,
+                              float *dD, float *dinit, void *workspace, size_t workspace_bytes, int64_t B,
+                              int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk_size,
+                              ssd_dtype dtype, hipStream_t stream);
+
+/*
  * One recurrent decode step: the update above for a single token, in place.
  *
  *   state  [B, H, P, N]  float32  read and overwritten with the updated state

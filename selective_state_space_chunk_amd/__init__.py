@@ -65,6 +65,10 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_workspace_check.restype = ctypes.c_int
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ssd_step.restype = ctypes.c_int
+    lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
+    lib.ssd_chunk_scan_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
+    lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -207,6 +211,57 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Te
                       Bsz, H, P, G, N, _dtype_code(x.dtype), _stream_handle(dev, stream))
     _check(st, "ssd_step")
     return y
+
+
+def ssd_chunk_scan_bwd_workspace_size(B: int, L: int, H: int, P: int, G: int, N: int,
+                                      chunk_size: int, dtype: torch.dtype) -> int:
+    return int(load_library().ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, chunk_size,
+                                                                _dtype_code(dtype)))
+
+
+def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, D: torch.Tensor, init_state: Optional[torch.Tensor],
+                       dy: torch.Tensor, dfinal: Optional[torch.Tensor] = None, chunk_size: int = 256, *,
+                       want_dinit: bool = True, workspace_tensor: Optional[torch.Tensor] = None,
+                       stream=None) -> Dict[str, Optional[torch.Tensor]]:
+    """Gradients of <dy, y> + <dfinal, final_state> of the chunk scan with
+    respect to x, dt, A, Bm, Cm, D and init_state.  Shapes as
+    ssd_chunk_scan_fwd; dy like x, dfinal [B,H,P,N] f32 or None.  Returns a dict
+    dx, ddt, dA, dBm, dCm, dD, dinit (dinit None unless want_dinit)."""
+    lib = load_library()
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    _need(x, "x", x.dtype, (Bsz, L, H, P), dev)
+    _need(dt, "dt", torch.float32, (Bsz, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(Bm, "Bm", x.dtype, (Bsz, L, G, N), dev)
+    _need(Cm, "Cm", x.dtype, (Bsz, L, G, N), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    _need(dy, "dy", x.dtype, (Bsz, L, H, P), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (Bsz, H, P, N), dev)
+    if dfinal is not None:
+        _need(dfinal, "dfinal", torch.float32, (Bsz, H, P, N), dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+           "dA": torch.empty((H,), dtype=torch.float32, device=dev),
+           "dBm": torch.empty_like(Bm), "dCm": torch.empty_like(Cm),
+           "dD": torch.empty((H,), dtype=torch.float32, device=dev),
+           "dinit": torch.empty((Bsz, H, P, N), dtype=torch.float32, device=dev) if want_dinit else None}
+    code = _dtype_code(x.dtype)
+    need = int(lib.ssd_chunk_scan_bwd_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
+    if workspace_tensor is None and need > 0:
+        workspace_tensor = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
+    st = lib.ssd_chunk_scan_bwd(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),
+        _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dBm"]), _ptr(out["dCm"]),
+        _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace_tensor), ws_bytes, Bsz, L, H, P, G, N,
+        chunk_size, code, _stream_handle(dev, stream))
+    _check(st, "ssd_chunk_scan_bwd")
+    return out
 
 
 def version() -> str:

@@ -19,6 +19,12 @@ hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
 bool pipe_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pair_scan(const ScanArgs &a, const Workspace &ws);
 bool pair_supported(int64_t H, int64_t G, int64_t N);
+bool bwd_supported(int64_t P, int64_t N, int64_t H, int64_t G);
+size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t N);
+hipError_t launch_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
+                           const float *D, const float *init, const void *dy, const float *dfinal, void *dx,
+                           float *ddt, float *dA, void *dBm, void *dCm, float *dD, float *dinit, float *ws,
+                           int64_t B, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream);
 }
 
 namespace {
@@ -224,6 +230,52 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    hipStream_t stream) {
     return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes,
                      B, L, H, P, G, N, chunk_size, dtype, algo, stream);
+}
+
+size_t ssd_chunk_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                         int64_t N, int64_t chunk_size, ssd_dtype dtype) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0) return 0;
+    if (H % G != 0 || !shape_supported(P, N, chunk_size)) return 0;
+    if (dtype != SSD_DTYPE_BF16 || !bwd_supported(P, N, H, G)) return 0;
+    return align_up(bwd_workspace_floats(B, L, H, N) * sizeof(float));
+}
+
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm,
+                              const void *Cm, const float *D, const float *init_state, const void *dy,
+                              const float *dfinal, void *dx, float *ddt, float *dA, void *dBm, void *dCm,
+                              float *dD, float *dinit, void *workspace, size_t workspace_bytes, int64_t B,
+                              int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk_size,
+                              ssd_dtype dtype, hipStream_t stream) {
+    const bool has_work = B > 0 && L > 0;
+    ssd_status st = common_checks(x, dt, A, Bm, Cm, D, dy, B, L, H, P, G, N, dtype, has_work);
+    if (st != SSD_OK) return st;
+    if (!dA || !dD) return SSD_ERR_INVALID_ARG;
+    if (has_work && (!dx || !ddt || !dBm || !dCm)) return SSD_ERR_INVALID_ARG;
+    const void *ptrs[] = {init_state, dfinal, dx, ddt, dA, dBm, dCm, dD, dinit};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return SSD_ERR_INVALID_ARG;
+    if (chunk_size <= 0) return SSD_ERR_INVALID_ARG;
+    if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !bwd_supported(P, N, H, G))
+        return SSD_ERR_UNSUPPORTED;
+    if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
+    const int64_t nsb = (L + 63) / 64;
+    if (B * H * nsb > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (!has_work) {
+        // no tokens: dA = dD = 0 and the initial state's gradient is dfinal (or 0)
+        fill_or_copy<<<(unsigned)((H + 255) / 256), 256, 0, stream>>>(dA, nullptr, H);
+        fill_or_copy<<<(unsigned)((H + 255) / 256), 256, 0, stream>>>(dD, nullptr, H);
+        if (dinit && B > 0) {
+            const int64_t n = B * H * P * N;
+            fill_or_copy<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(dinit, dfinal, n);
+        }
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    const size_t need = align_up(bwd_workspace_floats(B, L, H, N) * sizeof(float));
+    if (!workspace || workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
+    const hipError_t e = launch_scan_bwd(x, dt, A, Bm, Cm, D, init_state, dy, dfinal, dx, ddt, dA, dBm, dCm,
+                                         dD, dinit, (float *)workspace, B, L, H, G, N, stream);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
 ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes, int64_t B,

@@ -36,7 +36,8 @@ import numpy as np
 # tensor ids for default_rng([seed, id]); fixed so that every consumer draws the
 # same stream for the same tensor
 _TID = {"x": 1, "dt": 2, "A": 3, "Bm": 4, "Cm": 5, "D": 6, "init": 7,
-        "step_x": 11, "step_dt": 12, "step_Bm": 14, "step_Cm": 15}
+        "step_x": 11, "step_dt": 12, "step_Bm": 14, "step_Cm": 15,
+        "dy": 21, "dfinal": 22}
 
 SEED_BASE = 20240531
 
@@ -187,6 +188,18 @@ def make_step_state(B: int, H: int, P: int, N: int, *, seed: int = SEED_BASE) ->
 def workload_scan_inputs(w: Workload, regime: str = "default"):
     return make_scan_inputs(w.B, w.L, w.H, w.P, w.N, w.G, dtype=w.dtype, init=w.init,
                             seed=w.seed, regime=regime)
+
+
+def make_grad_inputs(B: int, L: int, H: int, P: int, N: int, *, dtype: str = "bf16",
+                     dfinal: bool = True, seed: int = SEED_BASE) -> Dict[str, Optional[np.ndarray]]:
+    """Seeded upstream gradients for the backward scan: dy ~ N(0,1) in the
+    storage dtype of y [B,L,H,P], and dfinal ~ N(0, 0.1) float32 [B,H,P,N]
+    (or None)."""
+    out: Dict[str, Optional[np.ndarray]] = {}
+    out["dy"] = _store(_rng(seed, "dy").standard_normal((B, L, H, P)), dtype)
+    out["dfinal"] = (np.ascontiguousarray(_rng(seed, "dfinal").standard_normal((B, H, P, N)) * 0.1,
+                                          dtype=np.float32) if dfinal else None)
+    return out
 
 
 def as_f64(arrs: Dict[str, Optional[np.ndarray]]) -> Dict[str, Optional[np.ndarray]]:

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
               "ssd_status_string", "ssd_chunk_scan_fwd_algo", "ssd_version",
-              "ssd_chunk_scan_workspace_check"):
+              "ssd_chunk_scan_workspace_check", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size"):
         assert n in names
 
 
@@ -134,3 +134,16 @@ def test_binding_refuses_to_run_without_library(monkeypatch):
     monkeypatch.setattr(ssd, "LIB_PATH", "/nonexistent/libssd.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         ssd.load_library()
+
+
+def test_backward_workspace_size(lib):
+    # states entering and gradients leaving every sub-block, and per-head parts of
+    # dBm and dCm: four float32 arrays of B*H*nsb*64*N, plus B*H*nsb parts of dA and dD
+    nsb = (L + 63) // 64
+    want = 4 * (4 * B * H * nsb * 64 * N + 2 * B * H * nsb)
+    want = (want + 255) // 256 * 256
+    assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 1) == want
+    # not covered: float32, P != 64, N = 256
+    assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 0) == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, 32, G, N, Q, 1) == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, 256, Q, 1) == 0
