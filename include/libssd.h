@@ -167,8 +167,8 @@ ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_byte
 /*
  * Bytes of device workspace ssd_chunk_scan_bwd needs for this shape: the
  * state entering every 64-token sub-block and the gradient of the state
- * leaving it, and per-head partial gradients of Bm and Cm (four float32
- * arrays of B*H*ceil(L/64)*64*N), plus per-sub-block parts of dA and dD.
+ * leaving it (two bfloat16 arrays of B*H*ceil(L/64)*64*N), plus float32
+ * parts of dA and dD per (batch row, head, sub-block).
  * Returns 0 when the backward does not cover the shape or dtype.  No
  * zero-filling is needed; calls sharing a workspace must be ordered on one
  * stream.

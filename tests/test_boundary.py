@@ -137,10 +137,10 @@ def test_binding_refuses_to_run_without_library(monkeypatch):
 
 
 def test_backward_workspace_size(lib):
-    # states entering and gradients leaving every sub-block, and per-head parts of
-    # dBm and dCm: four float32 arrays of B*H*nsb*64*N, plus B*H*nsb parts of dA and dD
+    # states entering and gradients leaving every sub-block: two bfloat16 arrays of
+    # B*H*nsb*64*N, plus B*H*nsb float32 parts of dA and of dD
     nsb = (L + 63) // 64
-    want = 4 * (4 * B * H * nsb * 64 * N + 2 * B * H * nsb)
+    want = 2 * 2 * B * H * nsb * 64 * N + 4 * 2 * B * H * nsb
     want = (want + 255) // 256 * 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 1) == want
     # not covered: float32, P != 64, N = 256
