@@ -77,6 +77,19 @@ def scan_algorithmic(w):
     return byts, flops
 
 
+def bwd_algorithmic(w):
+    """Bytes of the backward read or written once: x, dy, dt, Bm, Cm, the
+    initial state and dfinal in; dx, ddt, dBm, dCm, dA, dD, dinit out."""
+    B, L, H, P, N, G = w.B, w.L, w.H, w.P, w.N, w.G
+    e = 2 if w.dtype == "bf16" else 4
+    return (3 * B * L * H * P * e          # x, dy in; dx out
+            + 2 * B * L * H * 4            # dt in, ddt out
+            + 4 * B * L * G * N * e        # Bm, Cm in; dBm, dCm out
+            + 4 * H * 4                    # A, D in; dA, dD out
+            + (B * H * P * N * 4 if w.init else 0)   # initial state
+            + 2 * B * H * P * N * 4)       # dfinal in, dinit out
+
+
 def step_algorithmic(B, H, P, N, G, e=2):
     byts = (2 * B * H * P * N * 4          # state read + write
             + 2 * B * H * P * e            # x in, y out
@@ -164,6 +177,37 @@ def time_step(B, H, P, N, G, steps, warmup, device):
         i = ins[k % 4]
         starts[k].record()
         ssd.ssd_step(st, i["x"], i["dt"], i["A"], i["Bm"], i["Cm"], i["D"], y=ys[k % 4])
+        ends[k].record()
+    torch.cuda.synchronize(device)
+    return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def time_backward(w, steps, warmup, device):
+    """Per-call event times (ms) of ssd_chunk_scan_bwd over rotating input sets."""
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    import ssd_inputs as si
+    sets = make_device_sets(w, 3, device)
+    for k, s in enumerate(sets):
+        g = si.make_grad_inputs(w.B, w.L, w.H, w.P, w.N, dtype=w.dtype, seed=w.seed + 100 * k + 7)
+        s["dy"] = torch.from_numpy(g["dy"]).to(device=device, dtype=io_dtype(w))
+        s["dfinal"] = torch.from_numpy(g["dfinal"]).to(device=device)
+    nbytes = ssd.ssd_chunk_scan_bwd_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def run(k):
+        s = sets[k % len(sets)]
+        ssd.ssd_chunk_scan_bwd(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], s["D"], s["init"], s["dy"],
+                               s["dfinal"], w.chunk, workspace_tensor=ws)
+
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize(device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        starts[k].record()
+        run(k)
         ends[k].record()
     torch.cuda.synchronize(device)
     return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
@@ -329,6 +373,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -409,6 +454,18 @@ def main():
                                       "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
                                       "algorithmic_bytes": sb}}
+    if not args.no_backward and headline:
+        bp = time_backward(w, max(10, args.steps // 5), 3, device)
+        bmean = sum(bp) / len(bp)
+        bb = bwd_algorithmic(w)
+        out["backward"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_backward",
+                           "us_per_call": bmean * 1000.0, "us_median": bp[len(bp) // 2] * 1000.0,
+                           "tokens_per_s": tokens / (bmean * 1e-3),
+                           "kernels": "state_scan<128> forward and adjoint + chunk_grad<128> + reduce_head",
+                           "roofline": {"bound": "hbm", "achieved": bb / (bmean * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": bb}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -8,8 +8,9 @@
 // 64-token sub-blocks as in the block decomposition of the "Mamba-2 model
 // walkthrough" (section 6.1).  Only the states are sequential, so the work is
 // split into
-//   1. state_scan<N, false>: the state H_c entering every sub-block c;
-//   2. state_scan<N, true>:  backwards in time, the adjoint dH'_c of the state
+//   1. state_scans<N> (first half of its workgroups): the state H_c entering
+//      every sub-block c;
+//   2. state_scans<N> (second half): backwards in time, the adjoint dH'_c of the state
 //      leaving every sub-block, dH_c = g_c dH'_c + sum_i exp(Lambda_i) dy_i (x) Cm_i,
 //      whose last value is the initial state's gradient;
 //   3. chunk_grad<N>: one workgroup per (batch, group, sub-block), all in
@@ -41,14 +42,25 @@ struct BwdArgs {
     const float *dt, *A, *D, *init, *dfinal;   // init, dfinal nullable
     __bf16 *dx, *dBm, *dCm;
     float *ddt, *dA, *dD, *dinit;              // dinit nullable
-    float *Hs;    // [B*H, nsb, P, N] bf16  state entering each sub-block
-    float *dHs;   // [B*H, nsb, P, N] bf16  adjoint of the state leaving each sub-block
+    float *Hs;    // [B*H, nsb, P*N] bf16  state entering each sub-block
+    float *dHs;   // [B*H, nsb, P*N] bf16  adjoint of the state leaving each sub-block
+                  // (both in accumulator order: 4-value unit ((pq*NT + u)*64 + lane)
+                  //  holds p = 16pq + lane%16, n = 16u + 4(lane/16) + 0..3)
     float *dAp;   // [B*H, nsb]  each head's part of dA from each sub-block
     float *dDp;   // [B*H, nsb]
     int64_t B, L, H, G, nsb;
 };
 
 __device__ __forceinline__ float ex2f(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Waits for the loads of the state held in H before a step loop (otherwise
+// the loop's wait counts, derived for every path into it, make each step wait
+// for the latest loads where it first reads the state).
+template <int NT>
+__device__ __forceinline__ void settle(f32x4 (&H)[NT]) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) asm volatile("" ::"v"(H[u]));
+}
 
 __device__ __forceinline__ float shfl_xor(float v, int m) {
     const int lane = __lane_id();
@@ -74,12 +86,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 //             c = nsb-1 .. 0 and storing dH'_c; the last state is dinit.
 // with g = exp(Lambda_63) of the sub-block in both.
 template <int N, bool kRev>
-__global__ __launch_bounds__(256) void state_scan(BwdArgs a) {
+__device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
     __shared__ __align__(16) __bf16 lx[kSub * kP];
     __shared__ __align__(16) __bf16 lb[kSub * N];
     using O = LaneOffs<N>;
     constexpr int NT = N / 16, KB = N / 32;
-    const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const float Ah2 = a.A[h] * kLog2eB;
     const int tid = threadIdx.x;
@@ -90,21 +101,25 @@ __global__ __launch_bounds__(256) void state_scan(BwdArgs a) {
     const __bf16 *Mt = kRev ? a.Cm : a.Bm;
     const int nsb = (int)a.nsb;
 
-    uint4 ur[2], mr[KB];
-    float dtv = 0.f;
-    auto load = [&](int c) __attribute__((always_inline)) {
+    // register slot s % 2 holds the inputs of step s from its load (in step
+    // s - 2) until they are staged at the start of step s
+    uint4 ur[2][2], mr[2][KB];
+    float dtv[2];
+    auto load = [&](int s, int slot) __attribute__((always_inline)) {
+        s = s < nsb ? s : nsb - 1;
+        const int c = kRev ? nsb - 1 - s : s;
         const int64_t t0 = (int64_t)c * kSub;
         const int q = a.L - t0 < kSub ? (int)(a.L - t0) : kSub;
         const int64_t row0 = b * a.L + t0;
         const rsrc_t ru = rsrc(U + (row0 * a.H + h) * kP, (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2));
 #pragma unroll
-        for (int k = 0; k < 2; ++k) ur[k] = ld16(ru, o.gx + k * (int)(32 * a.H * kP * 2));
+        for (int k = 0; k < 2; ++k) ur[slot][k] = ld16(ru, o.gx + k * (int)(32 * a.H * kP * 2));
         const rsrc_t rm = rsrc(Mt + (row0 * a.G + g) * N, (int)(((int64_t)(q - 1) * a.G * N + N) * 2));
         const int step = (int)((256 / O::CPR) * a.G * N * 2);
 #pragma unroll
-        for (int k = 0; k < KB; ++k) mr[k] = ld16(rm, o.gb + k * step);
+        for (int k = 0; k < KB; ++k) mr[slot][k] = ld16(rm, o.gb + k * step);
         const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(q - 1) * a.H + 1) * 4));
-        dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+        dtv[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
     };
 
     const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
@@ -115,25 +130,28 @@ __global__ __launch_bounds__(256) void state_scan(BwdArgs a) {
         for (int u = 0; u < NT; ++u)
             Hacc[u] = src ? *reinterpret_cast<const f32x4 *>(src + bh * (kP * N) + lane_off + 16 * u)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        settle(Hacc);
     }
-    load(kRev ? nsb - 1 : 0);
-    __bf16 *sbase = reinterpret_cast<__bf16 *>(kRev ? a.dHs : a.Hs) + bh * a.nsb * (kP * N) + lane_off;
+    load(0, 0);
+    load(1, 1);
+    // states go out in accumulator order, 512 contiguous bytes per store
+    __bf16 *sbase = reinterpret_cast<__bf16 *>(kRev ? a.dHs : a.Hs) + bh * a.nsb * (kP * N) + 4 * (pq * NT * 64 + lane);
     const int row_k0 = tid >> 3;   // staged rows row_k0 and row_k0 + 32 of u
-    for (int s = 0; s < nsb; ++s) {
+    auto step = [&](int s, int par) __attribute__((always_inline)) {
         const int c = kRev ? nsb - 1 - s : s;
-        const float v = wave_scan(dtv * Ah2);
+        const float v = wave_scan(dtv[par] * Ah2);
         const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-        const float om = kRev ? ex2f(v) : ex2f(lend - v) * dtv;
+        const float om = kRev ? ex2f(v) : ex2f(lend - v) * dtv[par];
         const float gam = ex2f(lend);
 #pragma unroll
         for (int u = 0; u < NT; ++u)
-            *reinterpret_cast<uint2 *>(sbase + (int64_t)c * (kP * N) + 16 * u) =
+            *reinterpret_cast<uint2 *>(sbase + (int64_t)c * (kP * N) + 4 * 64 * u) =
                 uint2{pack2(Hacc[u][0], Hacc[u][1]), pack2(Hacc[u][2], Hacc[u][3])};
         // u weighted by om, and Mt, into LDS
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const float wgt = lane_get(om, row_k0 + 32 * k);
-            const bf16x8 xv = __builtin_bit_cast(bf16x8, ur[k]);
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, ur[par][k]);
             f32x4 x0, x1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -144,13 +162,9 @@ __global__ __launch_bounds__(256) void state_scan(BwdArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < KB; ++k)
-            lds_st<uint4>(reinterpret_cast<unsigned char *>(lb) + o.sb + k * (256 / O::CPR) * O::RB, mr[k]);
-        // the next sub-block into registers (past the ends it loads this one again)
-        {
-            int cn = kRev ? c - 1 : c + 1;
-            cn = cn < 0 ? 0 : (cn >= nsb ? nsb - 1 : cn);
-            load(cn);
-        }
+            lds_st<uint4>(reinterpret_cast<unsigned char *>(lb) + o.sb + k * (256 / O::CPR) * O::RB, mr[par][k]);
+        // step s+2 into the slot just staged (past the end it loads the last one again)
+        load(s + 2, par);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < NT; ++u) Hacc[u] *= gam;
@@ -169,11 +183,29 @@ __global__ __launch_bounds__(256) void state_scan(BwdArgs a) {
             }
         }
         __syncthreads();
+    };
+    int s = 0;
+    for (; s + 1 < nsb; s += 2) {
+        step(s, 0);
+        step(s + 1, 1);
     }
+    if (s < nsb) step(s, 0);
     if (kRev && a.dinit) {
 #pragma unroll
         for (int u = 0; u < NT; ++u) *reinterpret_cast<f32x4 *>(a.dinit + bh * (kP * N) + lane_off + 16 * u) = Hacc[u];
     }
+}
+
+// Both scans in one launch: workgroups below B*H take the forward states,
+// the others the adjoints, so that the two run side by side.
+template <int N>
+__global__ __launch_bounds__(256) void state_scans(BwdArgs a) {
+    const int64_t bhn = a.B * a.H;
+    const int64_t blk = blockIdx.x;
+    if (blk < bhn)
+        state_scan_body<N, false>(a, blk);
+    else
+        state_scan_body<N, true>(a, blk - bhn);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,7 +287,7 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
             *reinterpret_cast<uint4 *>(sm.C + r * SN + 8 * bc) = ld16(rc, off);
         }
     }
-    // this head's inputs: x, dy (two chunks each), dt, H and dH' (bf16 [p][n])
+    // this head's inputs: x, dy (two chunks each), dt, H and dH' (bf16, accumulator order)
     const int xr = tid >> 3, xc = tid & 7;
     uint4 xv[2], yv[2], hv[HCH], dv[HCH];
     float dtv;
@@ -306,10 +338,15 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         float hdot = 0.f;
 #pragma unroll
         for (int k = 0; k < HCH; ++k) {
-            const int idx = 8 * (k * 256 + tid);
-            const int p = idx / N, n = idx % N;
-            *reinterpret_cast<uint4 *>(sm.H + p * SN + n) = hv[k];
-            *reinterpret_cast<uint4 *>(sm.dH + p * SN + n) = dv[k];
+            // two 4-value units of the state in accumulator order: unit U holds
+            // p = 16 pq + l % 16, n = 16 u + 4 (l / 16) .. + 3 for U = (pq NT + u) 64 + l
+            const int U = 2 * (k * 256 + tid);
+            const int l = U % 64, u = (U / 64) % NT, pq = U / (64 * NT);
+            const int p = 16 * pq + (l & 15), n = 16 * u + 4 * (l >> 4);
+            *reinterpret_cast<uint2 *>(sm.H + p * SN + n) = uint2{hv[k].x, hv[k].y};
+            *reinterpret_cast<uint2 *>(sm.H + (p + 1) * SN + n) = uint2{hv[k].z, hv[k].w};
+            *reinterpret_cast<uint2 *>(sm.dH + p * SN + n) = uint2{dv[k].x, dv[k].y};
+            *reinterpret_cast<uint2 *>(sm.dH + (p + 1) * SN + n) = uint2{dv[k].z, dv[k].w};
             const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv[k]), d8 = __builtin_bit_cast(bf16x8, dv[k]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) hdot += (float)h8[e] * (float)d8[e];
@@ -516,8 +553,7 @@ __global__ __launch_bounds__(256) void reduce_head(BwdArgs a) {
 template <int N>
 hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     const int64_t bhn = a.B * a.H;
-    state_scan<N, false><<<dim3((unsigned)bhn), 256, 0, stream>>>(a);
-    state_scan<N, true><<<dim3((unsigned)bhn), 256, 0, stream>>>(a);
+    state_scans<N><<<dim3((unsigned)(2 * bhn)), 256, 0, stream>>>(a);
     chunk_grad<N><<<dim3((unsigned)(a.B * a.G * a.nsb)), 256, 0, stream>>>(a);
     reduce_head<<<dim3((unsigned)a.H), 256, 0, stream>>>(a);
     return hipGetLastError();
