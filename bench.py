@@ -45,11 +45,14 @@ WORKLOAD_NAMES = {"m2_2p7b": "mamba2_2.7b_layer_ssd_chunk_scan", "m2_130m": "mam
                   "long_n256": "long_sequence_n256_ssd_chunk_scan"}
 # the sources whose kernels run in one scan launch at this workload
 SCAN_SOURCES = ["pipe_scan.hip", "tile_ops.h", "mfma_scan.hip", "api.hip", "common.h"]
+# and in one backward call
+BWD_SOURCES = ["bwd_scan.hip", "api.hip", "common.h"]
+BWD_KERNELS = ("state_scans", "chunk_grad", "reduce_head")
 
 
-def scan_sources_digest() -> str:
+def scan_sources_digest(files=SCAN_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in SCAN_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "selective_state_space_chunk_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -292,6 +295,18 @@ def scan_traffic():
     return t.get("bytes_per_launch")
 
 
+def bwd_traffic():
+    """HBM bytes per backward call from the same summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("bwd_sources_sha256") != scan_sources_digest(BWD_SOURCES):
+        return None
+    return t.get("bwd_bytes_per_call")
+
+
 def calibrate_copy(mb, steps):
     """Only a plain device-to-device copy of `mb` megabytes, `steps` times."""
     import torch
@@ -360,6 +375,19 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
                                 "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
         total += b
     out["bytes_per_launch"] = total
+    out["bwd_sources_sha256"] = scan_sources_digest(BWD_SOURCES)
+    out["bwd_kernels"] = {}
+    btotal = 0.0
+    for name in BWD_KERNELS:
+        try:
+            fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
+            wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)
+        except SystemExit:
+            continue
+        out["bwd_kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
+                                    "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
+        btotal += fk * f_fetch + wk * f_write
+    out["bwd_bytes_per_call"] = btotal if out["bwd_kernels"] else None
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -461,11 +489,11 @@ def main():
         out["backward"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_backward",
                            "us_per_call": bmean * 1000.0, "us_median": bp[len(bp) // 2] * 1000.0,
                            "tokens_per_s": tokens / (bmean * 1e-3),
-                           "kernels": "state_scan<128> forward and adjoint + chunk_grad<128> + reduce_head",
+                           "kernels": "state_scans<128> (forward and adjoint states) + chunk_grad<128> + reduce_head",
                            "roofline": {"bound": "hbm", "achieved": bb / (bmean * 1e-3) / 1e9,
                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                         "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                        "algorithmic_bytes": bb}}
+                                        "traffic": bwd_traffic(), "algorithmic_bytes": bb}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
