@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import numpy as np
 
@@ -37,7 +37,7 @@ import numpy as np
 # same stream for the same tensor
 _TID = {"x": 1, "dt": 2, "A": 3, "Bm": 4, "Cm": 5, "D": 6, "init": 7,
         "step_x": 11, "step_dt": 12, "step_Bm": 14, "step_Cm": 15,
-        "dy": 21, "dfinal": 22}
+        "dy": 21, "dfinal": 22, "seq": 23}
 
 SEED_BASE = 20240531
 
@@ -199,6 +199,30 @@ def make_grad_inputs(B: int, L: int, H: int, P: int, N: int, *, dtype: str = "bf
     out["dy"] = _store(_rng(seed, "dy").standard_normal((B, L, H, P)), dtype)
     out["dfinal"] = (np.ascontiguousarray(_rng(seed, "dfinal").standard_normal((B, H, P, N)) * 0.1,
                                           dtype=np.float32) if dfinal else None)
+    return out
+
+
+def make_seq_idx(B: int, L: int, *, mean_len: float = 512.0, seed: int = SEED_BASE,
+                 lengths: Optional[Sequence[Sequence[int]]] = None) -> np.ndarray:
+    """Sequence index of every token of packed rows, int32 [B, L]: row b holds
+    documents 0, 1, 2, ... one after another.  With ``lengths`` the documents
+    of row b have those lengths (the last one cut or extended to fill L);
+    otherwise lengths are drawn log-normally with median ``mean_len`` (spread
+    of a factor e), at least 1 token, the last document cut at the row's end."""
+    out = np.zeros((B, L), dtype=np.int32)
+    rng = _rng(seed, "seq")
+    for b in range(B):
+        t, k = 0, 0
+        row_lengths = list(lengths[b]) if lengths is not None else None
+        while t < L:
+            if row_lengths is not None:
+                n = row_lengths[k] if k < len(row_lengths) else L - t
+            else:
+                n = int(max(1, round(float(rng.lognormal(np.log(mean_len), 1.0)))))
+            n = max(1, min(n, L - t))
+            out[b, t:t + n] = k
+            t += n
+            k += 1
     return out
 
 
