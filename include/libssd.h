@@ -151,6 +151,32 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    ssd_algo algo, hipStream_t stream);
 
 /*
+ * Packed rows of independent sequences ("Mamba" reading notes, section 3.5:
+ * boundary resetting, so that sequences concatenated into one row do not leak
+ * into one another).  seq_idx: device int32 [B, L]; token t of row b starts a
+ * new sequence when t > 0 and seq_idx[b][t] != seq_idx[b][t-1].  Each
+ * sequence is scanned as if it stood alone: the first sequence of a row
+ * starts from init_state (or zero), every later one from zero; y is written
+ * for every token and final_state (nullable) is the state after the row's
+ * last token, that of its last sequence.  Other arguments and layouts as
+ * ssd_chunk_scan_fwd; dt must be non-negative (its magnitude is used).
+ * Covered: bfloat16, P = 64, N = 64 or 128 (else SSD_ERR_UNSUPPORTED).
+ * The workspace (size from ssd_chunk_scan_varlen_workspace_size, which is
+ * larger than the plain scan's by B*L*H floats) is owned by the caller;
+ * asynchronous on `stream`; no allocation.
+ */
+size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                            int64_t N, int64_t chunk_size, ssd_dtype dtype);
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float *A,
+                                     const void *Bm, const void *Cm, const float *D,
+                                     const float *init_state, const int32_t *seq_idx, void *y,
+                                     float *final_state, void *workspace, size_t workspace_bytes,
+                                     int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                     int64_t N, int64_t chunk_size, ssd_dtype dtype,
+                                     hipStream_t stream);
+
+/*
  * Diagnostic: waits for `stream`, then checks the hand-off state that
  * SSD_ALGO_FUSED keeps in this workspace: no block-to-block hand-off ever gave
  * up waiting (a bounded wait that is never expected to expire; when it does,

@@ -65,6 +65,10 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_workspace_check.restype = ctypes.c_int
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ssd_step.restype = ctypes.c_int
+    lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_varlen_workspace_size.restype = sz
+    lib.ssd_chunk_scan_fwd_varlen.argtypes = [vp] * 11 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
+    lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
     lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
     lib.ssd_chunk_scan_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
@@ -173,6 +177,51 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
         _ptr(final_state), _ptr(workspace_tensor), ws_bytes, Bsz, L, H, P, G, N, chunk_size, code,
         ALGOS[algo], _stream_handle(dev, stream))
     _check(st, "ssd_chunk_scan_fwd")
+    return y, final_state
+
+
+def ssd_chunk_scan_fwd_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                              Cm: torch.Tensor, D: torch.Tensor, seq_idx: torch.Tensor,
+                              init_state: Optional[torch.Tensor] = None, chunk_size: int = 256, *,
+                              y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                              return_final: bool = True, workspace_tensor: Optional[torch.Tensor] = None,
+                              stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked SSD scan of packed rows: seq_idx [B,L] int32 names the sequence
+    of every token and the state resets where it changes.  Other shapes as
+    ssd_chunk_scan_fwd.  Returns (y, final_state of each row's last sequence)."""
+    lib = load_library()
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    _need(x, "x", x.dtype, (Bsz, L, H, P), dev)
+    _need(dt, "dt", torch.float32, (Bsz, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(Bm, "Bm", x.dtype, (Bsz, L, G, N), dev)
+    _need(Cm, "Cm", x.dtype, (Bsz, L, G, N), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    _need(seq_idx, "seq_idx", torch.int32, (Bsz, L), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (Bsz, H, P, N), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, (Bsz, L, H, P), dev)
+    if final_state is None and return_final:
+        final_state = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (Bsz, H, P, N), dev)
+    code = _dtype_code(x.dtype)
+    need = int(lib.ssd_chunk_scan_varlen_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
+    if workspace_tensor is None:
+        workspace_tensor = workspace(need, dev) if need > 0 else None
+    ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
+    st = lib.ssd_chunk_scan_fwd_varlen(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(seq_idx), _ptr(y),
+        _ptr(final_state), _ptr(workspace_tensor), ws_bytes, Bsz, L, H, P, G, N, chunk_size, code,
+        _stream_handle(dev, stream))
+    _check(st, "ssd_chunk_scan_fwd_varlen")
     return y, final_state
 
 

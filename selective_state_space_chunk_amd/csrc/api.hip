@@ -96,6 +96,20 @@ __global__ void fill_or_copy(float *__restrict__ dst, const float *__restrict__ 
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// dt of packed rows with the reset flag in the sign bit: token t of row b is
+// flagged when t > 0 and seq_idx changes there; every other dt keeps its
+// magnitude with the sign bit clear.  One thread per (b, t, h).
+__global__ void mark_resets(float *out, const float *dt, const int32_t *seq, int64_t L, int64_t H, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t bt = i / H;
+    const bool reset = (bt % L) > 0 && seq[bt] != seq[bt - 1];
+    const uint32_t m = __float_as_uint(dt[i]) & 0x7fffffffu;
+    out[i] = __uint_as_float(reset ? (m | 0x80000000u) : m);
+}
+
+size_t varlen_extra(int64_t B, int64_t L, int64_t H) { return align_up((size_t)(B * L * H) * sizeof(float)); }
+
 ssd_status common_checks(const void *x, const float *dt, const float *A, const void *Bm,
                          const void *Cm, const float *D, const void *y, int64_t B, int64_t L,
                          int64_t H, int64_t P, int64_t G, int64_t N, ssd_dtype dtype,
@@ -230,6 +244,48 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    hipStream_t stream) {
     return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes,
                      B, L, H, P, G, N, chunk_size, dtype, algo, stream);
+}
+
+size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                            int64_t N, int64_t chunk_size, ssd_dtype dtype) {
+    const size_t base = ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype);
+    if (base == 0) return 0;
+    return align_up(base) + varlen_extra(B, L, H);
+}
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float *A, const void *Bm,
+                                     const void *Cm, const float *D, const float *init_state,
+                                     const int32_t *seq_idx, void *y, float *final_state,
+                                     void *workspace, size_t workspace_bytes, int64_t B, int64_t L,
+                                     int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk_size,
+                                     ssd_dtype dtype, hipStream_t stream) {
+    const bool has_work = B > 0 && L > 0;
+    ssd_status st = common_checks(x, dt, A, Bm, Cm, D, y, B, L, H, P, G, N, dtype, has_work);
+    if (st != SSD_OK) return st;
+    if ((init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
+        return SSD_ERR_INVALID_ARG;
+    if (has_work && !seq_idx) return SSD_ERR_INVALID_ARG;
+    if (((uintptr_t)seq_idx & 3u) != 0) return SSD_ERR_INVALID_ARG;
+    if (chunk_size <= 0) return SSD_ERR_INVALID_ARG;
+    if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !mfma_supported(P, N, chunk_size) ||
+        !pipe_supported(H, G, N))
+        return SSD_ERR_UNSUPPORTED;
+    if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
+    if ((L + chunk_size - 1) / chunk_size > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (!has_work)
+        return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes, B, L, H, P, G,
+                         N, chunk_size, dtype, SSD_ALGO_PIPE, stream);
+    const Layout l = layout(B, L, H, P, G, N, chunk_size);
+    const size_t base = align_up(l.total);
+    if (!workspace || workspace_bytes < base + varlen_extra(B, L, H)) return SSD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
+    float *marked = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + base);
+    const int64_t n = B * L * H;
+    mark_resets<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(marked, dt, seq_idx, L, H, n);
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    ScanArgs a{x, marked, A, Bm, Cm, D, init_state, y, final_state, B, L, H, P, G, N, chunk_size, 1, stream, 1};
+    const hipError_t e = launch_pipe_scan(a, carve(workspace, l));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
 size_t ssd_chunk_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,

@@ -66,6 +66,7 @@ struct ScanArgs {
     int64_t B, L, H, P, G, N, Q;
     int bf16;            // 1: x, Bm, Cm, y are bfloat16
     hipStream_t stream;
+    int varlen = 0;      // 1: dt carries reset flags in its sign bit (packed rows)
 };
 
 // Workspace carve-up shared by host code and kernels.

@@ -83,6 +83,22 @@ __device__ __forceinline__ float *seg_log2decay(const Args &a, int e, int q) {
 
 
 
+// Packed rows of several independent sequences: the first token of every
+// sequence after a row's first carries its dt with the sign bit set, so that
+// one load gives both the step and the reset flag.  A reset at token r stops
+// everything before r from reaching r and the tokens after it.
+__device__ __forceinline__ float dt_mag(float v) { return __builtin_fabsf(v); }
+__device__ __forceinline__ uint64_t reset_mask(float v) {
+    return __builtin_amdgcn_ballot_w64((__float_as_uint(v) >> 31) != 0u);
+}
+// bits of tokens 0..k
+__device__ __forceinline__ uint64_t upto(int k) { return (2ull << k) - 1ull; }
+// last reset at or before token k of a sub-block, -1 if none
+__device__ __forceinline__ int last_reset(uint64_t m, int k) {
+    const uint64_t r = m & upto(k);
+    return r ? 63 - (int)__builtin_clzll(r) : -1;
+}
+
 __device__ __forceinline__ int sub_tokens(const Args &a, int sb) {
     const int64_t rem = a.L - (int64_t)sb * kSub;
     return rem < kSub ? (int)rem : kSub;
@@ -158,7 +174,7 @@ __device__ __forceinline__ void settle(f32x4 (&H)[NT]) {
     for (int u = 0; u < NT; ++u) asm volatile("" ::"v"(H[u]));
 }
 
-template <int N>
+template <int N, bool kV>
 __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PipeSmem<N> &sm = *reinterpret_cast<PipeSmem<N> *>(smem_raw);
@@ -309,12 +325,24 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             const unsigned char *Mr = reinterpret_cast<const unsigned char *>(sm.Mm[par]);
             const float Ah2 = t >= nown ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
-            const float dt = sm.dts[t & 3][lane];
+            const float dtr = sm.dts[t & 3][lane];
+            const float dt = kV ? dt_mag(dtr) : dtr;
             const float v = wave_scan(dt * Ah2);
             const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-            wd.w[lane] = ex2(lend - v) * dt;
-            wd.rdec[lane] = ex2(v);
-            const float gam = ex2(lend);
+            float wv = ex2(lend - v) * dt, rdv = ex2(v), gam = ex2(lend);
+            if constexpr (kV) {
+                // tokens before the last reset do not reach the end of the
+                // sub-block; the entering state reaches only the tokens
+                // before the first reset
+                const uint64_t rm = reset_mask(dtr);
+                if (rm) {
+                    if (lane < 63 - (int)__builtin_clzll(rm)) wv = 0.f;
+                    if (rm & upto(lane)) rdv = 0.f;
+                    gam = 0.f;
+                }
+            }
+            wd.w[lane] = wv;
+            wd.rdec[lane] = rdv;
             // this wave's dt quarter of step t+2 into LDS, that of t+4 into
             // its register
             {
@@ -472,7 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             const float Ah2 = xs ? Ahx2 : Ah2v;
             const float Dh = xs ? Dhx : Dhv;
             const float *dtrow = sm.dts[tau & 3];
-            wd.lam[lane] = wave_scan(dtrow[lane] * Ah2);
+            const float dself = dtrow[lane];
+            uint64_t rm = 0;
+            if constexpr (kV) rm = reset_mask(dself);
+            wd.lam[lane] = wave_scan((kV ? dt_mag(dself) : dself) * Ah2);
             uint2 mt[3];
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
@@ -484,13 +515,15 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 const f32x4 lj = *reinterpret_cast<const f32x4 *>(&wd.lam[j0]);
                 const f32x4 dj = *reinterpret_cast<const f32x4 *>(&dtrow[j0]);
                 const uint32_t gw[2] = {gt[m].x, gt[m].y};
+                // token j reaches token i when j <= i and no reset lies in (j, i]
+                const int rho = kV ? last_reset(rm, i) : -1;
                 float mv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float gv = (e & 1) ? hi_bf16(gw[e >> 1]) : lo_bf16(gw[e >> 1]);
-                    const float d = j0 + e <= i ? li - lj[e] : -__builtin_inff();
+                    const float d = (j0 + e <= i && j0 + e >= rho) ? li - lj[e] : -__builtin_inff();
                     // the skip term D x_i rides on the diagonal
-                    mv[e] = __builtin_fmaf(gv * ex2(d), dj[e], j0 + e == i ? Dh : 0.f);
+                    mv[e] = __builtin_fmaf(gv * ex2(d), kV ? dt_mag(dj[e]) : dj[e], j0 + e == i ? Dh : 0.f);
                 }
                 mt[m] = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
             }
@@ -580,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
 // s - 2) until it is staged to LDS slot s % 2 at the end of step s - 1.  A
 // pair that runs past the segment's end gets dt = 0 for its missing
 // sub-block: weight 0, decay 1.
-template <int N>
+template <int N, bool kV>
 __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     __shared__ __align__(16) __bf16 lds_x[2][2][kSub * kP];
     __shared__ __align__(16) __bf16 lds_bt[2][2][kSub * N];
@@ -643,15 +676,31 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     };
     // wave 0: weights and log2 decay of the pair of step st into ring slot st % 3
     auto weights = [&](int st, int slot) __attribute__((always_inline)) {
-        const float dta = dts[slot][0];
-        const float dtb = 2 * st + 1 < len ? dts[slot][1] : 0.f;
+        const float dra = dts[slot][0];
+        const float drb = 2 * st + 1 < len ? dts[slot][1] : 0.f;
+        const float dta = kV ? dt_mag(dra) : dra, dtb = kV ? dt_mag(drb) : drb;
         const float va = wave_scan(dta * Ah2), vb = wave_scan(dtb * Ah2);
         const float la = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), 63));
         const float lb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), 63));
         const int r = st % 3;
-        lds_w[r][0][lane] = ex2(la + lb - va) * dta;
-        lds_w[r][1][lane] = ex2(lb - vb) * dtb;
-        if (lane == 0) lds_l[r] = la + lb;
+        float wa = ex2(la + lb - va) * dta, wb = ex2(lb - vb) * dtb, lp = la + lb;
+        if constexpr (kV) {
+            // a reset in the pair: nothing before it reaches the pair's end,
+            // and the pair's decay is zero (log2 -inf)
+            const uint64_t ma = reset_mask(dra), mb = reset_mask(drb);
+            if (mb) {
+                if (lane < 63 - (int)__builtin_clzll(mb)) wb = 0.f;
+                wa = 0.f;
+                lp = -__builtin_inff();
+            }
+            if (ma) {
+                if (lane < 63 - (int)__builtin_clzll(ma)) wa = 0.f;
+                lp = -__builtin_inff();
+            }
+        }
+        lds_w[r][0][lane] = wa;
+        lds_w[r][1][lane] = wb;
+        if (lane == 0) lds_l[r] = lp;
     };
     // x of the pair of step st (register slot `slot`) times its weights, and
     // Bm, into LDS slot `slot`
@@ -767,10 +816,10 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
 // The work that must precede pipe_kernel when there are segments, in one
 // launch so that the two parts share the device: workgroups below nsegwg
 // compute segment states, the others one sub-block's gram tiles each.
-template <int N>
+template <int N, bool kV>
 __global__ __launch_bounds__(512) void prep_kernel(Args a, int nsegwg) {
     if ((int)blockIdx.x < nsegwg) {
-        seg_state_block<N>(a, blockIdx.x);
+        seg_state_block<N, kV>(a, blockIdx.x);
     } else {
         const int64_t k = (int64_t)blockIdx.x - nsegwg;
         gram_block<N, 8>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb,
@@ -791,7 +840,7 @@ int device_cus() {
     return cached[dev];
 }
 
-template <int N>
+template <int N, bool kV>
 hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int64_t nsb = (sa.L + kSub - 1) / kSub;
     hipError_t e = hipSuccess;
@@ -826,7 +875,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     }
     const int nwg = nmain > 0 ? nmain : nextra * nseg;
     const size_t smem = sizeof(PipeSmem<N>);
-    auto kern = pipe_kernel<N>;
+    auto kern = pipe_kernel<N, kV>;
     static bool configured = false;
     if (!configured) {
         e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -838,7 +887,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
            sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
     if (nextra > 0 && nseg > 1) {
         const int nsegwg = nextra * (nseg - 1);
-        prep_kernel<N><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 512, 0, sa.stream>>>(a, nsegwg);
+        prep_kernel<N, kV><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 512, 0, sa.stream>>>(a, nsegwg);
     } else {
         e = launch_gram(sa, ws, nsb);
     }
@@ -859,8 +908,8 @@ bool pipe_supported(int64_t H, int64_t G, int64_t N) {
 
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws) {
     switch (a.N) {
-        case 64: return launch<64>(a, ws);
-        case 128: return launch<128>(a, ws);
+        case 64: return a.varlen ? launch<64, true>(a, ws) : launch<64, false>(a, ws);
+        case 128: return a.varlen ? launch<128, true>(a, ws) : launch<128, false>(a, ws);
         default: return hipErrorInvalidValue;
     }
 }
