@@ -216,6 +216,45 @@ def time_backward(w, steps, warmup, device):
     return sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
 
 
+VARLEN_MEAN_LEN = 512.0
+
+
+def time_varlen(w, steps, warmup, device):
+    """Per-call event times (ms) of ssd_chunk_scan_fwd_varlen over rotating
+    input sets, each row packed with documents of log-normal length (median
+    512 tokens, the last one cut at the row's end)."""
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    import ssd_inputs as si
+    sets = make_device_sets(w, 3, device)
+    nseq = []
+    for k, s in enumerate(sets):
+        seq = si.make_seq_idx(w.B, w.L, mean_len=VARLEN_MEAN_LEN, seed=w.seed + 100 * k + 9)
+        nseq.append(int(sum(seq[b, -1] + 1 for b in range(w.B))))
+        s["seq"] = torch.from_numpy(seq).to(device)
+        s["yv"] = torch.empty_like(s["x"])
+        s["fv"] = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device=device)
+    nbytes = ssd.ssd_chunk_scan_varlen_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def run(k):
+        s = sets[k % len(sets)]
+        ssd.ssd_chunk_scan_fwd_varlen(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], s["D"], s["seq"], s["init"],
+                                      w.chunk, y=s["yv"], final_state=s["fv"], workspace_tensor=ws)
+
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize(device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        starts[k].record()
+        run(k)
+        ends[k].record()
+    torch.cuda.synchronize(device)
+    return sorted(s.elapsed_time(e) for s, e in zip(starts, ends)), nseq
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle (token-by-token recurrence, OpenMP over (batch, head)
     sequences) on a bounded sample of the same workload: whole sequences of
@@ -402,6 +441,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -494,6 +534,19 @@ def main():
                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                         "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                         "traffic": bwd_traffic(), "algorithmic_bytes": bb}}
+    if not args.no_varlen and headline:
+        vp, nseq = time_varlen(w, max(10, args.steps // 2), 3, device)
+        vmean = sum(vp) / len(vp)
+        vb = scan_algorithmic(w)[0] + w.B * w.L * 4      # + seq_idx
+        out["varlen"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_packed_documents",
+                         "documents_per_call": nseq, "median_document_tokens": VARLEN_MEAN_LEN,
+                         "us_per_call": vmean * 1000.0, "us_median": vp[len(vp) // 2] * 1000.0,
+                         "tokens_per_s": tokens / (vmean * 1e-3),
+                         "kernels": "mark_resets + prep_kernel<128, true> + pipe_kernel<128, true>",
+                         "roofline": {"bound": "hbm", "achieved": vb / (vmean * 1e-3) / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": vb / (vmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "algorithmic_bytes": vb}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -10,8 +10,13 @@ Entry points (same names as the C ABI):
 
 * ``ssd_chunk_scan_fwd(x, dt, A, Bm, Cm, D, init_state=None, chunk_size=256)``
   -> ``(y, final_state)``
+* ``ssd_chunk_scan_fwd_varlen(x, dt, A, Bm, Cm, D, seq_idx, init_state=None, chunk_size=256)``
+  -> ``(y, final_state)``: packed rows, the state reset wherever seq_idx changes
+* ``ssd_chunk_scan_bwd(x, dt, A, Bm, Cm, D, init_state, dy, dfinal=None, chunk_size=256)``
+  -> dict of gradients dx, ddt, dA, dBm, dCm, dD, dinit
 * ``ssd_step(state, x, dt, A, Bm, Cm, D)`` -> ``y`` (``state`` updated in place)
-* ``ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype)``
+* ``ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype)`` and the
+  ``_varlen_`` and ``_bwd_`` variants
 """
 from __future__ import annotations
 
@@ -260,6 +265,12 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Te
                       Bsz, H, P, G, N, _dtype_code(x.dtype), _stream_handle(dev, stream))
     _check(st, "ssd_step")
     return y
+
+
+def ssd_chunk_scan_varlen_workspace_size(B: int, L: int, H: int, P: int, G: int, N: int,
+                                         chunk_size: int, dtype: torch.dtype) -> int:
+    return int(load_library().ssd_chunk_scan_varlen_workspace_size(B, L, H, P, G, N, chunk_size,
+                                                                   _dtype_code(dtype)))
 
 
 def ssd_chunk_scan_bwd_workspace_size(B: int, L: int, H: int, P: int, G: int, N: int,

@@ -98,14 +98,18 @@ __global__ void fill_or_copy(float *__restrict__ dst, const float *__restrict__ 
 
 // dt of packed rows with the reset flag in the sign bit: token t of row b is
 // flagged when t > 0 and seq_idx changes there; every other dt keeps its
-// magnitude with the sign bit clear.  One thread per (b, t, h).
-__global__ void mark_resets(float *out, const float *dt, const int32_t *seq, int64_t L, int64_t H, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t bt = i / H;
+// magnitude with the sign bit clear.  One wave per token (b, t) of the B*L,
+// its lanes over the H heads.
+__global__ __launch_bounds__(256) void mark_resets(float *out, const float *dt, const int32_t *seq, int64_t L,
+                                                   int64_t H, int64_t ntok) {
+    const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bt >= ntok) return;
     const bool reset = (bt % L) > 0 && seq[bt] != seq[bt - 1];
-    const uint32_t m = __float_as_uint(dt[i]) & 0x7fffffffu;
-    out[i] = __uint_as_float(reset ? (m | 0x80000000u) : m);
+    const uint32_t flag = reset ? 0x80000000u : 0u;
+    const float *src = dt + bt * H;
+    float *dst = out + bt * H;
+    for (int64_t h = threadIdx.x & 63; h < H; h += 64)
+        dst[h] = __uint_as_float((__float_as_uint(src[h]) & 0x7fffffffu) | flag);
 }
 
 size_t varlen_extra(int64_t B, int64_t L, int64_t H) { return align_up((size_t)(B * L * H) * sizeof(float)); }
@@ -280,8 +284,9 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
     if (!workspace || workspace_bytes < base + varlen_extra(B, L, H)) return SSD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
     float *marked = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + base);
-    const int64_t n = B * L * H;
-    mark_resets<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(marked, dt, seq_idx, L, H, n);
+    const int64_t ntok = B * L;
+    if ((ntok + 3) / 4 > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    mark_resets<<<(unsigned)((ntok + 3) / 4), 256, 0, stream>>>(marked, dt, seq_idx, L, H, ntok);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     ScanArgs a{x, marked, A, Bm, Cm, D, init_state, y, final_state, B, L, H, P, G, N, chunk_size, 1, stream, 1};
     const hipError_t e = launch_pipe_scan(a, carve(workspace, l));
