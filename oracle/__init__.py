@@ -16,6 +16,8 @@ Forms:
   differences of ``recurrence``, exact adjointness and closed forms.
 * ``recurrence_varlen`` -- packed rows of independent sequences (``seq_idx``),
   each run of equal values scanned on its own (``varlen.py``).
+* ``block_prologue`` / ``gated_norm`` -- the steps before and after the scan
+  in a Mamba-2 block (``block.py``).
 
 Every function takes float64 arrays (the values the GPU receives, widened
 exactly) and returns float64 arrays.
@@ -32,6 +34,7 @@ import numpy as np
 from .forms import chunked, decay_mask, quadratic  # noqa: F401
 from .backward import recurrence_bwd  # noqa: F401
 from .varlen import recurrence_varlen, run_bounds  # noqa: F401
+from .block import block_prologue, gated_norm  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
