@@ -177,6 +177,42 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
                                      hipStream_t stream);
 
 /*
+ * The step before the scan in a Mamba-2 block ("Mamba-2" note, section
+ * "Mamba-2 block": one parallel projection yields z, X, B, C and dt).
+ * zxbcdt: bfloat16 [B, L, 2HP + 2GN + H], each token's row laid out
+ * [z (HP) | x (HP) | Bm (GN) | Cm (GN) | dt_raw (H)].  The C = HP + 2GN
+ * middle channels go through a causal depthwise convolution of width W
+ * (conv_w fp32 [C, W], tap W-1 on the current token, zero input before
+ * token 0; conv_b fp32 [C] or NULL) and SiLU, and are written to x
+ * [B, L, H, P], Bm and Cm [B, L, G, N] (bfloat16); dt fp32 [B, L, H] =
+ * softplus(dt_raw + dt_bias) (dt_bias fp32 [H] or NULL).  z stays in place
+ * for ssd_gated_norm.  Covered: bfloat16, 1 <= W <= 4, HP, GN and the row
+ * length multiples of 8 (else SSD_ERR_UNSUPPORTED).  Device pointers,
+ * caller-owned, 16-byte aligned for the bfloat16 arrays; asynchronous.
+ */
+ssd_status ssd_block_prologue(const void *zxbcdt, const float *conv_w, const float *conv_b,
+                              const float *dt_bias, void *x, void *Bm, void *Cm, float *dt,
+                              int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                              int64_t W, ssd_dtype dtype, hipStream_t stream);
+
+/*
+ * The step after the scan: the gate and the normalisation ("Mamba-2" note,
+ * section "Mamba-2 block"; a GroupNorm per the "Mamba-2" walkthrough,
+ * section 7.2).  For each of T tokens: v = y * SiLU(z) over its D channels;
+ * each of `ngroups` equal groups of channels is normalised (center = 1: minus
+ * its mean, over the root of its variance + eps; center = 0: over the root of
+ * its mean square + eps); out = that * weight (+ bias).  y, out bfloat16
+ * [T, D]; z bfloat16 with row stride z_stride elements (D for a [T, D] tensor,
+ * or the projection row length to read z straight out of zxbcdt); weight,
+ * bias fp32 [D] (bias may be NULL).  Covered: bfloat16, D a multiple of 8 up
+ * to 8192, 1 <= ngroups <= 8 with D / ngroups a multiple of 8, z_stride a
+ * multiple of 8 (else SSD_ERR_UNSUPPORTED).  Deterministic; asynchronous.
+ */
+ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const float *weight,
+                          const float *bias, void *out, int64_t T, int64_t D, int64_t ngroups,
+                          float eps, int center, ssd_dtype dtype, hipStream_t stream);
+
+/*
  * Diagnostic: waits for `stream`, then checks the hand-off state that
  * SSD_ALGO_FUSED keeps in this workspace: no block-to-block hand-off ever gave
  * up waiting (a bounded wait that is never expected to expire; when it does,

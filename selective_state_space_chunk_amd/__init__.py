@@ -74,6 +74,11 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_varlen_workspace_size.restype = sz
     lib.ssd_chunk_scan_fwd_varlen.argtypes = [vp] * 11 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
     lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
+    lib.ssd_block_prologue.argtypes = [vp] * 8 + [i64] * 7 + [ctypes.c_int, vp]
+    lib.ssd_block_prologue.restype = ctypes.c_int
+    lib.ssd_gated_norm.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                   ctypes.c_int, vp]
+    lib.ssd_gated_norm.restype = ctypes.c_int
     lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
     lib.ssd_chunk_scan_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
@@ -228,6 +233,71 @@ def ssd_chunk_scan_fwd_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor
         _stream_handle(dev, stream))
     _check(st, "ssd_chunk_scan_fwd_varlen")
     return y, final_state
+
+
+def ssd_block_prologue(zxbcdt: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[torch.Tensor],
+                       dt_bias: Optional[torch.Tensor], H: int, P: int, G: int, N: int, *,
+                       stream=None) -> Dict[str, torch.Tensor]:
+    """Split of the block's projection output zxbcdt [B, L, 2HP + 2GN + H]
+    (bfloat16), causal depthwise convolution (conv_w [HP + 2GN, W] f32,
+    conv_b [HP + 2GN] f32 or None) + SiLU into x [B,L,H,P], Bm, Cm [B,L,G,N],
+    and dt = softplus(dt_raw + dt_bias) [B,L,H] f32.  Returns a dict with
+    those and z, a view of zxbcdt (no copy)."""
+    lib = load_library()
+    if zxbcdt.dim() != 3:
+        raise ValueError("zxbcdt must be [B, L, 2HP + 2GN + H]")
+    Bsz, L, row = zxbcdt.shape
+    HP, GN = H * P, G * N
+    dev = zxbcdt.device
+    _need(zxbcdt, "zxbcdt", torch.bfloat16, (Bsz, L, 2 * HP + 2 * GN + H), dev)
+    W = conv_w.shape[1] if conv_w.dim() == 2 else -1
+    _need(conv_w, "conv_w", torch.float32, (HP + 2 * GN, W), dev)
+    if conv_b is not None:
+        _need(conv_b, "conv_b", torch.float32, (HP + 2 * GN,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    out = {"x": torch.empty((Bsz, L, H, P), dtype=torch.bfloat16, device=dev),
+           "Bm": torch.empty((Bsz, L, G, N), dtype=torch.bfloat16, device=dev),
+           "Cm": torch.empty((Bsz, L, G, N), dtype=torch.bfloat16, device=dev),
+           "dt": torch.empty((Bsz, L, H), dtype=torch.float32, device=dev)}
+    st = lib.ssd_block_prologue(_ptr(zxbcdt), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(out["x"]),
+                                _ptr(out["Bm"]), _ptr(out["Cm"]), _ptr(out["dt"]), Bsz, L, H, P, G, N, W,
+                                SSD_DTYPE_BF16, _stream_handle(dev, stream))
+    _check(st, "ssd_block_prologue")
+    out["z"] = zxbcdt[:, :, :HP]
+    return out
+
+
+def ssd_gated_norm(y: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                   ngroups: int = 1, eps: float = 1e-5, center: bool = True, *,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gate and group norm of T tokens of D channels: z [..., D] (bfloat16,
+    last dimension contiguous; rows may be strided, e.g. the z slice of the
+    projection output) and y holding T*D values contiguously (e.g. the scan's
+    [B, L, H, P] output for D = H*P).  Returns out shaped like y."""
+    lib = load_library()
+    D = z.shape[-1]
+    T = z.numel() // D if D else 0
+    dev = y.device
+    if y.dtype != torch.bfloat16 or z.dtype != torch.bfloat16:
+        raise TypeError("y and z must be bfloat16")
+    if not y.is_contiguous() or y.numel() != T * D:
+        raise ValueError("y must be contiguous and hold as many values as z")
+    z2 = z.reshape(T, D) if z.dim() != 2 else z
+    if z2.stride(1) != 1:
+        raise ValueError("z must have a contiguous last dimension")
+    zstride = z2.stride(0) if T > 1 else D
+    if z.dim() == 3 and T > 1 and z.stride(0) != z.shape[1] * z.stride(1):
+        raise ValueError("z rows must be evenly strided")
+    _need(weight, "weight", torch.float32, (D,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (D,), dev)
+    if out is None:
+        out = torch.empty_like(y)
+    st = lib.ssd_gated_norm(_ptr(y), _ptr(z2), zstride, _ptr(weight), _ptr(bias), _ptr(out), T, D, ngroups,
+                            float(eps), 1 if center else 0, SSD_DTYPE_BF16, _stream_handle(dev, stream))
+    _check(st, "ssd_gated_norm")
+    return out
 
 
 def ssd_chunk_scan_workspace_check(workspace_tensor: torch.Tensor, B: int, L: int, H: int, P: int,

@@ -16,6 +16,14 @@ bool fused_supported(int64_t H, int64_t G, int64_t N, int64_t Q);
 hipError_t launch_chain_scan(const ScanArgs &a, const Workspace &ws);
 bool chain_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
+bool block_prologue_supported(int64_t HP, int64_t GN, int64_t H, int64_t W);
+hipError_t launch_block_prologue(const void *zx, const float *conv_w, const float *conv_b, const float *dt_bias,
+                                 void *x, void *Bm, void *Cm, float *dt, int64_t B, int64_t L, int64_t H,
+                                 int64_t HP, int64_t GN, int64_t W, hipStream_t stream);
+bool gated_norm_supported(int64_t D, int64_t ngroups, int64_t zstride);
+hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, const float *w, const float *bias,
+                             void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
+                             hipStream_t stream);
 bool pipe_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pair_scan(const ScanArgs &a, const Workspace &ws);
 bool pair_supported(int64_t H, int64_t G, int64_t N);
@@ -290,6 +298,39 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     ScanArgs a{x, marked, A, Bm, Cm, D, init_state, y, final_state, B, L, H, P, G, N, chunk_size, 1, stream, 1};
     const hipError_t e = launch_pipe_scan(a, carve(workspace, l));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_block_prologue(const void *zxbcdt, const float *conv_w, const float *conv_b,
+                              const float *dt_bias, void *x, void *Bm, void *Cm, float *dt, int64_t B,
+                              int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t W,
+                              ssd_dtype dtype, hipStream_t stream) {
+    if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || W <= 0) return SSD_ERR_INVALID_ARG;
+    if (H % G != 0) return SSD_ERR_INVALID_ARG;
+    if (dtype != SSD_DTYPE_BF16 || !block_prologue_supported(H * P, G * N, H, W)) return SSD_ERR_UNSUPPORTED;
+    if (B == 0 || L == 0) return SSD_OK;
+    if (!zxbcdt || !conv_w || !x || !Bm || !Cm || !dt) return SSD_ERR_INVALID_ARG;
+    const void *ptrs[] = {zxbcdt, x, Bm, Cm};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
+    if ((L + 63) / 64 > 65535 || B > 65535) return SSD_ERR_UNSUPPORTED;
+    const hipError_t e = launch_block_prologue(zxbcdt, conv_w, conv_b, dt_bias, x, Bm, Cm, dt, B, L, H, H * P,
+                                               G * N, W, stream);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const float *weight, const float *bias,
+                          void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
+                          ssd_dtype dtype, hipStream_t stream) {
+    if (T < 0 || D <= 0 || ngroups <= 0 || !(eps >= 0.f)) return SSD_ERR_INVALID_ARG;
+    if (dtype != SSD_DTYPE_BF16 || !gated_norm_supported(D, ngroups, z_stride)) return SSD_ERR_UNSUPPORTED;
+    if (T == 0) return SSD_OK;
+    if (!y || !z || !weight || !out) return SSD_ERR_INVALID_ARG;
+    const void *ptrs[] = {y, z, out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
+    if (T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    const hipError_t e = launch_gated_norm(y, z, z_stride, weight, bias, out, T, D, ngroups, eps, center, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -1,0 +1,278 @@
+// The steps on either side of the scan in a Mamba-2 block (the "Mamba-2"
+// note, section "Mamba-2 block": one parallel projection gives the gate input
+// z, X, B, C and the step dt; the scan output is gated and normalised before
+// the output projection, a GroupNorm per the "Mamba-2" walkthrough, section
+// 7.2).  Both kernels stream HBM once: every value is read once and every
+// output written once, 16 bytes per lane, with the work of a token or a tile
+// of tokens kept in registers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+namespace {
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x8 ld_bf16x8(const __bf16 *p) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    f32x8 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+    return v;
+}
+__device__ __forceinline__ void st_bf16x8(__bf16 *p, const f32x8 &v) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    bf16x8_t o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)v[e];
+    *reinterpret_cast<bf16x8_t *>(p) = o;
+}
+__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+__device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
+
+// ---------------------------------------------------------------------------
+// Prologue.  Projection row of a token: [z (HP) | x (HP) | Bm (GN) | Cm (GN) |
+// dt (H)], bfloat16.  The C = HP + 2GN middle channels go through a causal
+// depthwise convolution of width W (taps conv_w[c][k], tap W-1 on the
+// current token, zero before token 0) plus bias and SiLU, into x, Bm, Cm;
+// dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 64 tokens of row b
+// from token 64 ty; lane k of channel tile cx takes channels 8(256 cx + k) ..
+// +7 for all 64 tokens, keeping the last W-1 inputs in registers.  The last
+// channel tile computes dt of the 64 tokens instead.
+struct ProArgs {
+    const __bf16 *zx;
+    const float *conv_w, *conv_b, *dt_bias;
+    __bf16 *x, *Bm, *Cm;
+    float *dt;
+    int64_t L, HP, GN, H, row;
+    int ctiles;
+};
+
+constexpr int kTok = 64;
+
+template <int W>
+__global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
+    const int64_t b = blockIdx.z;
+    const int64_t t0 = (int64_t)blockIdx.y * kTok;
+    const int nt = (int)(a.L - t0 < kTok ? a.L - t0 : kTok);
+    const __bf16 *rows = a.zx + (b * a.L) * a.row;
+    if ((int)blockIdx.x == a.ctiles) {
+        const int H = (int)a.H;
+        const int64_t off = 2 * a.HP + 2 * a.GN;
+        for (int i = threadIdx.x; i < nt * H; i += 256) {
+            const int tt = i / H, h = i - tt * H;
+            const float v = (float)rows[(t0 + tt) * a.row + off + h] + (a.dt_bias ? a.dt_bias[h] : 0.f);
+            a.dt[(b * a.L + t0 + tt) * a.H + h] = softplus(v);
+        }
+        return;
+    }
+    const int64_t C = a.HP + 2 * a.GN;
+    const int64_t c = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (c >= C) return;
+    float wk[W][8], bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bias[e] = a.conv_b ? a.conv_b[c + e] : 0.f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) wk[k][e] = a.conv_w[(c + e) * W + k];
+    }
+    const __bf16 *src = rows + a.HP + c;
+    // destination of these channels
+    __bf16 *dst;
+    int64_t dstride;
+    if (c < a.HP) {
+        dst = a.x + b * a.L * a.HP + c;
+        dstride = a.HP;
+    } else if (c < a.HP + a.GN) {
+        dst = a.Bm + b * a.L * a.GN + (c - a.HP);
+        dstride = a.GN;
+    } else {
+        dst = a.Cm + b * a.L * a.GN + (c - a.HP - a.GN);
+        dstride = a.GN;
+    }
+    f32x8 hist[W > 1 ? W - 1 : 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int64_t t = t0 - (W - 1) + j;
+        hist[j] = t >= 0 ? ld_bf16x8(src + t * a.row) : f32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // four tokens per round: their loads go out together
+    for (int tt = 0; tt < nt; tt += 4) {
+        f32x8 cur[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = tt + u < nt ? tt + u : nt - 1;
+            cur[u] = ld_bf16x8(src + (t0 + t) * a.row);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f32x8 acc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float s = bias[e];
+#pragma unroll
+                for (int k = 0; k < W - 1; ++k) s = __builtin_fmaf(wk[k][e], hist[k][e], s);
+                acc[e] = silu(__builtin_fmaf(wk[W - 1][e], cur[u][e], s));
+            }
+            if (tt + u < nt) st_bf16x8(dst + (t0 + tt + u) * dstride, acc);
+#pragma unroll
+            for (int j = 0; j + 1 < W - 1; ++j) hist[j] = hist[j + 1];
+            if constexpr (W > 1) hist[W - 2] = cur[u];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gated norm.  One workgroup per token: v = y * SiLU(z) over its D channels,
+// normalised within each of ngroups equal groups (mean-centred with variance,
+// or root mean square only), times weight, plus bias.  Thread k holds
+// channel chunks k, k + 256, ... (8 channels each, at most 4 chunks) in
+// registers; group sums go through per-wave partials in LDS in a fixed
+// order, so results are deterministic.
+struct NormArgs {
+    const __bf16 *y, *z;
+    const float *w, *bias;
+    __bf16 *out;
+    int64_t D, zstride;
+    int ngroups, center;
+    float eps;
+};
+
+constexpr int kMaxGroups = 8;
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// sum over the workgroup of part[k] for the chunks of group g, for every g;
+// result for group g in tot[g]
+__device__ __forceinline__ void group_sums(const float (&part)[4], const int (&grp)[4], int ngroups,
+                                           float (*red)[kMaxGroups], float (&tot)[kMaxGroups]) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // (loops to the constant bound, so that tot stays in registers)
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+        if (g < ngroups) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s += grp[k] == g ? part[k] : 0.f;
+            s = wave_sum64(s);
+            if (lane == 0) red[wave][g] = s;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g)
+        tot[g] = g < ngroups ? (red[0][g] + red[1][g]) + (red[2][g] + red[3][g]) : 0.f;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a) {
+    __shared__ float red[4][kMaxGroups];
+    const int64_t t = blockIdx.x;
+    const int nch = (int)(a.D / 8), gch = nch / a.ngroups;
+    const float inv = 1.f / (float)(a.D / a.ngroups);
+    f32x8 v[4];
+    int grp[4];
+    float part[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int ch = threadIdx.x + 256 * k;
+        grp[k] = ch < nch ? ch / gch : -1;
+        part[k] = 0.f;
+        if (ch < nch) {
+            const f32x8 yv = ld_bf16x8(a.y + t * a.D + 8 * ch);
+            const f32x8 zv = ld_bf16x8(a.z + t * a.zstride + 8 * ch);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[k][e] = yv[e] * silu(zv[e]);
+                part[k] += v[k][e];
+            }
+        }
+    }
+    float mean[kMaxGroups], tot[kMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) mean[g] = 0.f;
+    if (a.center) {
+        group_sums(part, grp, a.ngroups, red, tot);
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g) mean[g] = tot[g] * inv;
+    }
+    // second pass over the registers: squares about the mean
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        part[k] = 0.f;
+        if (grp[k] >= 0) {
+            float m = 0.f;
+#pragma unroll
+            for (int g = 0; g < kMaxGroups; ++g) m = g == grp[k] ? mean[g] : m;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[k][e] -= m;
+                part[k] = __builtin_fmaf(v[k][e], v[k][e], part[k]);
+            }
+        }
+    }
+    group_sums(part, grp, a.ngroups, red, tot);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (grp[k] < 0) continue;
+        float ms = 0.f;
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g) ms = g == grp[k] ? tot[g] : ms;
+        const float r = __builtin_amdgcn_rsqf(ms * inv + a.eps);
+        const int64_t c0 = 8 * (int64_t)(threadIdx.x + 256 * k);
+        f32x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[k][e] * r * a.w[c0 + e] + (a.bias ? a.bias[c0 + e] : 0.f);
+        st_bf16x8(a.out + t * a.D + c0, o);
+    }
+}
+
+}  // namespace
+
+bool block_prologue_supported(int64_t HP, int64_t GN, int64_t H, int64_t W) {
+    const int64_t row = 2 * HP + 2 * GN + H;
+    return HP % 8 == 0 && GN % 8 == 0 && row % 8 == 0 && W >= 1 && W <= 4;
+}
+
+hipError_t launch_block_prologue(const void *zx, const float *conv_w, const float *conv_b, const float *dt_bias,
+                                 void *x, void *Bm, void *Cm, float *dt, int64_t B, int64_t L, int64_t H,
+                                 int64_t HP, int64_t GN, int64_t W, hipStream_t stream) {
+    const int64_t C = HP + 2 * GN;
+    const int ctiles = (int)((C / 8 + 255) / 256);
+    ProArgs a{(const __bf16 *)zx, conv_w, conv_b, dt_bias, (__bf16 *)x, (__bf16 *)Bm, (__bf16 *)Cm, dt,
+              L, HP, GN, H, 2 * HP + 2 * GN + H, ctiles};
+    const dim3 grid((unsigned)(ctiles + 1), (unsigned)((L + kTok - 1) / kTok), (unsigned)B);
+    switch (W) {
+        case 1: prologue_kernel<1><<<grid, 256, 0, stream>>>(a); break;
+        case 2: prologue_kernel<2><<<grid, 256, 0, stream>>>(a); break;
+        case 3: prologue_kernel<3><<<grid, 256, 0, stream>>>(a); break;
+        case 4: prologue_kernel<4><<<grid, 256, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+bool gated_norm_supported(int64_t D, int64_t ngroups, int64_t zstride) {
+    return D % 8 == 0 && D / 8 <= 4 * 256 && ngroups >= 1 && ngroups <= kMaxGroups && D % ngroups == 0 &&
+           (D / ngroups) % 8 == 0 && zstride >= D && zstride % 8 == 0;
+}
+
+hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, const float *w, const float *bias,
+                             void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
+                             hipStream_t stream) {
+    NormArgs a{(const __bf16 *)y, (const __bf16 *)z, w, bias, (__bf16 *)out, D, zstride, (int)ngroups,
+               center ? 1 : 0, eps};
+    gated_norm_kernel<<<dim3((unsigned)T), 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

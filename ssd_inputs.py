@@ -37,7 +37,7 @@ import numpy as np
 # same stream for the same tensor
 _TID = {"x": 1, "dt": 2, "A": 3, "Bm": 4, "Cm": 5, "D": 6, "init": 7,
         "step_x": 11, "step_dt": 12, "step_Bm": 14, "step_Cm": 15,
-        "dy": 21, "dfinal": 22, "seq": 23}
+        "dy": 21, "dfinal": 22, "seq": 23, "zxbcdt": 24, "conv_w": 25, "conv_b": 26, "dt_bias": 27, "norm_w": 28, "norm_b": 29, "ynorm": 30}
 
 SEED_BASE = 20240531
 
@@ -224,6 +224,28 @@ def make_seq_idx(B: int, L: int, *, mean_len: float = 512.0, seed: int = SEED_BA
             t += n
             k += 1
     return out
+
+
+def make_block_inputs(B: int, L: int, H: int, P: int, G: int, N: int, W: int = 4, *,
+                      seed: int = SEED_BASE) -> Dict[str, np.ndarray]:
+    """Seeded inputs of the steps around the scan in a Mamba-2 block: the
+    projection output zxbcdt [B, L, 2HP + 2GN + H] ~ N(0, 1) in bfloat16,
+    conv taps [HP + 2GN, W] ~ N(0, 1/W) and bias ~ N(0, 0.1) (fp32), dt_bias
+    [H] so that softplus(dt_raw + dt_bias) spans small and large steps, norm
+    weight ~ 1 + N(0, 0.1) and bias ~ N(0, 0.1) over the HP channels, and a
+    scan output y [B, L, H, P] ~ N(0, 1) in bfloat16."""
+    HP, GN = H * P, G * N
+    C = HP + 2 * GN
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return {
+        "zxbcdt": round_bf16(_rng(seed, "zxbcdt").standard_normal((B, L, 2 * HP + 2 * GN + H))),
+        "conv_w": f32(_rng(seed, "conv_w").standard_normal((C, W)) / np.sqrt(W)),
+        "conv_b": f32(_rng(seed, "conv_b").standard_normal(C) * 0.1),
+        "dt_bias": f32(_rng(seed, "dt_bias").uniform(-4.0, 1.0, H)),
+        "norm_w": f32(1.0 + 0.1 * _rng(seed, "norm_w").standard_normal(HP)),
+        "norm_b": f32(0.1 * _rng(seed, "norm_b").standard_normal(HP)),
+        "y": round_bf16(_rng(seed, "ynorm").standard_normal((B, L, H, P))),
+    }
 
 
 def as_f64(arrs: Dict[str, Optional[np.ndarray]]) -> Dict[str, Optional[np.ndarray]]:
