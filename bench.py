@@ -217,6 +217,59 @@ def time_backward(w, steps, warmup, device):
 
 
 VARLEN_MEAN_LEN = 512.0
+CONV_WIDTH = 4
+
+
+def block_algorithmic(w):
+    """Bytes of the block prologue (the x, Bm, Cm and dt slices of the
+    projection output read once; x, Bm, Cm and dt written once) and of the
+    gated norm (y and z read once, the output written once)."""
+    bl, hp, gn = w.B * w.L, w.H * w.P, w.G * w.N
+    pro = bl * (hp + 2 * gn + w.H) * 2 + bl * (hp + 2 * gn) * 2 + bl * w.H * 4
+    norm = 3 * bl * hp * 2
+    return pro, norm
+
+
+def time_block(w, steps, warmup, device):
+    """Per-call event times (ms) of ssd_block_prologue and ssd_gated_norm at the
+    workload's shape, over two rotating sets of projection outputs and scan
+    outputs drawn on the device from a seeded generator (N(0, 1), bfloat16)."""
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    import ssd_inputs as si
+    small = si.make_block_inputs(1, 1, w.H, w.P, w.G, w.N, CONV_WIDTH, seed=w.seed + 11)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 12)
+    row = 2 * w.H * w.P + 2 * w.G * w.N + w.H
+    sets = [{"zx": torch.randn((w.B, w.L, row), generator=gen, device=device).to(torch.bfloat16),
+             "y": torch.randn((w.B, w.L, w.H, w.P), generator=gen, device=device).to(torch.bfloat16)}
+            for _ in range(2)]
+    cw, cb, db = (torch.from_numpy(small[k]).to(device) for k in ("conv_w", "conv_b", "dt_bias"))
+    nw, nb = (torch.from_numpy(small[k]).to(device) for k in ("norm_w", "norm_b"))
+    outs = [ssd.ssd_block_prologue(s["zx"], cw, cb, db, w.H, w.P, w.G, w.N) for s in sets]
+    nout = torch.empty_like(sets[0]["y"])
+
+    def run_pro(k):
+        s = sets[k % 2]
+        ssd.ssd_block_prologue(s["zx"], cw, cb, db, w.H, w.P, w.G, w.N)
+
+    def run_norm(k):
+        ssd.ssd_gated_norm(sets[k % 2]["y"], outs[k % 2]["z"], nw, nb, 1, 1e-5, True, out=nout)
+
+    res = []
+    for fn in (run_pro, run_norm):
+        for k in range(warmup):
+            fn(k)
+        torch.cuda.synchronize(device)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for k in range(steps):
+            starts[k].record()
+            fn(k)
+            ends[k].record()
+        torch.cuda.synchronize(device)
+        res.append(sorted(a.elapsed_time(b) for a, b in zip(starts, ends)))
+    return res
 
 
 def time_varlen(w, steps, warmup, device):
@@ -427,6 +480,15 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
                                     "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
         btotal += fk * f_fetch + wk * f_write
     out["bwd_bytes_per_call"] = btotal if out["bwd_kernels"] else None
+    out["block_kernels"] = {}
+    for name in ("prologue_kernel", "gated_norm_kernel"):
+        try:
+            fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
+            wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)
+        except SystemExit:
+            continue
+        out["block_kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
+                                      "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -442,6 +504,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -547,6 +610,20 @@ def main():
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": vb / (vmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "algorithmic_bytes": vb}}
+    if not args.no_block and headline:
+        tp, tn = time_block(w, max(10, args.steps // 2), 3, device)
+        pb, nb = block_algorithmic(w)
+
+        def leg(ts, nbytes, kernel):
+            m = sum(ts) / len(ts)
+            return {"kernel": kernel, "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
+                    "roofline": {"bound": "hbm", "achieved": nbytes / (m * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": nbytes}}
+        out["block"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name).replace("_ssd_chunk_scan", "_block_steps"),
+                        "conv_width": CONV_WIDTH, "norm": "group norm, 1 group, eps 1e-5",
+                        "prologue": leg(tp, pb, f"prologue_kernel<{CONV_WIDTH}>"),
+                        "gated_norm": leg(tn, nb, "gated_norm_kernel")}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -206,7 +206,8 @@ ssd_status ssd_block_prologue(const void *zxbcdt, const float *conv_w, const flo
  * or the projection row length to read z straight out of zxbcdt); weight,
  * bias fp32 [D] (bias may be NULL).  Covered: bfloat16, D a multiple of 8 up
  * to 8192, 1 <= ngroups <= 8 with D / ngroups a multiple of 8, z_stride a
- * multiple of 8 (else SSD_ERR_UNSUPPORTED).  Deterministic; asynchronous.
+ * multiple of 8 (else SSD_ERR_UNSUPPORTED); weight and bias 16-byte aligned.
+ * Deterministic; asynchronous.
  */
 ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const float *weight,
                           const float *bias, void *out, int64_t T, int64_t D, int64_t ngroups,

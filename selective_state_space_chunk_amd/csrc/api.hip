@@ -313,7 +313,7 @@ ssd_status ssd_block_prologue(const void *zxbcdt, const float *conv_w, const flo
     const void *ptrs[] = {zxbcdt, x, Bm, Cm};
     for (const void *p : ptrs)
         if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
-    if ((L + 63) / 64 > 65535 || B > 65535) return SSD_ERR_UNSUPPORTED;
+    if ((L + 31) / 32 > 65535 || B > 65535) return SSD_ERR_UNSUPPORTED;
     const hipError_t e = launch_block_prologue(zxbcdt, conv_w, conv_b, dt_bias, x, Bm, Cm, dt, B, L, H, H * P,
                                                G * N, W, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
@@ -329,7 +329,8 @@ ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const 
     const void *ptrs[] = {y, z, out};
     for (const void *p : ptrs)
         if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
-    if (T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if ((T + 3) / 4 > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (((uintptr_t)weight & 15u) != 0 || ((uintptr_t)bias & 15u) != 0) return SSD_ERR_INVALID_ARG;
     const hipError_t e = launch_gated_norm(y, z, z_stride, weight, bias, out, T, D, ngroups, eps, center, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }

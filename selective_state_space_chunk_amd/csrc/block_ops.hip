@@ -32,7 +32,9 @@ __device__ __forceinline__ void st_bf16x8(__bf16 *p, const f32x8 &v) {
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)v[e];
     *reinterpret_cast<bf16x8_t *>(p) = o;
 }
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// v * logistic(v) with the hardware reciprocal (about 1 ulp; the outputs are
+// rounded to bfloat16); v far below zero gives exp = inf, reciprocal 0, -0
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
 
 // ---------------------------------------------------------------------------
@@ -40,10 +42,10 @@ __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1p
 // dt (H)], bfloat16.  The C = HP + 2GN middle channels go through a causal
 // depthwise convolution of width W (taps conv_w[c][k], tap W-1 on the
 // current token, zero before token 0) plus bias and SiLU, into x, Bm, Cm;
-// dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 64 tokens of row b
-// from token 64 ty; lane k of channel tile cx takes channels 8(256 cx + k) ..
-// +7 for all 64 tokens, keeping the last W-1 inputs in registers.  The last
-// channel tile computes dt of the 64 tokens instead.
+// dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 32 tokens of row b
+// from token 32 ty; lane k of channel tile cx takes channels 8(256 cx + k) ..
+// +7 for all 32 tokens, keeping the last W-1 inputs in registers.  The last
+// channel tile computes dt of the 32 tokens instead.
 struct ProArgs {
     const __bf16 *zx;
     const float *conv_w, *conv_b, *dt_bias;
@@ -53,10 +55,10 @@ struct ProArgs {
     int ctiles;
 };
 
-constexpr int kTok = 64;
+constexpr int kTok = 32;
 
 template <int W>
-__global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prologue_kernel(ProArgs a) {
     const int64_t b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * kTok;
     const int nt = (int)(a.L - t0 < kTok ? a.L - t0 : kTok);
@@ -95,29 +97,38 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
         dst = a.Cm + b * a.L * a.GN + (c - a.HP - a.GN);
         dstride = a.GN;
     }
-    f32x8 hist[W > 1 ? W - 1 : 1];
+    // rows are kept as raw bfloat16 words and widened where they are used
+    constexpr int R = 8;   // tokens per round: their loads go out together
+    uint4 hist[W > 1 ? W - 1 : 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int64_t t = t0 - (W - 1) + j;
-        hist[j] = t >= 0 ? ld_bf16x8(src + t * a.row) : f32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        hist[j] = t >= 0 ? *reinterpret_cast<const uint4 *>(src + t * a.row) : uint4{0u, 0u, 0u, 0u};
     }
-    // four tokens per round: their loads go out together
-    for (int tt = 0; tt < nt; tt += 4) {
-        f32x8 cur[4];
+    auto widen = [](const uint4 &u, int e) {
+        const uint32_t w = e < 2 ? (e == 0 ? u.x : u.y) : (e == 2 ? u.z : u.w);
+        return w;
+    };
+    for (int tt = 0; tt < nt; tt += R) {
+        uint4 cur[R];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = tt + u < nt ? tt + u : nt - 1;
-            cur[u] = ld_bf16x8(src + (t0 + t) * a.row);
+        for (int u = 0; u < R; ++u) {
+            const int t = tt + u < nt ? tt + u : nt - 1;   // clamped: every load in bounds
+            cur[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < R; ++u) {
             f32x8 acc;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                auto val = [&](const uint4 &r) {
+                    const uint32_t w = widen(r, e >> 1);
+                    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                };
                 float s = bias[e];
 #pragma unroll
-                for (int k = 0; k < W - 1; ++k) s = __builtin_fmaf(wk[k][e], hist[k][e], s);
-                acc[e] = silu(__builtin_fmaf(wk[W - 1][e], cur[u][e], s));
+                for (int k = 0; k < W - 1; ++k) s = __builtin_fmaf(wk[k][e], val(hist[k]), s);
+                acc[e] = silu(__builtin_fmaf(wk[W - 1][e], val(cur[u]), s));
             }
             if (tt + u < nt) st_bf16x8(dst + (t0 + tt + u) * dstride, acc);
 #pragma unroll
@@ -128,17 +139,18 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gated norm.  One workgroup per token: v = y * SiLU(z) over its D channels,
-// normalised within each of ngroups equal groups (mean-centred with variance,
-// or root mean square only), times weight, plus bias.  Thread k holds
-// channel chunks k, k + 256, ... (8 channels each, at most 4 chunks) in
-// registers; group sums go through per-wave partials in LDS in a fixed
-// order, so results are deterministic.
+// Gated norm.  One wave per token (four tokens per workgroup): v = y * SiLU(z)
+// over its D channels, normalised within each of ngroups equal groups
+// (mean-centred with variance, or root mean square only), times weight, plus
+// bias.  Lane l holds channel chunks l, l + 64, ... (8 channels each, KC
+// chunks) in registers, so that all of a token's loads are in flight at once
+// and the group sums are wave reductions with no barrier.  The sums run in
+// a fixed order, so results are deterministic.
 struct NormArgs {
     const __bf16 *y, *z;
     const float *w, *bias;
     __bf16 *out;
-    int64_t D, zstride;
+    int64_t T, D, zstride;
     int ngroups, center;
     float eps;
 };
@@ -151,87 +163,90 @@ __device__ __forceinline__ float wave_sum64(float v) {
     return v;
 }
 
-// sum over the workgroup of part[k] for the chunks of group g, for every g;
-// result for group g in tot[g]
-__device__ __forceinline__ void group_sums(const float (&part)[4], const int (&grp)[4], int ngroups,
-                                           float (*red)[kMaxGroups], float (&tot)[kMaxGroups]) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // (loops to the constant bound, so that tot stays in registers)
+// tot[g] = sum over the wave of part[k] for this lane's chunks of group g
+template <int KC>
+__device__ __forceinline__ void group_sums(const float (&part)[KC], const int (&grp)[KC], int ngroups,
+                                           float (&tot)[kMaxGroups]) {
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) {
+        tot[g] = 0.f;
         if (g < ngroups) {
             float s = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) s += grp[k] == g ? part[k] : 0.f;
-            s = wave_sum64(s);
-            if (lane == 0) red[wave][g] = s;
+            for (int k = 0; k < KC; ++k) s += grp[k] == g ? part[k] : 0.f;
+            tot[g] = wave_sum64(s);
         }
     }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g)
-        tot[g] = g < ngroups ? (red[0][g] + red[1][g]) + (red[2][g] + red[3][g]) : 0.f;
-    __syncthreads();
 }
 
+template <int KC>
 __global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a) {
-    __shared__ float red[4][kMaxGroups];
-    const int64_t t = blockIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    const int lane = threadIdx.x & 63;
     const int nch = (int)(a.D / 8), gch = nch / a.ngroups;
     const float inv = 1.f / (float)(a.D / a.ngroups);
-    f32x8 v[4];
-    int grp[4];
-    float part[4];
+    f32x8 yv[KC], zv[KC];
+    int grp[KC];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int ch = threadIdx.x + 256 * k;
+    for (int k = 0; k < KC; ++k) {
+        const int ch = lane + 64 * k;
         grp[k] = ch < nch ? ch / gch : -1;
-        part[k] = 0.f;
-        if (ch < nch) {
-            const f32x8 yv = ld_bf16x8(a.y + t * a.D + 8 * ch);
-            const f32x8 zv = ld_bf16x8(a.z + t * a.zstride + 8 * ch);
+        const int cl = ch < nch ? ch : nch - 1;   // clamped: every load in bounds
+        yv[k] = ld_bf16x8(a.y + t * a.D + 8 * cl);
+        zv[k] = ld_bf16x8(a.z + t * a.zstride + 8 * cl);
+    }
+    f32x8 v[KC];
+    float part[KC];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[k][e] = yv[e] * silu(zv[e]);
-                part[k] += v[k][e];
-            }
+    for (int k = 0; k < KC; ++k) {
+        part[k] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[k][e] = yv[k][e] * silu(zv[k][e]);
+            part[k] += v[k][e];
         }
     }
-    float mean[kMaxGroups], tot[kMaxGroups];
-#pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) mean[g] = 0.f;
+    float tot[kMaxGroups];
     if (a.center) {
-        group_sums(part, grp, a.ngroups, red, tot);
+        group_sums<KC>(part, grp, a.ngroups, tot);
 #pragma unroll
-        for (int g = 0; g < kMaxGroups; ++g) mean[g] = tot[g] * inv;
-    }
-    // second pass over the registers: squares about the mean
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        part[k] = 0.f;
-        if (grp[k] >= 0) {
+        for (int k = 0; k < KC; ++k) {
             float m = 0.f;
 #pragma unroll
-            for (int g = 0; g < kMaxGroups; ++g) m = g == grp[k] ? mean[g] : m;
+            for (int g = 0; g < kMaxGroups; ++g) m = g == grp[k] ? tot[g] * inv : m;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[k][e] -= m;
-                part[k] = __builtin_fmaf(v[k][e], v[k][e], part[k]);
-            }
+            for (int e = 0; e < 8; ++e) v[k][e] -= m;
         }
     }
-    group_sums(part, grp, a.ngroups, red, tot);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < KC; ++k) {
+        part[k] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[k] = __builtin_fmaf(v[k][e], v[k][e], part[k]);
+    }
+    group_sums<KC>(part, grp, a.ngroups, tot);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
         if (grp[k] < 0) continue;
         float ms = 0.f;
 #pragma unroll
         for (int g = 0; g < kMaxGroups; ++g) ms = g == grp[k] ? tot[g] : ms;
         const float r = __builtin_amdgcn_rsqf(ms * inv + a.eps);
-        const int64_t c0 = 8 * (int64_t)(threadIdx.x + 256 * k);
+        const int64_t c0 = 8 * (int64_t)(lane + 64 * k);
+        const float4 w0 = *reinterpret_cast<const float4 *>(a.w + c0);
+        const float4 w1 = *reinterpret_cast<const float4 *>(a.w + c0 + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (a.bias) {
+            const float4 b0 = *reinterpret_cast<const float4 *>(a.bias + c0);
+            const float4 b1 = *reinterpret_cast<const float4 *>(a.bias + c0 + 4);
+            bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
+            bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+        }
         f32x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = v[k][e] * r * a.w[c0 + e] + (a.bias ? a.bias[c0 + e] : 0.f);
+        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(v[k][e] * r, wv[e], bv[e]);
         st_bf16x8(a.out + t * a.D + c0, o);
     }
 }
@@ -262,16 +277,26 @@ hipError_t launch_block_prologue(const void *zx, const float *conv_w, const floa
 }
 
 bool gated_norm_supported(int64_t D, int64_t ngroups, int64_t zstride) {
-    return D % 8 == 0 && D / 8 <= 4 * 256 && ngroups >= 1 && ngroups <= kMaxGroups && D % ngroups == 0 &&
+    return D % 8 == 0 && D / 8 <= 16 * 64 && ngroups >= 1 && ngroups <= kMaxGroups && D % ngroups == 0 &&
            (D / ngroups) % 8 == 0 && zstride >= D && zstride % 8 == 0;
 }
 
 hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, const float *w, const float *bias,
                              void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
                              hipStream_t stream) {
-    NormArgs a{(const __bf16 *)y, (const __bf16 *)z, w, bias, (__bf16 *)out, D, zstride, (int)ngroups,
+    NormArgs a{(const __bf16 *)y, (const __bf16 *)z, w, bias, (__bf16 *)out, T, D, zstride, (int)ngroups,
                center ? 1 : 0, eps};
-    gated_norm_kernel<<<dim3((unsigned)T), 256, 0, stream>>>(a);
+    const dim3 grid((unsigned)((T + 3) / 4));
+    const int kc = (int)((D / 8 + 63) / 64);   // chunks per lane
+    switch (kc) {
+#define SSD_NORM_CASE(K) \
+    case K: gated_norm_kernel<K><<<grid, 256, 0, stream>>>(a); break;
+        SSD_NORM_CASE(1) SSD_NORM_CASE(2) SSD_NORM_CASE(3) SSD_NORM_CASE(4) SSD_NORM_CASE(5) SSD_NORM_CASE(6)
+        SSD_NORM_CASE(7) SSD_NORM_CASE(8) SSD_NORM_CASE(9) SSD_NORM_CASE(10) SSD_NORM_CASE(11)
+        SSD_NORM_CASE(12) SSD_NORM_CASE(13) SSD_NORM_CASE(14) SSD_NORM_CASE(15) SSD_NORM_CASE(16)
+#undef SSD_NORM_CASE
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
