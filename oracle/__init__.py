@@ -18,6 +18,7 @@ Forms:
   each run of equal values scanned on its own (``varlen.py``).
 * ``block_prologue`` / ``gated_norm`` -- the steps before and after the scan
   in a Mamba-2 block (``block.py``).
+* ``selective_scan`` -- the Mamba-1 selective scan with diagonal A (``s6.py``).
 
 Every function takes float64 arrays (the values the GPU receives, widened
 exactly) and returns float64 arrays.
@@ -35,6 +36,7 @@ from .forms import chunked, decay_mask, quadratic  # noqa: F401
 from .backward import recurrence_bwd  # noqa: F401
 from .varlen import recurrence_varlen, run_bounds  # noqa: F401
 from .block import block_prologue, gated_norm  # noqa: F401
+from .s6 import selective_scan  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
