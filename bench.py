@@ -308,6 +308,54 @@ def time_varlen(w, steps, warmup, device):
     return sorted(s.elapsed_time(e) for s, e in zip(starts, ends)), nseq
 
 
+# Mamba-1 2.8B layer: d_inner 5120 channels, N = 16 states, the same 4 x 4096 tokens
+S6_SHAPE = {"batch": 4, "seq_len": 4096, "channels": 5120, "state": 16, "groups": 1}
+# vector-ALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (non-packed fp32)
+VALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
+# slots one state update needs at least: one exp2 (a quarter-rate transcendental, 4 slots)
+# and three multiply-adds (dt A, the input term, the output sum)
+S6_SLOTS_PER_UPDATE = 7
+
+
+def time_s6(steps, warmup, device):
+    """Per-call event times (ms) of ssd_selective_scan (zero-order hold) over two
+    rotating input sets drawn on the device from a seeded generator."""
+    import torch
+    import selective_state_space_chunk_amd as ssd
+    B, L, Dch, N = (S6_SHAPE[k] for k in ("batch", "seq_len", "channels", "state"))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED_S6)
+    sets = []
+    for _ in range(2):
+        sets.append({"x": torch.randn((B, L, Dch), generator=gen, device=device).to(torch.bfloat16),
+                     "dt": torch.nn.functional.softplus(torch.randn((B, L, Dch), generator=gen, device=device) - 1.0
+                                                        ).to(torch.bfloat16),
+                     "Bm": torch.randn((B, L, 1, N), generator=gen, device=device).to(torch.bfloat16),
+                     "Cm": torch.randn((B, L, 1, N), generator=gen, device=device).to(torch.bfloat16)})
+    A = -torch.exp(torch.rand((Dch, N), generator=gen, device=device) * 2.5 - 1.0)
+    D = torch.randn((Dch,), generator=gen, device=device)
+    init = torch.randn((B, Dch, N), generator=gen, device=device) * 0.3
+
+    def run(k):
+        s = sets[k % 2]
+        ssd.ssd_selective_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], D, init, zoh=True)
+
+    for k in range(warmup):
+        run(k)
+    torch.cuda.synchronize(device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        starts[k].record()
+        run(k)
+        ends[k].record()
+    torch.cuda.synchronize(device)
+    return sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+
+
+SEED_S6 = 20240531
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle (token-by-token recurrence, OpenMP over (batch, head)
     sequences) on a bounded sample of the same workload: whole sequences of
@@ -505,6 +553,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--no-s6", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -624,6 +673,20 @@ def main():
                         "conv_width": CONV_WIDTH, "norm": "group norm, 1 group, eps 1e-5",
                         "prologue": leg(tp, pb, f"prologue_kernel<{CONV_WIDTH}>"),
                         "gated_norm": leg(tn, nb, "gated_norm_kernel")}
+    if not args.no_s6 and headline:
+        ts = time_s6(max(10, args.steps // 2), 3, device)
+        m = sum(ts) / len(ts)
+        sh = S6_SHAPE
+        toks = sh["batch"] * sh["seq_len"]
+        updates = toks * sh["channels"] * sh["state"]
+        peak = VALU_LANE_SLOTS / S6_SLOTS_PER_UPDATE
+        nbytes = 3 * toks * sh["channels"] * 2 + 2 * toks * sh["state"] * 2 + 2 * sh["batch"] * sh["channels"] * sh["state"] * 4
+        out["s6"] = {"workload": "mamba1_2.8b_layer_selective_scan", "config": dict(sh, discretisation="zero-order hold"),
+                     "kernel": "s6_kernel<16>", "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
+                     "tokens_per_s": toks / (m * 1e-3),
+                     "roofline": {"bound": "alu", "achieved": updates / (m * 1e-3) / 1e12, "peak": peak / 1e12,
+                                  "unit": "T state updates/s", "frac": updates / (m * 1e-3) / peak,
+                                  "hbm_gbs": nbytes / (m * 1e-3) / 1e9, "algorithmic_bytes": nbytes}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -214,6 +214,27 @@ ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const 
                           float eps, int center, ssd_dtype dtype, hipStream_t stream);
 
 /*
+ * Mamba-1 selective scan with diagonal A ("Mamba" reading notes, section 2.2:
+ * h_t = Abar h_{t-1} + Bbar x_t, y_t = C h_t, zero-order hold
+ * Abar = exp(dt A), Bbar = (dt A)^-1 (exp(dt A) - I) dt B; section 3.2: dt,
+ * B, C depend on the token).  Per channel d and state n:
+ *   h[d][n] = exp(dt[d] A[d][n]) h[d][n] + bbar x[d],
+ *   y[d] = sum_n Cm[n] h[d][n] + D[d] x[d],
+ * with bbar = (exp(dt A) - 1) / A[d][n] * Bm[n] (zoh = 1; dt Bm[n] where A is
+ * 0) or bbar = dt[d] Bm[n] (zoh = 0).  Layouts: x, dt, y bfloat16
+ * [B, L, Dch] (dt the step, already positive); A fp32 [Dch, N]; Bm, Cm
+ * bfloat16 [B, L, G, N], channel d reading group d / (Dch / G); D fp32 [Dch]
+ * or NULL; init_state and final_state fp32 [B, Dch, N] or NULL.  Covered:
+ * bfloat16, N = 8, 16 or 32, Dch / G a multiple of 64 (else
+ * SSD_ERR_UNSUPPORTED).  Device pointers, caller-owned, 16-byte aligned for
+ * the bfloat16 arrays; no workspace; asynchronous on `stream`.
+ */
+ssd_status ssd_selective_scan(const void *x, const void *dt, const float *A, const void *Bm,
+                              const void *Cm, const float *D, const float *init_state, void *y,
+                              float *final_state, int64_t B, int64_t L, int64_t Dch, int64_t G,
+                              int64_t N, int zoh, ssd_dtype dtype, hipStream_t stream);
+
+/*
  * Diagnostic: waits for `stream`, then checks the hand-off state that
  * SSD_ALGO_FUSED keeps in this workspace: no block-to-block hand-off ever gave
  * up waiting (a bounded wait that is never expected to expire; when it does,

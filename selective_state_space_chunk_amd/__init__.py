@@ -79,6 +79,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_gated_norm.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                    ctypes.c_int, vp]
     lib.ssd_gated_norm.restype = ctypes.c_int
+    lib.ssd_selective_scan.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_int, vp]
+    lib.ssd_selective_scan.restype = ctypes.c_int
     lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
     lib.ssd_chunk_scan_bwd.argtypes = [vp] * 17 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
@@ -298,6 +300,37 @@ def ssd_gated_norm(y: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, bias:
                             float(eps), 1 if center else 0, SSD_DTYPE_BF16, _stream_handle(dev, stream))
     _check(st, "ssd_gated_norm")
     return out
+
+
+def ssd_selective_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Cm: torch.Tensor,
+                       D: Optional[torch.Tensor] = None, init_state: Optional[torch.Tensor] = None, *,
+                       zoh: bool = True, return_final: bool = True,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-1 selective scan: x, dt [B, L, Dch] bfloat16, A [Dch, N] f32,
+    Bm, Cm [B, L, G, N] bfloat16, D [Dch] f32 or None, init_state
+    [B, Dch, N] f32 or None.  Returns (y [B, L, Dch], final_state)."""
+    lib = load_library()
+    if x.dim() != 3 or Bm.dim() != 4:
+        raise ValueError("x must be [B, L, Dch] and Bm [B, L, G, N]")
+    Bsz, L, Dch = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (Bsz, L, Dch), dev)
+    _need(dt, "dt", torch.bfloat16, (Bsz, L, Dch), dev)
+    _need(A, "A", torch.float32, (Dch, N), dev)
+    _need(Bm, "Bm", torch.bfloat16, (Bsz, L, G, N), dev)
+    _need(Cm, "Cm", torch.bfloat16, (Bsz, L, G, N), dev)
+    if D is not None:
+        _need(D, "D", torch.float32, (Dch,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (Bsz, Dch, N), dev)
+    y = torch.empty_like(x)
+    final = torch.empty((Bsz, Dch, N), dtype=torch.float32, device=dev) if return_final else None
+    st = lib.ssd_selective_scan(_ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y),
+                                _ptr(final), Bsz, L, Dch, G, N, 1 if zoh else 0, SSD_DTYPE_BF16,
+                                _stream_handle(dev, stream))
+    _check(st, "ssd_selective_scan")
+    return y, final
 
 
 def ssd_chunk_scan_workspace_check(workspace_tensor: torch.Tensor, B: int, L: int, H: int, P: int,

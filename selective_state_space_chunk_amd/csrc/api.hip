@@ -21,6 +21,10 @@ hipError_t launch_block_prologue(const void *zx, const float *conv_w, const floa
                                  void *x, void *Bm, void *Cm, float *dt, int64_t B, int64_t L, int64_t H,
                                  int64_t HP, int64_t GN, int64_t W, hipStream_t stream);
 bool gated_norm_supported(int64_t D, int64_t ngroups, int64_t zstride);
+bool s6_supported(int64_t Dch, int64_t G, int64_t N);
+hipError_t launch_s6(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                     const float *init, void *y, float *final_state, int64_t B, int64_t L, int64_t Dch, int64_t G,
+                     int64_t N, int zoh, hipStream_t stream);
 hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, const float *w, const float *bias,
                              void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
                              hipStream_t stream);
@@ -332,6 +336,30 @@ ssd_status ssd_gated_norm(const void *y, const void *z, int64_t z_stride, const 
     if ((T + 3) / 4 > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (((uintptr_t)weight & 15u) != 0 || ((uintptr_t)bias & 15u) != 0) return SSD_ERR_INVALID_ARG;
     const hipError_t e = launch_gated_norm(y, z, z_stride, weight, bias, out, T, D, ngroups, eps, center, stream);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_selective_scan(const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
+                              const float *D, const float *init_state, void *y, float *final_state, int64_t B,
+                              int64_t L, int64_t Dch, int64_t G, int64_t N, int zoh, ssd_dtype dtype,
+                              hipStream_t stream) {
+    if (B < 0 || L < 0 || Dch <= 0 || G <= 0 || N <= 0 || Dch % G != 0) return SSD_ERR_INVALID_ARG;
+    if (dtype != SSD_DTYPE_BF16 || !s6_supported(Dch, G, N)) return SSD_ERR_UNSUPPORTED;
+    if (B > 65535 || Dch / 64 > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (B == 0) return SSD_OK;
+    if (L == 0) {
+        if (final_state) {
+            const int64_t n = B * Dch * N;
+            if (init_state != final_state)
+                fill_or_copy<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(final_state, init_state, n);
+        }
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    if (!x || !dt || !A || !Bm || !Cm || !y) return SSD_ERR_INVALID_ARG;
+    const void *ptrs[] = {x, dt, Bm, Cm, y};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
+    const hipError_t e = launch_s6(x, dt, A, Bm, Cm, D, init_state, y, final_state, B, L, Dch, G, N, zoh, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -37,7 +37,7 @@ import numpy as np
 # same stream for the same tensor
 _TID = {"x": 1, "dt": 2, "A": 3, "Bm": 4, "Cm": 5, "D": 6, "init": 7,
         "step_x": 11, "step_dt": 12, "step_Bm": 14, "step_Cm": 15,
-        "dy": 21, "dfinal": 22, "seq": 23, "zxbcdt": 24, "conv_w": 25, "conv_b": 26, "dt_bias": 27, "norm_w": 28, "norm_b": 29, "ynorm": 30}
+        "dy": 21, "dfinal": 22, "seq": 23, "zxbcdt": 24, "conv_w": 25, "conv_b": 26, "dt_bias": 27, "norm_w": 28, "norm_b": 29, "ynorm": 30, "s6x": 31, "s6dt": 32, "s6A": 33, "s6B": 34, "s6C": 35, "s6D": 36, "s6init": 37}
 
 SEED_BASE = 20240531
 
@@ -245,6 +245,24 @@ def make_block_inputs(B: int, L: int, H: int, P: int, G: int, N: int, W: int = 4
         "norm_w": f32(1.0 + 0.1 * _rng(seed, "norm_w").standard_normal(HP)),
         "norm_b": f32(0.1 * _rng(seed, "norm_b").standard_normal(HP)),
         "y": round_bf16(_rng(seed, "ynorm").standard_normal((B, L, H, P))),
+    }
+
+
+def make_s6_inputs(B: int, L: int, Dch: int, N: int, G: int = 1, *, init: bool = True,
+                   seed: int = SEED_BASE) -> Dict[str, Optional[np.ndarray]]:
+    """Seeded inputs of the Mamba-1 selective scan: x ~ N(0, 1) and dt =
+    softplus(N(-1, 1)) in bfloat16 [B, L, Dch]; A = -exp(U(-1, 1.5)) fp32
+    [Dch, N] (decays from mild to strong); Bm, Cm ~ N(0, 1) bfloat16
+    [B, L, G, N]; D ~ N(0, 1) fp32 [Dch]; init ~ N(0, 0.3) fp32 [B, Dch, N]."""
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return {
+        "x": round_bf16(_rng(seed, "s6x").standard_normal((B, L, Dch))),
+        "dt": round_bf16(_softplus(_rng(seed, "s6dt").standard_normal((B, L, Dch)) - 1.0)),
+        "A": f32(-np.exp(_rng(seed, "s6A").uniform(-1.0, 1.5, (Dch, N)))),
+        "Bm": round_bf16(_rng(seed, "s6B").standard_normal((B, L, G, N))),
+        "Cm": round_bf16(_rng(seed, "s6C").standard_normal((B, L, G, N))),
+        "D": f32(_rng(seed, "s6D").standard_normal(Dch)),
+        "init": f32(_rng(seed, "s6init").standard_normal((B, Dch, N)) * 0.3) if init else None,
     }
 
 
