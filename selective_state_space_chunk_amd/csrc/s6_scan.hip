@@ -7,10 +7,14 @@
 //
 // Workgroup (channel block, b): 64 channels of batch row b, four waves.  Lane
 // l of wave w takes channel 16w + l % 16 and its states n = (l / 16) N/4 ..
-// + N/4 - 1, so each lane runs N/4 independent chains; y is summed over the
-// four lanes of a channel with two cross-lane adds.  Tokens go in chunks of
-// 32: x, dt (32 rows x 128 bytes) and Bm, Cm of a chunk are staged in LDS
-// from registers loaded one chunk ahead, and y leaves as whole 128-byte rows.
+// + N/4 - 1, so each lane runs N/4 independent chains.  Tokens go in chunks
+// of 32: x and dt (32 rows x 128 bytes) are staged in LDS transposed, so
+// that a lane reads 8 tokens of its channel at once, and Bm, Cm as they come,
+// all from registers loaded one chunk ahead.  A lane keeps its partial sums of
+// y for the whole chunk in registers; the four partials of a channel are added
+// once per chunk through LDS, and y leaves as whole 128-byte rows.  Tokens
+// past the end are zeros (dt = 0, x = 0), which leave the state as it is, so
+// every chunk runs all 32 steps unrolled.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,15 +35,20 @@ constexpr int kCh = 64;   // channels per workgroup
 constexpr int kT = 32;    // tokens per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int N>
+// kZoh: zero-order-hold input term (else dt Bm x); a template parameter so
+// that the unrolled chunk is one block the scheduler can interleave
+template <int N, bool kZoh>
 __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
     constexpr int SPL = N / 4;          // states per lane
     constexpr int BCT = kT * N / 8;     // threads that stage Bm (and Cm) of a chunk
-    __shared__ __align__(16) __bf16 xs[2][kT][kCh];
-    __shared__ __align__(16) __bf16 ds[2][kT][kCh];
-    __shared__ __align__(16) __bf16 bs[2][kT][N];
-    __shared__ __align__(16) __bf16 cs[2][kT][N];
-    __shared__ __align__(16) __bf16 ys[kT][kCh];
+    constexpr int XS = kT + 4;          // row of the transposed x / dt tiles (fp32)
+    constexpr int YS = kT + 4;          // row of the partial-sum tile (fp32)
+    // staged in fp32: the conversions happen once, at staging
+    __shared__ __align__(16) float xt[2][kCh][XS];   // [channel][token]
+    __shared__ __align__(16) float dtt[2][kCh][XS];
+    __shared__ __align__(16) float bs[2][kT][N];
+    __shared__ __align__(16) float cs[2][kT][N];
+    __shared__ __align__(16) float yq[4][kCh][YS];    // per-quarter partial sums of y
     const int64_t b = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * kCh;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -49,26 +58,33 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
     const int64_t g = c0 / (a.Dch / a.G);
     const int64_t L = a.L;
 
-    float A2[SPL], invA[SPL], h[SPL];
+    // zero-order hold: h' = av h + coef Bm x with coef = (av - 1) / A, where
+    // A = 0 its limit dt (invA = 0 and zf = 1 there: coef = dt)
+    float A2[SPL], invA[SPL], zf[SPL], h[SPL];
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
         const int n = q * SPL + j;
         const float Av = a.A[c * N + n];
         A2[j] = Av * kLog2e;
         invA[j] = Av != 0.f ? 1.f / Av : 0.f;
+        zf[j] = Av != 0.f ? 0.f : 1.f;
         h[j] = a.init ? a.init[(b * a.Dch + c) * N + n] : 0.f;
     }
-    const float Dd = a.D ? a.D[c] : 0.f;
 
-    // staging roles: row sr, 8 channels from sc of the x and dt tiles; row br,
-    // 8 states from bcol of the Bm and Cm tiles (threads below BCT)
+    // staging roles: token sr, channels sc .. sc+7 of the x and dt tiles (also
+    // the y rows this thread stores); token br, states bcol .. +7 of the Bm and
+    // Cm tiles (threads below BCT)
     const int sr = tid >> 3, sc = (tid & 7) * 8;
     const int br = tid / (N / 8), bcol = (tid % (N / 8)) * 8;
+    float Dv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Dv[e] = a.D ? a.D[c0 + sc + e] : 0.f;
     const uint4 zero = {0u, 0u, 0u, 0u};
     uint4 rx, rd, rb = zero, rc = zero;
+    auto bf = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); };
     auto load = [&](int64_t t0) __attribute__((always_inline)) {
         const int64_t t = t0 + sr;
-        const bool ok = t < L;   // rows past the end read as zeros
+        const bool ok = t < L;   // tokens past the end read as zeros: dt = 0 and x = 0 leave h as it is
         const int64_t xo = (b * L + (ok ? t : 0)) * a.Dch + c0 + sc;
         rx = ok ? *reinterpret_cast<const uint4 *>(a.x + xo) : zero;
         rd = ok ? *reinterpret_cast<const uint4 *>(a.dt + xo) : zero;
@@ -81,14 +97,22 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
         }
     };
     auto stage = [&](int buf) __attribute__((always_inline)) {
-        *reinterpret_cast<uint4 *>(&xs[buf][sr][sc]) = rx;
-        *reinterpret_cast<uint4 *>(&ds[buf][sr][sc]) = rd;
+        const uint32_t wx[4] = {rx.x, rx.y, rx.z, rx.w}, wd[4] = {rd.x, rd.y, rd.z, rd.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xt[buf][sc + e][sr] = bf(wx[e >> 1], e & 1);
+            dtt[buf][sc + e][sr] = bf(wd[e >> 1], e & 1);
+        }
         if (tid < BCT) {
-            *reinterpret_cast<uint4 *>(&bs[buf][br][bcol]) = rb;
-            *reinterpret_cast<uint4 *>(&cs[buf][br][bcol]) = rc;
+            const uint32_t wb[4] = {rb.x, rb.y, rb.z, rb.w}, wc[4] = {rc.x, rc.y, rc.z, rc.w};
+            float4 *bo = reinterpret_cast<float4 *>(&bs[buf][br][bcol]);
+            float4 *co = reinterpret_cast<float4 *>(&cs[buf][br][bcol]);
+            bo[0] = float4{bf(wb[0], 0), bf(wb[0], 1), bf(wb[1], 0), bf(wb[1], 1)};
+            bo[1] = float4{bf(wb[2], 0), bf(wb[2], 1), bf(wb[3], 0), bf(wb[3], 1)};
+            co[0] = float4{bf(wc[0], 0), bf(wc[0], 1), bf(wc[1], 0), bf(wc[1], 1)};
+            co[1] = float4{bf(wc[2], 0), bf(wc[2], 1), bf(wc[3], 0), bf(wc[3], 1)};
         }
     };
-
     const int nchunks = (int)((L + kT - 1) / kT);
     load(0);
     stage(0);
@@ -97,24 +121,24 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
     for (int k = 0; k < nchunks; ++k) {
         const int buf = k & 1;
         const int nt = (int)(L - (int64_t)k * kT < kT ? L - (int64_t)k * kT : kT);
-        for (int tt = 0; tt < nt; ++tt) {
-            const float xv = (float)xs[buf][tt][ci];
-            const float dv = (float)ds[buf][tt][ci];
+        float yp[kT];
+#pragma unroll
+        for (int tt = 0; tt < kT; ++tt) {
+            const float xv = xt[buf][ci][tt], dv = dtt[buf][ci][tt];
             float bv[SPL], cv[SPL];
 #pragma unroll
             for (int j = 0; j < SPL; ++j) {
-                bv[j] = (float)bs[buf][tt][q * SPL + j];
-                cv[j] = (float)cs[buf][tt][q * SPL + j];
+                bv[j] = bs[buf][tt][q * SPL + j];
+                cv[j] = cs[buf][tt][q * SPL + j];
             }
-            float yp = 0.f;
-            if (a.zoh) {
-                // bbar x = (exp(dt A) - 1) / A * B x; its limit dt B x where A = 0
+            float acc = 0.f;
+            if constexpr (kZoh) {
 #pragma unroll
                 for (int j = 0; j < SPL; ++j) {
                     const float av = __builtin_amdgcn_exp2f(dv * A2[j]);
-                    const float coef = invA[j] != 0.f ? (av - 1.f) * invA[j] : dv;
+                    const float coef = __builtin_fmaf(zf[j], dv, __builtin_fmaf(av, invA[j], -invA[j]));
                     h[j] = __builtin_fmaf(av, h[j], coef * (bv[j] * xv));
-                    yp = __builtin_fmaf(cv[j], h[j], yp);
+                    acc = __builtin_fmaf(cv[j], h[j], acc);
                 }
             } else {
                 const float dtx = dv * xv;
@@ -122,17 +146,30 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
                 for (int j = 0; j < SPL; ++j) {
                     const float av = __builtin_amdgcn_exp2f(dv * A2[j]);
                     h[j] = __builtin_fmaf(av, h[j], dtx * bv[j]);
-                    yp = __builtin_fmaf(cv[j], h[j], yp);
+                    acc = __builtin_fmaf(cv[j], h[j], acc);
                 }
             }
-            yp += __shfl_xor(yp, 16, 64);
-            yp += __shfl_xor(yp, 32, 64);
-            if (q == 0) ys[tt][ci] = (__bf16)__builtin_fmaf(Dd, xv, yp);
+            yp[tt] = acc;
         }
+#pragma unroll
+        for (int r = 0; r < kT / 4; ++r)
+            *reinterpret_cast<float4 *>(&yq[q][ci][4 * r]) = float4{yp[4 * r], yp[4 * r + 1], yp[4 * r + 2], yp[4 * r + 3]};
         __syncthreads();
-        if (sr < nt)
-            *reinterpret_cast<uint4 *>(a.y + (b * L + (int64_t)k * kT + sr) * a.Dch + c0 + sc) =
-                *reinterpret_cast<const uint4 *>(&ys[sr][sc]);
+        // y of token sr, channels sc .. sc+7: the four quarters' partial sums plus D x
+        if (sr < nt) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = xt[buf][sc + e][sr];
+                o[e] = ((yq[0][sc + e][sr] + yq[1][sc + e][sr]) + (yq[2][sc + e][sr] + yq[3][sc + e][sr])) +
+                       Dv[e] * xv;
+            }
+            typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+            bf16x8_t ov;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ov[e] = (__bf16)o[e];
+            *reinterpret_cast<bf16x8_t *>(a.y + (b * L + (int64_t)k * kT + sr) * a.Dch + c0 + sc) = ov;
+        }
         if (k + 1 < nchunks) {
             stage(buf ^ 1);
             if (k + 2 < nchunks) load((int64_t)(k + 2) * kT);
@@ -157,10 +194,13 @@ hipError_t launch_s6(const void *x, const void *dt, const float *A, const void *
     S6Args a{(const __bf16 *)x, (const __bf16 *)dt, (const __bf16 *)Bm, (const __bf16 *)Cm, A, D, init,
              (__bf16 *)y, final_state, L, Dch, G, zoh ? 1 : 0};
     const dim3 grid((unsigned)(Dch / kCh), (unsigned)B);
-    switch (N) {
-        case 8: s6_kernel<8><<<grid, 256, 0, stream>>>(a); break;
-        case 16: s6_kernel<16><<<grid, 256, 0, stream>>>(a); break;
-        case 32: s6_kernel<32><<<grid, 256, 0, stream>>>(a); break;
+    switch (N * 2 + (zoh ? 1 : 0)) {
+        case 16: s6_kernel<8, false><<<grid, 256, 0, stream>>>(a); break;
+        case 17: s6_kernel<8, true><<<grid, 256, 0, stream>>>(a); break;
+        case 32: s6_kernel<16, false><<<grid, 256, 0, stream>>>(a); break;
+        case 33: s6_kernel<16, true><<<grid, 256, 0, stream>>>(a); break;
+        case 64: s6_kernel<32, false><<<grid, 256, 0, stream>>>(a); break;
+        case 65: s6_kernel<32, true><<<grid, 256, 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
