@@ -32,7 +32,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
               "ssd_status_string", "ssd_chunk_scan_fwd_algo", "ssd_version",
-              "ssd_chunk_scan_workspace_check", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size"):
+              "ssd_chunk_scan_workspace_check", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
+              "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_varlen_workspace_size", "ssd_block_prologue",
+              "ssd_gated_norm", "ssd_selective_scan"):
         assert n in names
 
 
@@ -147,3 +149,71 @@ def test_backward_workspace_size(lib):
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 0) == 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, 32, G, N, Q, 1) == 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, 256, Q, 1) == 0
+
+
+def test_varlen_rejects_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+
+    def call(x=0x10000, seq=0x90000, ws=0x80000, ws_bytes=1 << 40, shape=(B, L, H, P, G, N, Q), dtype=1):
+        b, l, h, p, g, n, q = shape
+        return lib.ssd_chunk_scan_fwd_varlen(fake(x) if x else None, fake(0x20000), fake(0x30000), fake(0x40000),
+                                             fake(0x50000), fake(0x60000), None, fake(seq) if seq else None,
+                                             fake(0x70000), None, fake(ws) if ws else None, ws_bytes,
+                                             b, l, h, p, g, n, q, dtype, None)
+    assert call(x=0) == ssd.SSD_ERR_INVALID_ARG
+    assert call(seq=0) == ssd.SSD_ERR_INVALID_ARG                    # no sequence index
+    assert call(seq=0x90002) == ssd.SSD_ERR_INVALID_ARG              # misaligned int32
+    assert call(shape=(B, L, H, P, G, N, 0)) == ssd.SSD_ERR_INVALID_ARG
+    assert call(dtype=0) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(shape=(B, L, H, 32, G, N, Q)) == ssd.SSD_ERR_UNSUPPORTED
+    need = lib.ssd_chunk_scan_varlen_workspace_size(B, L, H, P, G, N, Q, 1)
+    assert need >= lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 1) + B * L * H * 4
+    assert call(ws=0) == ssd.SSD_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == ssd.SSD_ERR_WORKSPACE
+
+
+def test_block_steps_reject_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+
+    def pro(zx=0x10000, x=0x20000, shape=(4, 4096, 80, 64, 1, 128, 4), dtype=1):
+        b, l, h, p, g, n, w = shape
+        return lib.ssd_block_prologue(fake(zx) if zx else None, fake(0x30000), None, None, fake(x) if x else None,
+                                      fake(0x40000), fake(0x50000), fake(0x60000), b, l, h, p, g, n, w, dtype, None)
+    assert pro(zx=0) == ssd.SSD_ERR_INVALID_ARG
+    assert pro(x=0x20008) == ssd.SSD_ERR_INVALID_ARG                 # misaligned output
+    assert pro(shape=(4, 4096, 80, 64, 3, 128, 4)) == ssd.SSD_ERR_INVALID_ARG      # H % G
+    assert pro(shape=(4, 4096, 80, 64, 1, 128, 0)) == ssd.SSD_ERR_INVALID_ARG
+    assert pro(shape=(4, 4096, 80, 64, 1, 128, 5)) == ssd.SSD_ERR_UNSUPPORTED      # width 5
+    assert pro(shape=(4, 4096, 4, 64, 1, 128, 4)) == ssd.SSD_ERR_UNSUPPORTED       # row not a multiple of 8
+    assert pro(dtype=0) == ssd.SSD_ERR_UNSUPPORTED
+    assert pro(shape=(0, 4096, 80, 64, 1, 128, 4)) == ssd.SSD_OK                   # nothing to do
+
+    def norm(y=0x10000, w=0x30000, T=16, D=5120, zstride=5120, ngroups=1, eps=1e-5, dtype=1):
+        return lib.ssd_gated_norm(fake(y) if y else None, fake(0x20000), zstride, fake(w), None, fake(0x40000),
+                                  T, D, ngroups, eps, 1, dtype, None)
+    assert norm(y=0) == ssd.SSD_ERR_INVALID_ARG
+    assert norm(w=0x30004) == ssd.SSD_ERR_INVALID_ARG                # misaligned weight
+    assert norm(eps=-1.0) == ssd.SSD_ERR_INVALID_ARG
+    assert norm(ngroups=0) == ssd.SSD_ERR_INVALID_ARG
+    assert norm(ngroups=9) == ssd.SSD_ERR_UNSUPPORTED
+    assert norm(D=8200, zstride=8200) == ssd.SSD_ERR_UNSUPPORTED     # wider than 8192
+    assert norm(zstride=5000) == ssd.SSD_ERR_UNSUPPORTED             # stride below the row
+    assert norm(dtype=0) == ssd.SSD_ERR_UNSUPPORTED
+    assert norm(T=0) == ssd.SSD_OK
+
+
+def test_selective_scan_rejects_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+
+    def call(x=0x10000, y=0x70000, shape=(4, 4096, 5120, 1, 16), dtype=1):
+        b, l, dch, g, n = shape
+        return lib.ssd_selective_scan(fake(x) if x else None, fake(0x20000), fake(0x30000), fake(0x40000),
+                                      fake(0x50000), None, None, fake(y) if y else None, None,
+                                      b, l, dch, g, n, 1, dtype, None)
+    assert call(x=0) == ssd.SSD_ERR_INVALID_ARG
+    assert call(y=0x70002) == ssd.SSD_ERR_INVALID_ARG
+    assert call(shape=(4, 4096, 5120, 3, 16)) == ssd.SSD_ERR_INVALID_ARG   # Dch % G
+    assert call(shape=(4, 4096, 5120, 1, 12)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(shape=(4, 4096, 96, 1, 16)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(dtype=0) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(shape=(0, 4096, 5120, 1, 16)) == ssd.SSD_OK
