@@ -69,9 +69,25 @@ __device__ __forceinline__ float shfl_xor(float v, int m) {
 __device__ __forceinline__ float lane_get(float v, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(v)));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int m = 1; m < 64; m <<= 1) v += shfl_xor(v, m);
+// sum over the 16 lanes of a row with DPP (no LDS round trips): lane pairs,
+// then quads, then the two halves of each 8, then the two 8s of the row; every
+// lane of the row ends with the sum
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
     return v;
+}
+// sum over the wave, the same value in every lane (fixed order: deterministic)
+__device__ __forceinline__ float wave_sum(float v) {
+    const int r = __float_as_int(row_sum16(v));
+    return (__int_as_float(__builtin_amdgcn_readlane(r, 0)) + __int_as_float(__builtin_amdgcn_readlane(r, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(r, 32)) + __int_as_float(__builtin_amdgcn_readlane(r, 48)));
 }
 
 // ---------------------------------------------------------------------------
@@ -230,7 +246,7 @@ struct GradSmem {
     __bf16 MT[64 * S64];     // M^T [j][i]
     __bf16 QT[64 * S64];     // Q^T [j][i]
     float lam[64], dtl[64], ww[64], ee[64];
-    float zrow[64], zcolw[4][64], zrcolw[4][64], qv[64], uv[64];
+    float zrow[64], zcolw[16][64], zrcolw[16][64], qv[64], uv[64];   // column parts per (wave, lane row)
     float red[8];
 };
 
@@ -248,13 +264,7 @@ __device__ __forceinline__ bf16x8 frag_col(const __bf16 *base, int r0, int strid
     const bf16x4 lo = tr4(p), hi = tr4(p + 4 * stride * 2);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-__device__ __forceinline__ float red16(float v) {   // sum over the 16 lanes of a group
-    v += shfl_xor(v, 1);
-    v += shfl_xor(v, 2);
-    v += shfl_xor(v, 4);
-    v += shfl_xor(v, 8);
-    return v;
-}
+__device__ __forceinline__ float red16(float v) { return row_sum16(v); }   // sum over the 16 lanes of a group
 
 template <int N>
 __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
@@ -392,14 +402,8 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
             }
             *reinterpret_cast<uint2 *>(sm.MT + j * S64 + 16 * w + 4 * lgrp) = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
             *reinterpret_cast<uint2 *>(sm.QT + j * S64 + 16 * w + 4 * lgrp) = uint2{pack2(qv[0], qv[1]), pack2(qv[2], qv[3])};
-            zc += shfl_xor(zc, 16);
-            zc += shfl_xor(zc, 32);
-            zrc += shfl_xor(zrc, 16);
-            zrc += shfl_xor(zrc, 32);
-            if (lgrp == 0) {
-                sm.zcolw[w][j] = zc;
-                sm.zrcolw[w][j] = zrc;
-            }
+            sm.zcolw[4 * w + lgrp][j] = zc;
+            sm.zrcolw[4 * w + lgrp][j] = zrc;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -488,15 +492,20 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         // ---- d/dLambda per token, ddt, and this head's parts of dA, dD (wave 0)
         if (w == 0) {
             const int k = lane;
-            const float zc = sm.zcolw[0][k] + sm.zcolw[1][k] + sm.zcolw[2][k] + sm.zcolw[3][k];
-            const float zrc = sm.zrcolw[0][k] + sm.zrcolw[1][k] + sm.zrcolw[2][k] + sm.zrcolw[3][k];
+            float zc = 0.f, zrc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                zc += sm.zcolw[m][k];
+                zrc += sm.zrcolw[m][k];
+            }
             const float wk = sm.ww[k], qk = sm.qv[k];
             float dl = sm.uv[k] + sm.zrow[k] - zc - wk * qk;
             const float wq = wave_sum(wk * qk);
             const float hd = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
             if (k == 63) dl += ex2f(lend) * hd + wq;
-            // rs_k = sum over i >= k of dl_i
-            const float rs = lane_get(wave_scan(lane_get(dl, 63 - k)), 63 - k);
+            // rs_k = sum over i >= k of dl_i = total - (prefix through k) + dl_k
+            const float pre = wave_scan(dl);
+            const float rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), 63)) - pre + dl;
             const float g_dt = Ah * rs + zrc + ex2f(lend - sm.lam[k]) * qk;
             if (k < q) a.ddt[(row0 + k) * a.H + h] = g_dt;
             const float da = wave_sum(sm.dtl[k] * rs);
