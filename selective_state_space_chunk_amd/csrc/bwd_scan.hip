@@ -250,6 +250,13 @@ struct GradSmem {
     float red[8];
 };
 
+// The four values a lane's accumulator covers, (r0 + 4 lgrp + r, c0 + lrow) for
+// r = 0..3, of a row-major tile: one transposing read instead of four
+__device__ __forceinline__ bf16x4 dvals(const __bf16 *base, int r0, int c0, int stride, int lrow, int lgrp) {
+    const int a = lrow & 3, qq = lrow >> 2;
+    return tr4(reinterpret_cast<const unsigned char *>(base + (r0 + 4 * lgrp + qq) * stride + c0 + 4 * a));
+}
+
 // Fragment for the 16x16x32 products, 8 k values from k0 + 8 lgrp:
 // row-wise: element (r, k) at base[r * stride + k], r = r0 + lrow;
 __device__ __forceinline__ bf16x8 frag_row(const __bf16 *base, int r0, int stride, int k0, int lrow, int lgrp) {
@@ -429,10 +436,11 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
                 for (int kk = 0; kk < KN; ++kk)
                     vv = mfma(frag_row(sm.B, 16 * w, SN, 32 * kk, lrow, lgrp), frag_row(sm.dH, 16 * pt, SN, 32 * kk, lrow, lgrp), vv);
                 const int p = 16 * pt + lrow;
+                const bf16x4 xj = dvals(sm.X, 16 * w, 16 * pt, S64, lrow, lgrp);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * w + 4 * lgrp + r;
-                    qs[r] += (float)sm.X[j * S64 + p] * vv[r];
+                    qs[r] += (float)xj[r] * vv[r];
                     if (j < q) a.dx[((row0 + j) * a.H + h) * kP + p] = (__bf16)(dxa[r] + wj[r] * vv[r]);
                 }
             }
@@ -455,12 +463,11 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
                     c1 = mfma(frag_row(sm.Y, 16 * w, S64, 32 * kk, lrow, lgrp), frag_col(sm.H, 16 * nt, SN, 32 * kk, lrow, lgrp), c1);
                     c2 = mfma(frag_col(sm.QT, 16 * w, S64, 32 * kk, lrow, lgrp), frag_col(sm.B, 16 * nt, SN, 32 * kk, lrow, lgrp), c2);
                 }
-                const int n = 16 * nt + lrow;
+                const bf16x4 cin = dvals(sm.C, 16 * w, 16 * nt, SN, lrow, lgrp);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * w + 4 * lgrp + r;
                     const float ci = ei[r] * c1[r];
-                    us[r] += (float)sm.C[i * SN + n] * ci;
+                    us[r] += (float)cin[r] * ci;
                     dCacc[nt][r] += ci + c2[r];
                 }
             }
