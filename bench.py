@@ -682,7 +682,7 @@ def main():
         peak = VALU_LANE_SLOTS / S6_SLOTS_PER_UPDATE
         nbytes = 3 * toks * sh["channels"] * 2 + 2 * toks * sh["state"] * 2 + 2 * sh["batch"] * sh["channels"] * sh["state"] * 4
         out["s6"] = {"workload": "mamba1_2.8b_layer_selective_scan", "config": dict(sh, discretisation="zero-order hold"),
-                     "kernel": "s6_kernel<16>", "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
+                     "kernel": "s6_lane_kernel<16, true>", "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
                      "tokens_per_s": toks / (m * 1e-3),
                      "roofline": {"bound": "alu", "achieved": updates / (m * 1e-3) / 1e12, "peak": peak / 1e12,
                                   "unit": "T state updates/s", "frac": updates / (m * 1e-3) / peak,

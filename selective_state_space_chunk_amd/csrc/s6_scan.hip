@@ -182,6 +182,154 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
     }
 }
 
+// One state per lane, for N = 8 or 16: the lanes of a channel form one
+// DPP row (16 lanes) or half-row (8), so y of a token is a row sum without
+// LDS.  A workgroup takes CW = 256 / N channels of one batch row, so there
+// are many small workgroups (Dch / CW per row): five per compute unit at the
+// Mamba-1 2.8B shape, every SIMD with the same load.  x, dt, Bm and Cm of a
+// chunk are staged transposed in fp32 ([channel or state][token]), so a lane
+// reads four tokens per LDS load.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {   // over the N lanes of a channel
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror: the 8 lanes
+    if constexpr (N == 16) v += dpp_mov<0x140>(v);   // row_mirror: the 16 lanes
+    return v;
+}
+
+template <int N, bool kZoh>
+__global__ __launch_bounds__(256) void s6_lane_kernel(S6Args a) {
+    constexpr int CW = 256 / N;          // channels per workgroup
+    constexpr int TS = kT + 4;           // row of the transposed tiles (fp32)
+    constexpr int XU = kT * CW / 8;      // 16-byte units of the x (and dt) tile
+    constexpr int BU = kT * N / 8;       // 16-byte units of the Bm (and Cm) tile
+    constexpr int UN = 2 * XU + 2 * BU;  // units per chunk
+    constexpr int UPT = (UN + 255) / 256;
+    __shared__ __align__(16) float xt[2][CW][TS];
+    __shared__ __align__(16) float dtt[2][CW][TS];
+    __shared__ __align__(16) float bt[2][N][TS];
+    __shared__ __align__(16) float ct[2][N][TS];
+    __shared__ __align__(16) float yt[kT][CW];
+    const int64_t b = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * CW;
+    const int tid = threadIdx.x;
+    const int ci = tid / N, n = tid % N;
+    const int64_t c = c0 + ci;
+    const int64_t g = c0 / (a.Dch / a.G);
+    const int64_t L = a.L;
+
+    const float Av = a.A[c * N + n];
+    const float A2 = Av * kLog2e, invA = Av != 0.f ? 1.f / Av : 0.f, zf = Av != 0.f ? 0.f : 1.f;
+    float h = a.init ? a.init[(b * a.Dch + c) * N + n] : 0.f;
+
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    uint4 reg[UPT];
+    // unit u: x (u < XU), dt, Bm, Cm; row (token) and 8 columns within the tile
+    auto unit_src = [&](int u, int64_t t0, const __bf16 *&src, int64_t &off, bool &ok) __attribute__((always_inline)) {
+        int k = u, cols = CW;
+        const __bf16 *base = a.x;
+        if (k >= XU) { k -= XU; base = a.dt; }
+        if (u >= 2 * XU) { k = u - 2 * XU; cols = N; base = a.Bm; }
+        if (u >= 2 * XU + BU) { k = u - 2 * XU - BU; base = a.Cm; }
+        const int per = cols / 8;
+        const int r = k / per, col = (k % per) * 8;
+        const int64_t t = t0 + r;
+        ok = t < L;
+        const int64_t tt = ok ? t : 0;
+        off = u < 2 * XU ? (b * L + tt) * a.Dch + c0 + col : ((b * L + tt) * a.G + g) * N + col;
+        src = base;
+    };
+    auto load = [&](int64_t t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < UPT; ++m) {
+            const int u = tid + 256 * m;
+            reg[m] = zero;
+            if (u < UN) {
+                const __bf16 *src;
+                int64_t off;
+                bool ok;
+                unit_src(u, t0, src, off, ok);
+                if (ok) reg[m] = *reinterpret_cast<const uint4 *>(src + off);
+            }
+        }
+    };
+    auto bf = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); };
+    auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < UPT; ++m) {
+            const int u = tid + 256 * m;
+            if (u >= UN) continue;
+            int k = u, cols = CW;
+            float (*dst)[TS] = xt[buf];
+            if (u >= XU) { k = u - XU; dst = dtt[buf]; }
+            if (u >= 2 * XU) { k = u - 2 * XU; cols = N; dst = bt[buf]; }
+            if (u >= 2 * XU + BU) { k = u - 2 * XU - BU; dst = ct[buf]; }
+            const int per = cols / 8;
+            const int r = k / per, col = (k % per) * 8;
+            const uint32_t wv[4] = {reg[m].x, reg[m].y, reg[m].z, reg[m].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[col + e][r] = bf(wv[e >> 1], e & 1);
+        }
+    };
+
+    const int nchunks = (int)((L + kT - 1) / kT);
+    load(0);
+    stage(0);
+    if (nchunks > 1) load(kT);
+    __syncthreads();
+    for (int k = 0; k < nchunks; ++k) {
+        const int buf = k & 1;
+        const int nt = (int)(L - (int64_t)k * kT < kT ? L - (int64_t)k * kT : kT);
+#pragma unroll
+        for (int t4 = 0; t4 < kT; t4 += 4) {
+            const float4 x4 = *reinterpret_cast<const float4 *>(&xt[buf][ci][t4]);
+            const float4 d4 = *reinterpret_cast<const float4 *>(&dtt[buf][ci][t4]);
+            const float4 b4 = *reinterpret_cast<const float4 *>(&bt[buf][n][t4]);
+            const float4 c4 = *reinterpret_cast<const float4 *>(&ct[buf][n][t4]);
+            const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
+            const float bs[4] = {b4.x, b4.y, b4.z, b4.w}, cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float av = __builtin_amdgcn_exp2f(ds[e] * A2);
+                if constexpr (kZoh) {
+                    const float coef = __builtin_fmaf(zf, ds[e], __builtin_fmaf(av, invA, -invA));
+                    h = __builtin_fmaf(av, h, coef * (bs[e] * xs[e]));
+                } else {
+                    h = __builtin_fmaf(av, h, (ds[e] * xs[e]) * bs[e]);
+                }
+                const float yv = lanes_sum<N>(cs[e] * h);
+                if (n == 0) yt[t4 + e][ci] = yv;
+            }
+        }
+        __syncthreads();
+        // y rows of the chunk: CW channels (plus D x) per token, 16 bytes per thread
+        for (int u = tid; u < kT * CW / 8; u += 256) {
+            const int r = u / (CW / 8), col = (u % (CW / 8)) * 8;
+            if (r < nt) {
+                typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+                bf16x8_t ov;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dd = a.D ? a.D[c0 + col + e] : 0.f;
+                    ov[e] = (__bf16)__builtin_fmaf(dd, xt[buf][col + e][r], yt[r][col + e]);
+                }
+                *reinterpret_cast<bf16x8_t *>(a.y + (b * L + (int64_t)k * kT + r) * a.Dch + c0 + col) = ov;
+            }
+        }
+        if (k + 1 < nchunks) {
+            stage(buf ^ 1);
+            if (k + 2 < nchunks) load((int64_t)(k + 2) * kT);
+        }
+        __syncthreads();
+    }
+    if (a.final_state) a.final_state[(b * a.Dch + c) * N + n] = h;
+}
+
 }  // namespace
 
 bool s6_supported(int64_t Dch, int64_t G, int64_t N) {
@@ -194,11 +342,13 @@ hipError_t launch_s6(const void *x, const void *dt, const float *A, const void *
     S6Args a{(const __bf16 *)x, (const __bf16 *)dt, (const __bf16 *)Bm, (const __bf16 *)Cm, A, D, init,
              (__bf16 *)y, final_state, L, Dch, G, zoh ? 1 : 0};
     const dim3 grid((unsigned)(Dch / kCh), (unsigned)B);
+    // N = 8, 16: one state per lane, 256 / N channels per workgroup
+    const dim3 lgrid8((unsigned)(Dch / 32), (unsigned)B), lgrid16((unsigned)(Dch / 16), (unsigned)B);
     switch (N * 2 + (zoh ? 1 : 0)) {
-        case 16: s6_kernel<8, false><<<grid, 256, 0, stream>>>(a); break;
-        case 17: s6_kernel<8, true><<<grid, 256, 0, stream>>>(a); break;
-        case 32: s6_kernel<16, false><<<grid, 256, 0, stream>>>(a); break;
-        case 33: s6_kernel<16, true><<<grid, 256, 0, stream>>>(a); break;
+        case 16: s6_lane_kernel<8, false><<<lgrid8, 256, 0, stream>>>(a); break;
+        case 17: s6_lane_kernel<8, true><<<lgrid8, 256, 0, stream>>>(a); break;
+        case 32: s6_lane_kernel<16, false><<<lgrid16, 256, 0, stream>>>(a); break;
+        case 33: s6_lane_kernel<16, true><<<lgrid16, 256, 0, stream>>>(a); break;
         case 64: s6_kernel<32, false><<<grid, 256, 0, stream>>>(a); break;
         case 65: s6_kernel<32, true><<<grid, 256, 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
