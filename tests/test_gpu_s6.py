@@ -44,7 +44,24 @@ CASES = [
     ("n32", 1, 65, 128, 32, 1, True, True),
     ("one_token", 1, 1, 64, 16, 1, True, True),
     ("several_chunks", 1, 300, 192, 16, 3, True, True),
+    ("n8_simple_term", 1, 40, 64, 8, 1, False, True),
+    ("n32_simple_term", 1, 50, 64, 32, 1, False, False),
 ]
+
+
+@pytest.mark.parametrize("N", [16, 32])
+def test_zero_decay_states_take_the_limit(N):
+    # A = 0 for some states: the zero-order-hold term is its limit dt Bm x there
+    B, L, Dch = 1, 90, 64
+    d = si.make_s6_inputs(B, L, Dch, N, 1, init=True, seed=6401 + N)
+    d["A"][::3, ::2] = 0.0
+    f = si.as_f64(d)
+    y_ref, f_ref = selective_scan(f["x"], f["dt"], f["A"], f["Bm"], f["Cm"], f["D"], f["init"], zoh=True)
+    announce(f"selective scan with zero decays: B{B} L{L} Dch{Dch} N{N}")
+    y, fin = _gpu(_dev(d), True)
+    ey, ef = rel_err(y, y_ref), rel_err(fin, f_ref)
+    print(f"    y {ey:.3e}  final {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
