@@ -101,3 +101,22 @@ def test_backward_rejects_uncovered_shapes():
     with pytest.raises(ssd.SSDError) as ei:
         gpu_grads(dd, dg)
     assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_backward_at_the_130m_shape_sampled_heads():
+    # the Mamba-2 130M layer shape: B 8, L 2048, H 24; the oracle on three (batch, head) pairs
+    B, L, H, N = 8, 2048, 24, 128
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=True, seed=3401)
+    g = si.make_grad_inputs(B, L, H, 64, N, dtype="bf16", seed=3402)
+    announce(f"bwd at the 130M shape: B{B} L{L} H{H} N{N}, sampled heads")
+    got = gpu_grads(to_device(d, "bf16"), grad_device(g))
+    f, gf = si.as_f64(d), si.as_f64(g)
+    for b, h in ((0, 0), (3, 11), (7, 23)):
+        sl = lambda a, ax=2: np.take(a[b:b + 1], [h], axis=ax)
+        ref = recurrence_bwd(sl(f["x"]), sl(f["dt"]), f["A"][[h]], f["Bm"][b:b + 1], f["Cm"][b:b + 1], f["D"][[h]],
+                             sl(f["init"], 1), sl(gf["dy"]), sl(gf["dfinal"], 1))
+        for k, gk in (("dx", got["dx"][b:b + 1, :, h:h + 1]), ("ddt", got["ddt"][b:b + 1, :, h:h + 1]),
+                      ("dinit", got["dinit"][b:b + 1, h:h + 1])):
+            e = rel_err(to_np(gk), ref[k])
+            print(f"    b{b} h{h} {k}: {e:.3e}", flush=True)
+            assert e <= TOL["bf16"], (b, h, k, e)

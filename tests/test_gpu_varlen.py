@@ -120,3 +120,20 @@ def test_varlen_rejects_uncovered_shapes():
     with pytest.raises(ssd.SSDError) as ei:
         _gpu(dd, np.zeros((1, 70), dtype=np.int32))
     assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_varlen_at_the_130m_shape_sampled_heads():
+    # the Mamba-2 130M layer shape (B 8, L 2048, H 24: 192 sequences, one workgroup each)
+    B, L, H, N = 8, 2048, 24, 128
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=True, seed=4601)
+    seq = si.make_seq_idx(B, L, mean_len=256.0, seed=4602)
+    bh = [0 * H + 0, 3 * H + 12, 7 * H + 23]
+    y_ref, f_ref = _oracle(d, seq, bh)
+    announce(f"varlen at the 130M shape: B{B} L{L} H{H} N{N}, sampled heads")
+    y, fin = _gpu(to_device(d, "bf16"), seq)
+    y, fin = to_np(y), to_np(fin)
+    for k in bh:
+        b, h = divmod(k, H)
+        ey, ef = rel_err(y[b, :, h], y_ref[b, :, h]), rel_err(fin[b, h], f_ref[b, h])
+        print(f"    b{b} h{h}: y {ey:.3e} final {ef:.3e}", flush=True)
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (k, ey, ef)
