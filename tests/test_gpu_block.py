@@ -149,3 +149,27 @@ def test_uncovered_shapes_are_rejected():
     with pytest.raises(ssd.SSDError) as ei:
         ssd.ssd_gated_norm(y, y, torch.ones(8200, device=dev))
     assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_130m_shape_windows():
+    # the Mamba-2 130M layer shape: H 24 (HP 1536), N 128, W 4; norm in 4 groups, RMS
+    import selective_state_space_chunk_amd as ssd
+    B, L, H, P, G, N, W = 8, 2048, 24, 64, 1, 128, 4
+    b = si.make_block_inputs(B, L, H, P, G, N, W, seed=5601)
+    announce(f"block steps at the 130M shape: B{B} L{L} H{H} P{P} N{N} W{W}")
+    g = _prologue_gpu(b, H, P, G, N)
+    for t0, t1 in ((0, 40), (1000, 1040), (2008, 2048)):
+        s0 = max(0, t0 - (W - 1))
+        ref = oracle.block_prologue(b["zxbcdt"][:, s0:t1], b["conv_w"], b["conv_b"], b["dt_bias"], H, P, G, N)
+        for k in ("x", "Bm", "Cm", "dt"):
+            e = rel_err(to_np(g[k][:, t0:t1]), ref[k][:, t0 - s0:])
+            assert e <= (1e-5 if k == "dt" else TOL["bf16"]), (t0, k, e)
+    out = ssd.ssd_gated_norm(_t(b["y"], torch.bfloat16), g["z"], _t(b["norm_w"]), None, 4, 1e-5, False)
+    torch.cuda.synchronize()
+    T = B * L
+    idx = np.arange(0, T, 61)
+    z = b["zxbcdt"].reshape(T, -1)[idx, :H * P]
+    ref = oracle.gated_norm(b["y"].reshape(T, H * P)[idx], z, b["norm_w"], None, 4, 1e-5, False)
+    e = rel_err(to_np(out).reshape(T, H * P)[idx], ref)
+    print(f"    norm sampled: {e:.3e}", flush=True)
+    assert e <= TOL["bf16"], e

@@ -104,3 +104,17 @@ def test_without_tokens_and_uncovered_shapes():
         with pytest.raises(ssd.SSDError) as ei:
             _gpu(d, True)
         assert ei.value.status == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_mamba1_130m_shape_sampled_channels():
+    # Mamba-1 130M layer: d_inner 1536 channels, N 16; batch 8 of 2048 tokens
+    B, L, Dch, N = 8, 2048, 1536, 16
+    d = si.make_s6_inputs(B, L, Dch, N, 1, init=True, seed=6501)
+    ch = [0, 15, 16, 767, 1535]
+    f = si.as_f64(d)
+    y_ref, f_ref = selective_scan(f["x"], f["dt"], f["A"], f["Bm"], f["Cm"], f["D"], f["init"], zoh=True, channels=ch)
+    announce(f"selective scan at the Mamba-1 130M shape: B{B} L{L} Dch{Dch} N{N}, channels {ch}")
+    y, fin = _gpu(_dev(d), True)
+    ey, ef = rel_err(y[:, :, ch], y_ref[:, :, ch]), rel_err(fin[:, ch], f_ref[:, ch])
+    print(f"    y {ey:.3e}  final {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
