@@ -90,24 +90,36 @@ def test_gated_norm_matches_oracle(case):
 
 
 def test_block_steps_chained():
+    # The three steps chained on the GPU (prologue -> scan -> gated norm)
+    # against a chain that runs only the oracle: the oracle prologue, its x,
+    # Bm, Cm rounded to bfloat16 and dt to float32 as the GPU stores them, the
+    # oracle scan, its y rounded to bfloat16, the oracle norm.  No value of the
+    # GPU chain enters the reference.
     import selective_state_space_chunk_amd as ssd
     B, L, H, P, G, N, W = 2, 300, 8, 64, 1, 128, 4
     b = si.make_block_inputs(B, L, H, P, G, N, W, seed=5301)
     A = -np.exp(np.random.default_rng(5302).uniform(-1.0, 1.5, H)).astype(np.float32)
     D = np.random.default_rng(5303).standard_normal(H).astype(np.float32)
     pro = oracle.block_prologue(b["zxbcdt"], b["conv_w"], b["conv_b"], b["dt_bias"], H, P, G, N)
-    announce(f"block chain: prologue, scan, gated norm; B{B} L{L} H{H} P{P} N{N}")
-    g = _prologue_gpu(b, H, P, G, N)
-    # the scan oracle takes the GPU prologue's own bfloat16 outputs, so that the
-    # comparison of the chain isolates the scan and the norm
-    xg, Bg, Cg, dtg = (to_np(g[k]) for k in ("x", "Bm", "Cm", "dt"))
-    assert rel_err(xg, pro["x"]) <= TOL["bf16"]
-    y_ref, _ = oracle.recurrence(xg, dtg, A, Bg, Cg, D, None)
+    xr, Br, Cr = (si.round_bf16(pro[k]).astype(np.float64) for k in ("x", "Bm", "Cm"))
+    dtr = pro["dt"].astype(np.float32).astype(np.float64)
+    y_ref, _ = oracle.recurrence(xr, dtr, A.astype(np.float64), Br, Cr, D.astype(np.float64), None)
     out_ref = oracle.gated_norm(si.round_bf16(y_ref).reshape(B * L, H * P), pro["z"].reshape(B * L, H * P),
                                 b["norm_w"], b["norm_b"], 1, 1e-5, True)
+    announce(f"block chain: prologue, scan, gated norm; B{B} L{L} H{H} P{P} N{N}")
+    g = _prologue_gpu(b, H, P, G, N)
+    for k in ("x", "Bm", "Cm"):
+        e = rel_err(to_np(g[k]), pro[k])
+        print(f"    prologue {k}: {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (k, e)
+    e = rel_err(to_np(g["dt"]), pro["dt"])
+    assert e <= 1e-5, ("dt", e)
     y, _ = ssd.ssd_chunk_scan_fwd(g["x"], g["dt"], _t(A), g["Bm"], g["Cm"], _t(D), None)
     out = ssd.ssd_gated_norm(y, g["z"], _t(b["norm_w"]), _t(b["norm_b"]), 1, 1e-5, True)
     torch.cuda.synchronize()
+    e = rel_err(to_np(y), y_ref)
+    print(f"    scan y: {e:.3e}", flush=True)
+    assert e <= TOL["bf16"], e
     e = rel_err(to_np(out).reshape(B * L, H * P), out_ref)
     print(f"    out: {e:.3e}", flush=True)
     assert e <= TOL["bf16"], e

@@ -49,6 +49,12 @@ CASES = [
     ("one_token", 2, 1, 2, 128, 1, True, True, "default"),
     ("long_memory_many_blocks", 1, 1100, 2, 128, 1, True, True, "long_memory"),
     ("no_decay", 1, 260, 2, 64, 1, True, True, "no_decay"),
+    # the head counts per group of the layer shapes: dBm and dCm are summed over
+    # every head of a group in matrix-core accumulators, dA and dD over tokens
+    ("eighty_heads_one_group", 1, 300, 80, 128, 1, True, True, "default"),
+    ("twenty_four_heads_one_group", 2, 140, 24, 128, 1, True, False, "default"),
+    ("five_heads_one_group", 2, 200, 5, 128, 1, True, True, "default"),
+    ("three_heads_per_group", 1, 180, 6, 64, 2, True, True, "long_memory"),
 ]
 
 
@@ -120,3 +126,37 @@ def test_backward_at_the_130m_shape_sampled_heads():
             e = rel_err(to_np(gk), ref[k])
             print(f"    b{b} h{h} {k}: {e:.3e}", flush=True)
             assert e <= TOL["bf16"], (b, h, k, e)
+
+
+def test_backward_at_the_2p7b_shape_sampled_heads():
+    # the Mamba-2 2.7B layer shape the bench times: B 4, L 4096, H 80, N 128,
+    # one group, a random initial state.  The oracle runs on sampled (batch,
+    # head) pairs for dx, ddt and dinit, and on every batch row of two heads
+    # for dA and dD (summed over batch rows and tokens).  dBm and dCm sum over
+    # all 80 heads; they are compared at 80 heads per group in
+    # eighty_heads_one_group above.
+    B, L, H, N = 4, 4096, 80, 128
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=True, seed=3501)
+    g = si.make_grad_inputs(B, L, H, 64, N, dtype="bf16", seed=3502)
+    announce(f"bwd at the 2.7B shape: B{B} L{L} H{H} N{N}, sampled heads")
+    got = gpu_grads(to_device(d, "bf16"), grad_device(g))
+    f, gf = si.as_f64(d), si.as_f64(g)
+    for b, h in ((0, 0), (2, 41), (3, 79)):
+        sl = lambda a, ax=2: np.take(a[b:b + 1], [h], axis=ax)
+        ref = recurrence_bwd(sl(f["x"]), sl(f["dt"]), f["A"][[h]], f["Bm"][b:b + 1], f["Cm"][b:b + 1], f["D"][[h]],
+                             sl(f["init"], 1), sl(gf["dy"]), sl(gf["dfinal"], 1))
+        for k, gk in (("dx", got["dx"][b:b + 1, :, h:h + 1]), ("ddt", got["ddt"][b:b + 1, :, h:h + 1]),
+                      ("dinit", got["dinit"][b:b + 1, h:h + 1])):
+            e = rel_err(to_np(gk), ref[k])
+            print(f"    b{b} h{h} {k}: {e:.3e}", flush=True)
+            assert e <= TOL["bf16"], (b, h, k, e)
+    # dA and dD of the sampled heads as one tensor each (the metric's scale is
+    # the largest magnitude over the sampled heads)
+    heads = [7, 66]
+    sl = lambda a, ax=2: np.take(a, heads, axis=ax)
+    ref = recurrence_bwd(sl(f["x"]), sl(f["dt"]), f["A"][heads], f["Bm"], f["Cm"], f["D"][heads],
+                         sl(f["init"], 1), sl(gf["dy"]), sl(gf["dfinal"], 1))
+    for k in ("dA", "dD"):
+        e = rel_err(to_np(got[k][heads]), ref[k])
+        print(f"    heads {heads} {k}: {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (k, e)
