@@ -81,7 +81,8 @@ typedef enum {
     SSD_ALGO_FUSED = 3,       /* bf16 matrix cores, one pass: states handed from block to block */
     SSD_ALGO_CHAIN = 4,       /* bf16 matrix cores, one workgroup per (batch, head) sequence */
     SSD_ALGO_PIPE = 5,        /* as CHAIN, eight waves in two roles (state / outputs) per sequence */
-    SSD_ALGO_PAIR = 6         /* as CHAIN, one workgroup per two adjacent heads sharing Bm / Cm */
+    SSD_ALGO_PAIR = 6,        /* as CHAIN, one workgroup per two adjacent heads sharing Bm / Cm */
+    SSD_ALGO_DUO = 7          /* one workgroup per two adjacent heads of a group, whole sequence */
 } ssd_algo;
 
 /* Human-readable name of a status code (static storage). */

@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libssd.so")
 
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
-ALGOS = {"auto": 0, "reference": 1, "staged": 2, "fused": 3, "chain": 4, "pipe": 5, "pair": 6}
+ALGOS = {"auto": 0, "reference": 1, "staged": 2, "fused": 3, "chain": 4, "pipe": 5, "pair": 6, "duo": 7}
 
 _lib = None
 

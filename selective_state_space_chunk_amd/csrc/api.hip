@@ -31,6 +31,8 @@ hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, cons
 bool pipe_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pair_scan(const ScanArgs &a, const Workspace &ws);
 bool pair_supported(int64_t H, int64_t G, int64_t N);
+bool duo_supported(int64_t H, int64_t G, int64_t N, int kh);
+hipError_t launch_duo_scan(const ScanArgs &a, int kh);
 bool bwd_supported(int64_t P, int64_t N, int64_t H, int64_t G);
 size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t N);
 hipError_t launch_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
@@ -157,16 +159,18 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
-        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE && algo != SSD_ALGO_PAIR)
+        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE && algo != SSD_ALGO_PAIR &&
+        algo != SSD_ALGO_DUO)
         return SSD_ERR_UNSUPPORTED;
     const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
     if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN || algo == SSD_ALGO_PIPE ||
-         algo == SSD_ALGO_PAIR) &&
+         algo == SSD_ALGO_PAIR || algo == SSD_ALGO_DUO) &&
         !mfma_ok)
         return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_CHAIN && !chain_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_PIPE && !pipe_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_PAIR && !pair_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
+    if (algo == SSD_ALGO_DUO && !duo_supported(H, G, N, 2)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && !fused_supported(H, G, N, Q)) return SSD_ERR_UNSUPPORTED;
     if (algo == SSD_ALGO_FUSED && B * H * ((L + Q - 1) / Q) > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
 
@@ -213,6 +217,7 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
         case SSD_ALGO_CHAIN: e = launch_chain_scan(a, ws); break;
         case SSD_ALGO_PIPE: e = launch_pipe_scan(a, ws); break;
         case SSD_ALGO_PAIR: e = launch_pair_scan(a, ws); break;
+        case SSD_ALGO_DUO: e = launch_duo_scan(a, 2); break;
         default: return SSD_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

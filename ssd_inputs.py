@@ -127,6 +127,12 @@ def make_scan_inputs(B: int, L: int, H: int, P: int, N: int, G: int = 1, *,
     * ``"long_memory"``: dt ~ U(0.3, 1.5), A_h = -U(0.05, 0.5) -- slow decay,
       so errors in the state passed between chunks are not hidden by forgetting.
     * ``"no_decay"``: A = 0 -- states are passed at full magnitude.
+    * ``"decay_bursts"``: the default distributions, with dt multiplied by 40
+      inside random 96-token stretches (about a quarter of every row and head):
+      stretches where the state is all but erased within a few tokens, next
+      to ordinary ones.
+    * ``"strong_decay"``: dt ~ U(0.3, 1.5), A_h = -U(1, 16) -- every step
+      forgets most of the state.
     """
     if H % G:
         raise ValueError("H must be a multiple of G")
@@ -144,6 +150,18 @@ def make_scan_inputs(B: int, L: int, H: int, P: int, N: int, G: int = 1, *,
     elif regime == "no_decay":
         dt = _softplus(_rng(seed, "dt").standard_normal((B, L, H)) - 4.0)
         A = np.zeros(H)
+    elif regime == "decay_bursts":
+        r = _rng(seed, "dt")
+        dt = _softplus(r.standard_normal((B, L, H)) - 4.0)
+        A = -np.exp(_rng(seed, "A").uniform(math.log(1.0), math.log(16.0), H))
+        nb = max(1, L // 384)
+        for b in range(B):
+            for h in range(H):
+                for s0 in r.integers(0, max(1, L), nb):
+                    dt[b, s0:s0 + 96, h] *= 40.0
+    elif regime == "strong_decay":
+        dt = _rng(seed, "dt").uniform(0.3, 1.5, (B, L, H))
+        A = -_rng(seed, "A").uniform(1.0, 16.0, H)
     else:
         raise ValueError(f"unknown regime {regime!r}")
     out["dt"] = np.ascontiguousarray(dt, dtype=np.float32)

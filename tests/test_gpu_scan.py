@@ -11,12 +11,14 @@ from gpu_util import TOL, announce, gpu_scan, oracle_scan, rel_err, to_device, t
 
 pytestmark = pytest.mark.gpu
 
-MFMA_ALGOS = ["reference", "staged", "fused", "chain", "pipe", "pair"]
+MFMA_ALGOS = ["reference", "staged", "fused", "chain", "pipe", "pair", "duo"]
 
 
 def covers(algo, H, G):
     """The pair algorithm takes heads two at a time within one group."""
-    return algo != "pair" or (H % 2 == 0 and (H // G) % 2 == 0)
+    if algo in ("pair", "duo"):
+        return H % 2 == 0 and (H // G) % 2 == 0
+    return True
 
 # (name, B, L, H, P, N, G, chunk, dtype, init, regime, algos)
 SMALL = [
@@ -30,6 +32,11 @@ SMALL = [
     ("bf16_no_decay_groups_n256", 2, 513, 4, 64, 256, 2, 128, "bf16", True, "no_decay", ["reference", "staged", "auto"]),
     ("bf16_long_memory_n128_q128", 2, 777, 6, 64, 128, 3, 128, "bf16", True, "long_memory", MFMA_ALGOS),
     ("bf16_many_chunks", 1, 4100, 2, 64, 128, 1, 64, "bf16", True, "long_memory", MFMA_ALGOS),
+    # sub-blocks whose decay underflows a factored form, next to ordinary ones
+    ("bf16_decay_bursts", 2, 1500, 4, 64, 128, 1, 256, "bf16", True, "decay_bursts", MFMA_ALGOS),
+    ("bf16_strong_decay_n64_groups", 1, 700, 4, 64, 64, 2, 64, "bf16", True, "strong_decay", MFMA_ALGOS),
+    # long runs of ordinary decay (the state's scale factor is renormalised)
+    ("bf16_default_long", 1, 3000, 2, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
 ]
 
 

@@ -105,8 +105,9 @@ def test_four_token_walkthrough_one_step_at_a_time():
     announce("four-token walkthrough through ssd_step, fp32, P16 N16")
     ys = []
     for t in range(4):
-        y = ssd.ssd_step(state, d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
-                         d["Bm"][:, t].contiguous(), d["Cm"][:, t].contiguous(), d["D"])
+        # fresh (16-byte aligned) tensors for the one token's inputs
+        y = ssd.ssd_step(state, d["x"][:, t].clone(), d["dt"][:, t].clone(), d["A"],
+                         d["Bm"][:, t].clone(), d["Cm"][:, t].clone(), d["D"])
         torch.cuda.synchronize()
         ys.append(float(y[0, 0, 0]))
     ye = np.array(fx["y_printed_recurrence"])
