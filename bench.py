@@ -133,7 +133,7 @@ def time_scan(w, steps, warmup, device):
     import selective_state_space_chunk_amd as ssd
     sets = make_device_sets(w, 3, device)
     nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def run(k):
         s = sets[k % len(sets)]
@@ -155,7 +155,6 @@ def time_scan(w, steps, warmup, device):
     torch.cuda.synchronize(device)
     wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms
-    ssd.ssd_chunk_scan_workspace_check(ws, w.B, w.L, w.H, w.P, w.G, w.N, w.chunk)
     return wall, per
 
 
@@ -504,7 +503,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_fetch, "write_scale_bytes_per_kib": f_write, "kernels": {}}
     total = 0.0
-    for name in ("pipe_kernel", "prep_kernel", "seg_state_kernel", "chain_kernel", "scan_fused", "gram_kernel", "scan_mfma", "ref_"):
+    for name in ("pipe_kernel", "prep_kernel", "gram_kernel", "scan_mfma", "ref_"):
         try:
             fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
             wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)

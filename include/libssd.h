@@ -73,16 +73,14 @@ typedef enum {
 } ssd_dtype;
 
 /* Which kernel sequence evaluates the chunk scan.  All give the same result
- * up to rounding.  SSD_ALGO_AUTO picks by shape and dtype. */
+ * up to rounding.  SSD_ALGO_AUTO picks by shape and dtype: SSD_ALGO_PIPE
+ * wherever it covers the shape, else SSD_ALGO_STAGED for the other bfloat16
+ * shapes with P == 64, else SSD_ALGO_REFERENCE. */
 typedef enum {
     SSD_ALGO_AUTO = 0,
     SSD_ALGO_REFERENCE = 1,   /* float32 vector arithmetic, three kernels, every supported shape */
     SSD_ALGO_STAGED = 2,      /* bf16 matrix cores: block states, state pass, block outputs */
-    SSD_ALGO_FUSED = 3,       /* bf16 matrix cores, one pass: states handed from block to block */
-    SSD_ALGO_CHAIN = 4,       /* bf16 matrix cores, one workgroup per (batch, head) sequence */
-    SSD_ALGO_PIPE = 5,        /* as CHAIN, eight waves in two roles (state / outputs) per sequence */
-    SSD_ALGO_PAIR = 6,        /* as CHAIN, one workgroup per two adjacent heads sharing Bm / Cm */
-    SSD_ALGO_DUO = 7          /* one workgroup per two adjacent heads of a group, whole sequence */
+    SSD_ALGO_PIPE = 3         /* bf16 matrix cores, one workgroup walks each (batch, head) sequence */
 } ssd_algo;
 
 /* Human-readable name of a status code (static storage). */
@@ -92,17 +90,28 @@ const char *ssd_status_string(ssd_status status);
 const char *ssd_version(void);
 
 /*
- * Bytes of device workspace ssd_chunk_scan_fwd needs for this shape (with
- * SSD_ALGO_AUTO; every algorithm fits in it).  Returns 0 when the shape is
- * not supported.  The workspace holds per-block states (scratch) and the
- * hand-off flags and counters of SSD_ALGO_FUSED.  It must be ZERO-FILLED once
- * before its first use; every call leaves the flags and counters at zero when
- * its kernels finish, so one workspace serves any sequence of calls.  Calls
- * sharing a workspace must be ordered on one stream (they would race
- * otherwise).
+ * Bytes of device workspace ssd_chunk_scan_fwd needs for this shape: that of
+ * the algorithm SSD_ALGO_AUTO runs (ssd_chunk_scan_workspace_size_algo with
+ * SSD_ALGO_AUTO).  Returns 0 when the shape is not supported.
  */
 size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                      int64_t N, int64_t chunk_size, ssd_dtype dtype);
+
+/*
+ * Bytes of device workspace ssd_chunk_scan_fwd_algo needs with `algo`, 0 when
+ * `algo` does not cover the shape or dtype.  The workspace is scratch that
+ * every call writes before it reads: SSD_ALGO_PIPE keeps the Cm.Bm^T tiles of
+ * every 64-token sub-block (B*G*ceil(L/64)*64*64 bfloat16) and the states of
+ * the time segments it cuts sequences into (at most 256 of P*N + 1 floats);
+ * SSD_ALGO_STAGED and SSD_ALGO_REFERENCE keep the state and decay of every
+ * block (B*ceil(L/chunk_size)*H*(P*N + 1) floats), SSD_ALGO_STAGED also the
+ * Cm.Bm^T tiles.  It needs no initialisation.  Calls that share a workspace
+ * must be ordered (one stream, or synchronised): two calls in flight on one
+ * workspace race.
+ */
+size_t ssd_chunk_scan_workspace_size_algo(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                          int64_t N, int64_t chunk_size, ssd_dtype dtype,
+                                          ssd_algo algo);
 
 /*
  * Chunked SSD scan, forward.
@@ -118,6 +127,7 @@ size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
  *   final_state  [B, H, P, N]   float32      state after token L-1, or NULL to skip;
  *                                            may alias init_state
  *   workspace    device memory of at least ssd_chunk_scan_workspace_size(...) bytes
+ *                (contents need no initialisation and are not kept)
  *
  * Errors: SSD_ERR_INVALID_ARG for a null required pointer, a misaligned
  * pointer or a negative size; SSD_ERR_UNSUPPORTED outside the support matrix;
@@ -132,16 +142,15 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               int64_t chunk_size, ssd_dtype dtype, hipStream_t stream);
 
 /*
- * As ssd_chunk_scan_fwd, with the kernel sequence chosen by the caller.  An
+ * As ssd_chunk_scan_fwd, with the kernel sequence chosen by the caller and a
+ * workspace of ssd_chunk_scan_workspace_size_algo(..., algo) bytes.  An
  * algorithm that does not cover the shape or dtype returns
- * SSD_ERR_UNSUPPORTED (the matrix-core algorithms need SSD_DTYPE_BF16 and
- * P == 64; SSD_ALGO_STAGED takes N in {64, 128, 256}, SSD_ALGO_FUSED,
- * SSD_ALGO_CHAIN, SSD_ALGO_PIPE and SSD_ALGO_PAIR N in {64, 128}; SSD_ALGO_PAIR
- * also needs H and H / G even).  SSD_ALGO_CHAIN, SSD_ALGO_PIPE and
- * SSD_ALGO_PAIR walk every (batch, head) sequence in 64-token steps whatever
- * chunk_size is (the result is the same up to rounding).  SSD_ALGO_PIPE spreads
- * few sequences over the device in time segments; SSD_ALGO_AUTO picks it
- * wherever it covers the shape.
+ * SSD_ERR_UNSUPPORTED: SSD_ALGO_STAGED and SSD_ALGO_PIPE need SSD_DTYPE_BF16
+ * and P == 64; SSD_ALGO_STAGED takes N in {64, 128, 256}, SSD_ALGO_PIPE N in
+ * {64, 128}.  SSD_ALGO_PIPE walks every (batch, head) sequence in 64-token
+ * sub-blocks whatever chunk_size is (the result is the same up to rounding)
+ * and spreads sequences over the device's compute units in time segments
+ * when there are fewer of them than compute units, or fewer than twice as many.
  */
 ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *A,
                                    const void *Bm, const void *Cm, const float *D,
@@ -162,8 +171,8 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
  * last token, that of its last sequence.  Other arguments and layouts as
  * ssd_chunk_scan_fwd; dt must be non-negative (its magnitude is used).
  * Covered: bfloat16, P = 64, N = 64 or 128 (else SSD_ERR_UNSUPPORTED).
- * The workspace (size from ssd_chunk_scan_varlen_workspace_size, which is
- * larger than the plain scan's by B*L*H floats) is owned by the caller;
+ * The workspace (size from ssd_chunk_scan_varlen_workspace_size: that of
+ * SSD_ALGO_PIPE plus B*L*H floats) is owned by the caller;
  * asynchronous on `stream`; no allocation.
  */
 size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
@@ -234,20 +243,6 @@ ssd_status ssd_selective_scan(const void *x, const void *dt, const float *A, con
                               const void *Cm, const float *D, const float *init_state, void *y,
                               float *final_state, int64_t B, int64_t L, int64_t Dch, int64_t G,
                               int64_t N, int zoh, ssd_dtype dtype, hipStream_t stream);
-
-/*
- * Diagnostic: waits for `stream`, then checks the hand-off state that
- * SSD_ALGO_FUSED keeps in this workspace: no block-to-block hand-off ever gave
- * up waiting (a bounded wait that is never expected to expire; when it does,
- * outputs of that call are wrong), and the work counters and the hand-off flags
- * of the B*H (batch, head) chains are back at zero, as every completed call
- * leaves them.  Returns SSD_OK when all hold, SSD_ERR_HIP when one does not or
- * a HIP call failed; clears the expired-wait indicator.  Same shape arguments
- * as the scan.  Meant for tests and debugging: it synchronizes and copies.
- */
-ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes,
-                                          int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
-                                          int64_t N, int64_t chunk_size, hipStream_t stream);
 
 /*
  * Bytes of device workspace ssd_chunk_scan_bwd needs for this shape: the

@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libssd.so")
 
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
-ALGOS = {"auto": 0, "reference": 1, "staged": 2, "fused": 3, "chain": 4, "pipe": 5, "pair": 6, "duo": 7}
+ALGOS = {"auto": 0, "reference": 1, "staged": 2, "pipe": 3}
 
 _lib = None
 
@@ -61,13 +61,13 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_version.restype = ctypes.c_char_p
     lib.ssd_chunk_scan_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_workspace_size.restype = sz
+    lib.ssd_chunk_scan_workspace_size_algo.argtypes = [i64] * 7 + [ctypes.c_int, ctypes.c_int]
+    lib.ssd_chunk_scan_workspace_size_algo.restype = sz
     scan_args = [vp] * 10 + [sz] + [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_fwd.argtypes = scan_args + [vp]
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_algo.argtypes = scan_args + [ctypes.c_int, vp]
     lib.ssd_chunk_scan_fwd_algo.restype = ctypes.c_int
-    lib.ssd_chunk_scan_workspace_check.argtypes = [vp, sz] + [i64] * 7 + [vp]
-    lib.ssd_chunk_scan_workspace_check.restype = ctypes.c_int
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ssd_step.restype = ctypes.c_int
     lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
@@ -110,9 +110,12 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream(device: torch.device, stream=None):
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def _stream_handle(device: torch.device, stream=None):
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream(device, stream).cuda_stream)
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None:
@@ -127,21 +130,32 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None
 
 
 def ssd_chunk_scan_workspace_size(B: int, L: int, H: int, P: int, G: int, N: int,
-                                  chunk_size: int, dtype: torch.dtype) -> int:
-    return int(load_library().ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size,
-                                                            _dtype_code(dtype)))
+                                  chunk_size: int, dtype: torch.dtype, algo: str = "auto") -> int:
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}")
+    return int(load_library().ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, chunk_size,
+                                                                 _dtype_code(dtype), ALGOS[algo]))
 
 
 _workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
-def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
-    """A zero-filled device workspace of at least ``nbytes``, cached per device
-    (calls leave its flags zeroed, so it is reused across calls on one stream)."""
-    key = (device.index if device.index is not None else torch.cuda.current_device(), 0)
+def workspace(nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
+    """A device workspace of at least ``nbytes``, cached per (device, stream).
+
+    The library writes its scratch before reading it, so the bytes need no
+    initialisation.  Calls on one stream run in order and can share one
+    workspace; calls on two streams get two.  The tensor is allocated with
+    that stream current, so when a larger one replaces it, the caching
+    allocator hands its memory out again only to work ordered after the
+    stream's earlier kernels."""
+    s = _stream(device, stream)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -178,12 +192,12 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
     elif final_state is not None:
         _need(final_state, "final_state", torch.float32, (Bsz, H, P, N), dev)
     code = _dtype_code(x.dtype)
-    need = int(lib.ssd_chunk_scan_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
-    if workspace_tensor is None:
-        workspace_tensor = workspace(need, dev) if need > 0 else None
-    ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
     if algo not in ALGOS:
         raise ValueError(f"algo must be one of {sorted(ALGOS)}")
+    need = int(lib.ssd_chunk_scan_workspace_size_algo(Bsz, L, H, P, G, N, chunk_size, code, ALGOS[algo]))
+    if workspace_tensor is None:
+        workspace_tensor = workspace(need, dev, stream) if need > 0 else None
+    ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
     st = lib.ssd_chunk_scan_fwd_algo(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y),
         _ptr(final_state), _ptr(workspace_tensor), ws_bytes, Bsz, L, H, P, G, N, chunk_size, code,
@@ -227,7 +241,7 @@ def ssd_chunk_scan_fwd_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor
     code = _dtype_code(x.dtype)
     need = int(lib.ssd_chunk_scan_varlen_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
     if workspace_tensor is None:
-        workspace_tensor = workspace(need, dev) if need > 0 else None
+        workspace_tensor = workspace(need, dev, stream) if need > 0 else None
     ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
     st = lib.ssd_chunk_scan_fwd_varlen(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(seq_idx), _ptr(y),
@@ -333,17 +347,6 @@ def ssd_selective_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
     return y, final
 
 
-def ssd_chunk_scan_workspace_check(workspace_tensor: torch.Tensor, B: int, L: int, H: int, P: int,
-                                   G: int, N: int, chunk_size: int, stream=None) -> None:
-    """Raise unless the one-pass hand-off state in this workspace is clean: no
-    hand-off ever gave up waiting, and the counters and flags are back at zero."""
-    lib = load_library()
-    nbytes = workspace_tensor.numel() * workspace_tensor.element_size()
-    st = lib.ssd_chunk_scan_workspace_check(_ptr(workspace_tensor), nbytes, B, L, H, P, G, N,
-                                            chunk_size, _stream_handle(workspace_tensor.device, stream))
-    _check(st, "ssd_chunk_scan_workspace_check")
-
-
 def ssd_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
              Bm: torch.Tensor, Cm: torch.Tensor, D: torch.Tensor, *,
              y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -416,7 +419,8 @@ def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
     code = _dtype_code(x.dtype)
     need = int(lib.ssd_chunk_scan_bwd_workspace_size(Bsz, L, H, P, G, N, chunk_size, code))
     if workspace_tensor is None and need > 0:
-        workspace_tensor = torch.empty(need, dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(_stream(dev, stream)):
+            workspace_tensor = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace_tensor is None else workspace_tensor.numel() * workspace_tensor.element_size()
     st = lib.ssd_chunk_scan_bwd(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),

@@ -3,19 +3,14 @@
 #include "libssd.h"
 #include "common.h"
 
-#include <vector>
-
 #include <hip/hip_runtime.h>
 
 namespace ssd {
 hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws);
-hipError_t launch_fused_scan(const ScanArgs &a, const Workspace &ws);
 bool mfma_supported(int64_t P, int64_t N, int64_t Q);
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
-bool fused_supported(int64_t H, int64_t G, int64_t N, int64_t Q);
-hipError_t launch_chain_scan(const ScanArgs &a, const Workspace &ws);
-bool chain_supported(int64_t H, int64_t G, int64_t N);
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
+bool pipe_supported(int64_t H, int64_t G, int64_t N);
 bool block_prologue_supported(int64_t HP, int64_t GN, int64_t H, int64_t W);
 hipError_t launch_block_prologue(const void *zx, const float *conv_w, const float *conv_b, const float *dt_bias,
                                  void *x, void *Bm, void *Cm, float *dt, int64_t B, int64_t L, int64_t H,
@@ -28,11 +23,6 @@ hipError_t launch_s6(const void *x, const void *dt, const float *A, const void *
 hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, const float *w, const float *bias,
                              void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
                              hipStream_t stream);
-bool pipe_supported(int64_t H, int64_t G, int64_t N);
-hipError_t launch_pair_scan(const ScanArgs &a, const Workspace &ws);
-bool pair_supported(int64_t H, int64_t G, int64_t N);
-bool duo_supported(int64_t H, int64_t G, int64_t N, int kh);
-hipError_t launch_duo_scan(const ScanArgs &a, int kh);
 bool bwd_supported(int64_t P, int64_t N, int64_t H, int64_t G);
 size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t N);
 hipError_t launch_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
@@ -59,36 +49,62 @@ bool shape_supported(int64_t P, int64_t N, int64_t Q) {
     return pow2_in(P, 16, 128) && pow2_in(N, 16, 256) && pow2_in(Q, 64, 256);
 }
 
+// Workspace regions of one call: only those the chosen kernels use.
 struct Layout {
-    size_t states, decay, flags, counters, ring, gram, total;
-    size_t ring_floats;
+    size_t states, decay, seg, gram, total;
+    size_t seg_floats;
 };
 
-// Segment states the workspace holds for the per-sequence scan.
+// Most segment states the per-sequence scan keeps: it cuts sequences into at
+// most as many segments as the device has compute units (256 on MI355X).
 constexpr int64_t kSegStates = 256;
 
-// Most (batch, head) chains the hand-off flags cover; scans are limited to it.
+// Most (batch, head) sequences of one chunk-scan call.
 constexpr int64_t kMaxChains = 65535;
 
-// Byte offsets of each workspace region.  The counters and flags sit at the
-// same offsets for every shape, ahead of all scratch, so that they are never
-// overwritten by another call's scratch and stay zero between calls.
-Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t Q) {
+// The algorithm a call runs: `algo` itself, or for SSD_ALGO_AUTO the
+// per-sequence scan wherever it covers the shape, the staged matrix-core scan
+// for the other bfloat16 shapes with P = 64, and the float32 reference
+// otherwise.  -1 when `algo` does not cover the shape or dtype.
+int resolve(int64_t H, int64_t P, int64_t G, int64_t N, int64_t Q, ssd_dtype dtype, ssd_algo algo) {
+    const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
+    switch (algo) {
+        case SSD_ALGO_AUTO:
+            if (!mfma_ok) return SSD_ALGO_REFERENCE;
+            return pipe_supported(H, G, N) ? SSD_ALGO_PIPE : SSD_ALGO_STAGED;
+        case SSD_ALGO_REFERENCE: return SSD_ALGO_REFERENCE;
+        case SSD_ALGO_STAGED: return mfma_ok ? SSD_ALGO_STAGED : -1;
+        case SSD_ALGO_PIPE: return mfma_ok && pipe_supported(H, G, N) ? SSD_ALGO_PIPE : -1;
+    }
+    return -1;
+}
+
+// Byte offsets of each region for a resolved algorithm:
+//  - reference and staged: the state of every block [B, nc, H, P, N] and its
+//    decay [B, H, nc] (float32), and for staged the gram tiles of every block;
+//  - per-sequence: the gram tiles of every 64-token sub-block and room for
+//    the segment states (P*N floats and one log2 decay each) of the
+//    sequences it cuts into time segments.
+Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t Q, int algo) {
     Layout l{};
-    const int64_t nc = (L + Q - 1) / Q;
+    const int64_t nc = (L + Q - 1) / Q, nsb = (L + 63) / 64;
     size_t off = 0;
-    l.counters = off; off = align_up(off + 4 * sizeof(unsigned));
-    l.flags = off;    off = align_up(off + (size_t)kMaxChains * sizeof(unsigned));
-    l.states = off;   off = align_up(off + (size_t)(B * nc * H * P * N) * sizeof(float));
-    l.decay = off;    off = align_up(off + (size_t)(B * H * nc) * sizeof(float));
-    // the ring also holds the segment states of the per-sequence matrix-core
-    // scan (P = 64, N <= 128): room for 256 of them, one per compute unit
-    const int64_t seg_floats = (P == 64 && (N == 64 || N == 128)) ? kSegStates * (P * N + 1) : 0;
-    const int64_t ring_floats = B * H * 2 * P * N > seg_floats ? B * H * 2 * P * N : seg_floats;
-    l.ring = off;     off = align_up(off + (size_t)ring_floats * sizeof(float));
-    l.ring_floats = (size_t)ring_floats;
-    l.gram = off;     off = align_up(off + gram_bytes(B, L, G, Q));
-    l.total = off;
+    if (algo == SSD_ALGO_REFERENCE || algo == SSD_ALGO_STAGED) {
+        l.states = off; off = align_up(off + (size_t)(B * nc * H * P * N) * sizeof(float));
+        l.decay = off;  off = align_up(off + (size_t)(B * H * nc) * sizeof(float));
+    }
+    if (algo == SSD_ALGO_STAGED) {
+        l.gram = off; off = align_up(off + gram_bytes(B, L, G, Q));
+    }
+    if (algo == SSD_ALGO_PIPE) {
+        const int64_t cut = B * H * (nsb > 1 ? nsb - 1 : 0);
+        const int64_t nseg = cut < kSegStates ? cut : kSegStates;
+        l.seg_floats = (size_t)(nseg * (P * N + 1));
+        l.seg = off;  off = align_up(off + l.seg_floats * sizeof(float));
+        l.gram = off; off = align_up(off + gram_bytes(B, L, G, 64));
+    }
+    // never zero for a supported shape, so that a zero size means "not supported"
+    l.total = off > 0 ? off : kAlign;
     return l;
 }
 
@@ -97,10 +113,8 @@ Workspace carve(void *base, const Layout &l) {
     Workspace w;
     w.states = (float *)(p + l.states);
     w.decay = (float *)(p + l.decay);
-    w.flags = (unsigned *)(p + l.flags);
-    w.counters = (unsigned *)(p + l.counters);
-    w.ring = (float *)(p + l.ring);
-    w.ring_floats = l.ring_floats;
+    w.seg = (float *)(p + l.seg);
+    w.seg_floats = l.seg_floats;
     w.gram = (void *)(p + l.gram);
     return w;
 }
@@ -158,23 +172,9 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
     if (!shape_supported(P, N, Q)) return SSD_ERR_UNSUPPORTED;
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + Q - 1) / Q > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
-    if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_REFERENCE && algo != SSD_ALGO_STAGED &&
-        algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHAIN && algo != SSD_ALGO_PIPE && algo != SSD_ALGO_PAIR &&
-        algo != SSD_ALGO_DUO)
-        return SSD_ERR_UNSUPPORTED;
-    const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
-    if ((algo == SSD_ALGO_STAGED || algo == SSD_ALGO_FUSED || algo == SSD_ALGO_CHAIN || algo == SSD_ALGO_PIPE ||
-         algo == SSD_ALGO_PAIR || algo == SSD_ALGO_DUO) &&
-        !mfma_ok)
-        return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_CHAIN && !chain_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_PIPE && !pipe_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_PAIR && !pair_supported(H, G, N)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_DUO && !duo_supported(H, G, N, 2)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_FUSED && !fused_supported(H, G, N, Q)) return SSD_ERR_UNSUPPORTED;
-    if (algo == SSD_ALGO_FUSED && B * H * ((L + Q - 1) / Q) > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
-
-    const Layout l = layout(B, L, H, P, G, N, Q);
+    const int run = resolve(H, P, G, N, Q, dtype, algo);
+    if (run < 0) return SSD_ERR_UNSUPPORTED;
+    const Layout l = layout(B, L, H, P, G, N, Q, run);
     if (has_work) {
         if (!workspace || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
@@ -194,30 +194,11 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
                dtype == SSD_DTYPE_BF16 ? 1 : 0, stream};
     const Workspace ws = carve(workspace, l);
 
-    if (algo == SSD_ALGO_AUTO) {
-        if (!mfma_ok) {
-            algo = SSD_ALGO_REFERENCE;
-        } else {
-            const int64_t nc = (L + Q - 1) / Q;
-            // per-sequence scan (spread over the device in time segments when
-            // sequences are few) wherever it covers the shape; else one pass
-            // while chains of blocks are short and many; staged otherwise
-            if (pipe_supported(H, G, N))
-                algo = SSD_ALGO_PIPE;
-            else
-                algo = (nc <= 64 && fused_supported(H, G, N, Q) && B * H >= 64 && B * H * nc <= 0x7fffffff)
-                           ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
-        }
-    }
     hipError_t e;
-    switch (algo) {
+    switch (run) {
         case SSD_ALGO_REFERENCE: e = launch_reference_scan(a, ws); break;
         case SSD_ALGO_STAGED: e = launch_staged_scan(a, ws); break;
-        case SSD_ALGO_FUSED: e = launch_fused_scan(a, ws); break;
-        case SSD_ALGO_CHAIN: e = launch_chain_scan(a, ws); break;
         case SSD_ALGO_PIPE: e = launch_pipe_scan(a, ws); break;
-        case SSD_ALGO_PAIR: e = launch_pair_scan(a, ws); break;
-        case SSD_ALGO_DUO: e = launch_duo_scan(a, 2); break;
         default: return SSD_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
@@ -240,12 +221,19 @@ const char *ssd_status_string(ssd_status status) {
 
 const char *ssd_version(void) { return "libssd 0.1 (gfx950)"; }
 
-size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
-                                     int64_t N, int64_t chunk_size, ssd_dtype dtype) {
+size_t ssd_chunk_scan_workspace_size_algo(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                                          int64_t chunk_size, ssd_dtype dtype, ssd_algo algo) {
     if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0) return 0;
     if (H % G != 0 || !shape_supported(P, N, chunk_size)) return 0;
     if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return 0;
-    return layout(B, L, H, P, G, N, chunk_size).total;
+    const int run = resolve(H, P, G, N, chunk_size, dtype, algo);
+    if (run < 0) return 0;
+    return layout(B, L, H, P, G, N, chunk_size, run).total;
+}
+
+size_t ssd_chunk_scan_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                     int64_t N, int64_t chunk_size, ssd_dtype dtype) {
+    return ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, chunk_size, dtype, SSD_ALGO_AUTO);
 }
 
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *Bm,
@@ -269,7 +257,8 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
 
 size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                             int64_t N, int64_t chunk_size, ssd_dtype dtype) {
-    const size_t base = ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype);
+    if (dtype != SSD_DTYPE_BF16) return 0;
+    const size_t base = ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, chunk_size, dtype, SSD_ALGO_PIPE);
     if (base == 0) return 0;
     return align_up(base) + varlen_extra(B, L, H);
 }
@@ -296,7 +285,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
     if (!has_work)
         return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes, B, L, H, P, G,
                          N, chunk_size, dtype, SSD_ALGO_PIPE, stream);
-    const Layout l = layout(B, L, H, P, G, N, chunk_size);
+    const Layout l = layout(B, L, H, P, G, N, chunk_size, SSD_ALGO_PIPE);
     const size_t base = align_up(l.total);
     if (!workspace || workspace_bytes < base + varlen_extra(B, L, H)) return SSD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
@@ -412,35 +401,6 @@ ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, co
     const hipError_t e = launch_scan_bwd(x, dt, A, Bm, Cm, D, init_state, dy, dfinal, dx, ddt, dA, dBm, dCm,
                                          dD, dinit, (float *)workspace, B, L, H, G, N, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-}
-
-ssd_status ssd_chunk_scan_workspace_check(void *workspace, size_t workspace_bytes, int64_t B,
-                                          int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
-                                          int64_t chunk_size, hipStream_t stream) {
-    if (!workspace || B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0)
-        return SSD_ERR_INVALID_ARG;
-    const Layout l = layout(B, L, H, P, G, N, chunk_size);
-    if (workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
-    unsigned *ctr = (unsigned *)((char *)workspace + l.counters);
-    unsigned host[4] = {0, 0, 0, 0};
-    if (hipStreamSynchronize(stream) != hipSuccess) return SSD_ERR_HIP;
-    if (hipMemcpy(host, ctr, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess) return SSD_ERR_HIP;
-    if (host[2] != 0) {
-        const unsigned zero = 0;
-        if (hipMemcpy(ctr + 2, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SSD_ERR_HIP;
-        return SSD_ERR_HIP;
-    }
-    if (host[0] != 0 || host[1] != 0) return SSD_ERR_HIP;
-    const int64_t chains = B * H < kMaxChains ? B * H : kMaxChains;
-    if (chains > 0) {
-        std::vector<unsigned> flags((size_t)chains);
-        if (hipMemcpy(flags.data(), (char *)workspace + l.flags, flags.size() * sizeof(unsigned),
-                      hipMemcpyDeviceToHost) != hipSuccess)
-            return SSD_ERR_HIP;
-        for (unsigned f : flags)
-            if (f != 0) return SSD_ERR_HIP;
-    }
-    return SSD_OK;
 }
 
 ssd_status ssd_step(float *state, const void *x, const float *dt, const float *A, const void *Bm,

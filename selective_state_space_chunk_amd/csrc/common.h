@@ -69,16 +69,30 @@ struct ScanArgs {
     int varlen = 0;      // 1: dt carries reset flags in its sign bit (packed rows)
 };
 
-// Workspace carve-up shared by host code and kernels.
+// Workspace carve-up shared by host code and kernels (regions a call's
+// algorithm does not use are not reserved; their pointers are then unusable).
 struct Workspace {
     float *states;      // [B, nc, H, P, N]    block states / states entering each block
     float *decay;       // [B, H, nc]          exp(sum of dt*A over the block)
-    unsigned *flags;    // hand-off flags of the one-pass algorithm
-    unsigned *counters; // ticket and completion counters of the one-pass algorithm
-    float *ring;        // [B*H, 2, P, N] states handed from block to block, or segment states
-    size_t ring_floats; // floats in ring
-    void *gram;         // [B*G, nsb, 64, 64] bf16 Cm.Bm^T of every 64-token block
+    float *seg;         // segment states of the per-sequence scan and their log2 decays
+    size_t seg_floats;  // floats in seg
+    void *gram;         // [B*G, blocks, 64, 64] bf16 Cm.Bm^T of every 64-token sub-block
 };
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute is held per device).  `done` is the call site's
+// own record of the devices already set.
+constexpr int kMaxDevices = 64;
+inline hipError_t allow_lds(const void *kern, size_t bytes, bool (&done)[kMaxDevices]) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (done[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done[dev] = true;
+    return e;
+}
 
 hipError_t launch_reference_scan(const ScanArgs &a, const Workspace &ws);
 // Cm.Bm^T of every 64-token block (matrix-core paths), into ws.gram.

@@ -429,13 +429,9 @@ template <int N, int Q, int MODE>
 hipError_t launch_mode(const ScanArgs &a, const Workspace &ws, dim3 grid) {
     const size_t smem = sizeof(Smem<N, Q>);
     auto kern = scan_mfma<N, Q, MODE>;
-    static bool configured = false;
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static bool configured[kMaxDevices] = {};
+    const hipError_t e = allow_lds((const void *)kern, smem, configured);
+    if (e != hipSuccess) return e;
     kern<<<grid, kThreads, smem, a.stream>>>(
         (const __bf16 *)a.x, a.dt, a.A, (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, a.D,
         (__bf16 *)a.y, ws.states, ws.decay, (const __bf16 *)ws.gram, a.L, a.H, a.G);

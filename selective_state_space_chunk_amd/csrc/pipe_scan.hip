@@ -1,30 +1,28 @@
-// Chunk scan with one workgroup per (batch, head) sequence and two wave
-// roles, on gfx950 matrix cores (bf16 operands, fp32 accumulation).
+// Chunk scan with one workgroup per (batch, head) sequence, on gfx950 matrix
+// cores (bf16 operands, fp32 accumulation).
 //
-// The arithmetic is that of the per-sequence kernel in chain_scan.hip: the
-// sequence is walked in sub-blocks of 64 tokens, the P x N state stays in
-// matrix-core accumulators from the first token to the last, and per
-// sub-block, with Lambda the inclusive prefix sum of dt*A inside it, the
-// block decomposition of the "Mamba-2" note (section "taking each path half
-// way") and of the "Mamba-2 model walkthrough" (sections 6.1-6.2) gives
+// The sequence is walked in sub-blocks of 64 tokens and the P x N state stays
+// in matrix-core accumulators from the first token to the last.  Per
+// sub-block, with Lambda the inclusive prefix sum of dt*A inside it, the block
+// decomposition of the "Mamba-2" note (section "taking each path half way")
+// and of the "Mamba-2 model walkthrough" (sections 6.1-6.2) gives
 //   y_i = exp(Lambda_i) Cm_i . H  +  sum_{j<=i} G[i][j] exp(Lambda_i - Lambda_j) dt_j x_j  +  D x_i
 //   H  <- exp(Lambda_63) H  +  sum_j Bm_j (outer) (exp(Lambda_63 - Lambda_j) dt_j x_j)
-// with G[i][j] = Cm_i . Bm_j from the gram kernel and H the state entering
-// the sub-block.
+// with G[i][j] = Cm_i . Bm_j from the gram tiles and H the state entering the
+// sub-block.
 //
-// What differs is the division of labour.  A workgroup has eight waves, two
-// on each SIMD, with different jobs, so that each SIMD always has a second
-// instruction stream to issue from while one waits on LDS or memory:
-//   state waves 0-3   own rows p = 16w..16w+15 of the state.  In step t they
-//                     form the inter-block term of sub-block t from the state
-//                     entering it (written to LDS for the output waves) and
-//                     then advance the state over sub-block t;
-//   output waves 4-7  finish sub-block t-1 for the same rows: the inter-block
-//                     term from LDS, the masked intra-block product (the skip
-//                     term D x_i rides on the diagonal of the masked matrix),
-//                     and the stores of y; and build the masked decay matrix of
-//                     sub-block t for the next step.
-// The state waves stage the next sub-block's x, the output waves its Bm and Cm.
+// A workgroup has eight waves, two on each SIMD, in two roles, so that each
+// SIMD has a second instruction stream to issue from while one waits on LDS
+// or memory:
+//   compute waves 0-3  own rows p = 16w..16w+15 of the state.  In step t they
+//                      form the whole output of sub-block t (inter-block term,
+//                      masked intra-block product with D on the diagonal of
+//                      the masked matrix, y into an LDS tile stored as whole
+//                      rows in the next step) and advance the state over it;
+//                      they also stage x and load dt;
+//   prep waves 4-7     build the masked decay matrix of sub-block t+1 from its
+//                      gram tiles and the prefix scan of dt*A, and stage its
+//                      Bm and Cm.
 // One barrier per step; LDS buffers rotate so that nothing written in a step
 // is read in the same step by another wave.
 #include "tile_ops.h"
@@ -866,7 +864,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     }
     if (nextra > 0) {
         // no more segment states than the workspace holds
-        const int64_t cap = (int64_t)(ws.ring_floats / ((size_t)kP * N + 1));
+        const int64_t cap = (int64_t)(ws.seg_floats / ((size_t)kP * N + 1));
         if ((int64_t)nextra * (nseg - 1) > cap) nseg = (int)(1 + cap / nextra);
         if (nseg > nsb) nseg = (int)nsb;
         if (nseg < 1) nseg = 1;
@@ -876,14 +874,11 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int nwg = nmain > 0 ? nmain : nextra * nseg;
     const size_t smem = sizeof(PipeSmem<N>);
     auto kern = pipe_kernel<N, kV>;
-    static bool configured = false;
-    if (!configured) {
-        e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static bool configured[kMaxDevices] = {};
+    e = allow_lds((const void *)kern, smem, configured);
+    if (e != hipSuccess) return e;
     Args a{(const __bf16 *)sa.x, sa.dt, sa.A, (const __bf16 *)sa.Bm, (const __bf16 *)sa.Cm, sa.D,
-           sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, ws.ring,
+           sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, ws.seg,
            sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
     if (nextra > 0 && nseg > 1) {
         const int nsegwg = nextra * (nseg - 1);

@@ -1,5 +1,5 @@
-// Device helpers shared by the per-sequence matrix-core scan kernels
-// (pipe_scan.hip, pair_scan.hip): vector types, matrix-core and buffer
+// Device helpers of the per-sequence matrix-core scan kernels
+// (pipe_scan.hip): vector types, matrix-core and buffer
 // intrinsics, the LDS swizzles of the x, Bm, Cm and masked-decay tiles, the
 // per-lane offsets of the fragment reads and staging copies, and the wave-wide
 // prefix sum of dt*A.

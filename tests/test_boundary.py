@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ssd_chunk_scan_fwd", "ssd_step", "ssd_chunk_scan_workspace_size",
               "ssd_status_string", "ssd_chunk_scan_fwd_algo", "ssd_version",
-              "ssd_chunk_scan_workspace_check", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
+              "ssd_chunk_scan_workspace_size_algo", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
               "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_varlen_workspace_size", "ssd_block_prologue",
               "ssd_gated_norm", "ssd_selective_scan"):
         assert n in names
@@ -58,17 +58,43 @@ def test_status_strings_and_version(lib):
 B, L, H, P, G, N, Q = 4, 4096, 80, 64, 1, 128, 256
 
 
+def align(v):
+    return (v + 255) // 256 * 256
+
+
 def test_workspace_size(lib):
+    AUTO, REFERENCE, STAGED, PIPE = 0, 1, 2, 3
+    # the per-sequence scan (what AUTO runs here): the gram tiles of every
+    # 64-token sub-block and room for 256 segment states, nothing per block
     ws = lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 1)
+    gram = B * G * (L // 64) * 64 * 64 * 2
+    seg = 256 * (P * N + 1) * 4
+    assert ws == align(seg) + align(gram)
+    assert ws == lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, PIPE)
+    assert ws == lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, AUTO)
+    # the staged and reference forms keep every block's state and decay
     nc = L // Q
-    assert ws >= B * nc * H * P * N * 4 + B * H * 2 * P * N * 4
-    # ragged L rounds the block count up
+    states = align(B * nc * H * P * N * 4) + align(B * H * nc * 4)
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, STAGED) == states + align(gram)
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, REFERENCE) == states
+    # N = 256 runs staged under AUTO; float32 runs the reference
+    assert lib.ssd_chunk_scan_workspace_size(1, 1000, 4, P, 1, 256, 128, 1) == \
+        lib.ssd_chunk_scan_workspace_size_algo(1, 1000, 4, P, 1, 256, 128, 1, STAGED)
+    assert lib.ssd_chunk_scan_workspace_size(1, 1000, 4, P, 1, 128, 128, 0) == \
+        lib.ssd_chunk_scan_workspace_size_algo(1, 1000, 4, P, 1, 128, 128, 0, REFERENCE)
+    # a short sequence is cut into at most its sub-blocks: two sub-blocks, one segment state
+    assert lib.ssd_chunk_scan_workspace_size(1, 128, 1, P, 1, N, Q, 1) == align((P * N + 1) * 4) + align(2 * 8192)
+    # ragged L rounds the sub-block count up
     assert lib.ssd_chunk_scan_workspace_size(B, L + 1, H, P, G, N, Q, 1) > ws
-    # unsupported shapes report 0
+    # unsupported shapes, dtypes and algorithms report 0
     for bad in [(B, L, H, 48, G, N, Q), (B, L, H, P, G, 512, Q), (B, L, H, P, G, N, 32),
                 (B, L, H, P, 3, N, Q), (-1, L, H, P, G, N, Q)]:
         assert lib.ssd_chunk_scan_workspace_size(*bad, 1) == 0
     assert lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 7) == 0
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, 9) == 0
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 0, PIPE) == 0      # float32
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, 256, Q, 1, PIPE) == 0    # N = 256
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, 32, G, N, Q, 1, STAGED) == 0   # P = 32
 
 
 def fake(addr):
@@ -106,10 +132,11 @@ def test_scan_rejects_bad_arguments_before_launch(lib):
     # matrix-core algorithms need bf16 and P = 64
     assert scan_call(lib, dtype=0, algo=3) == ssd.SSD_ERR_UNSUPPORTED
     assert scan_call(lib, shape=(B, L, H, 32, G, N, Q), algo=2) == ssd.SSD_ERR_UNSUPPORTED
-    # workspace missing or too small
+    # workspace missing or too small, for the algorithm the call runs
     assert scan_call(lib, ws=0) == ssd.SSD_ERR_WORKSPACE
     need = lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 1)
     assert scan_call(lib, ws_bytes=need - 1) == ssd.SSD_ERR_WORKSPACE
+    assert scan_call(lib, ws_bytes=need, algo=2) == ssd.SSD_ERR_WORKSPACE   # staged needs its block states
 
 
 def test_step_rejects_bad_arguments_before_launch(lib):
