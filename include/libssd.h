@@ -30,8 +30,11 @@
  *
  *  - Memory.  Every tensor argument is a DEVICE pointer to dense, row-major
  *    memory in the shape stated, owned by the caller.  The library allocates
- *    nothing and keeps no state between calls.  Every pointer must be 16-byte
- *    aligned, else SSD_ERR_INVALID_ARG.
+ *    nothing at run time and keeps no state between calls (the one exception,
+ *    ssd_chunk_scan_fwd_noalloc, keeps its scratch in a static device array).
+ *    Every pointer must be 16-byte aligned, else SSD_ERR_INVALID_ARG.
+ *  - Device.  `stream` belongs to the current device (0 = its null stream);
+ *    per-device set-up is done for the current device.
  *  - Types.  dt, A, D and all states are float32.  x, Bm, Cm and y are
  *    float32 (SSD_DTYPE_F32) or bfloat16 (SSD_DTYPE_BF16).  Arithmetic
  *    accumulates in float32; products inside a block may use bfloat16 operands
@@ -64,7 +67,8 @@ typedef enum {
     SSD_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, H % G != 0 */
     SSD_ERR_UNSUPPORTED = 2,   /* shape, chunk size, dtype or algorithm not supported */
     SSD_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
-    SSD_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+    SSD_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    SSD_ERR_TOO_LARGE = 5      /* more scratch than ssd_chunk_scan_fwd_noalloc holds */
 } ssd_status;
 
 typedef enum {
@@ -159,6 +163,31 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                    int64_t N, int64_t chunk_size, ssd_dtype dtype,
                                    ssd_algo algo, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * forward scan of ssd_chunk_scan_fwd (SSD_ALGO_AUTO) with no workspace
+ * argument.  Its scratch is a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES per device, created with the library's code
+ * object on that device and held until the process ends; the call allocates
+ * nothing (no hipMalloc, no library allocation).  A shape whose workspace
+ * (ssd_chunk_scan_workspace_size) exceeds that size returns SSD_ERR_TOO_LARGE
+ * before anything is enqueued.  Every call on one device shares that
+ * device's array, which keeps the last call's contents (nothing in it needs
+ * to start at zero): calls that overlap on one device (two streams, or two
+ * host threads) race and give wrong results; order them.  Arguments, layouts
+ * and other errors as ssd_chunk_scan_fwd; the caller passes y and
+ * final_state.  The first call on a device looks up the array's address.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *Bm, const void *Cm, const float *D,
+                                      const float *init_state, void *y, float *final_state,
+                                      int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                      int64_t N, int64_t chunk_size, ssd_dtype dtype,
+                                      hipStream_t stream);
 
 /*
  * Packed rows of independent sequences ("Mamba" reading notes, section 3.5:

@@ -29,8 +29,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libssd.so")
 
-SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_TOO_LARGE = range(6)
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
+# bytes of the static per-device scratch of ssd_chunk_scan_fwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 ALGOS = {"auto": 0, "reference": 1, "staged": 2, "pipe": 3}
 
 _lib = None
@@ -68,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_algo.argtypes = scan_args + [ctypes.c_int, vp]
     lib.ssd_chunk_scan_fwd_algo.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [vp] * 9 + [i64] * 7 + [ctypes.c_int, vp]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ssd_step.restype = ctypes.c_int
     lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
@@ -204,6 +208,38 @@ def ssd_chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
         ALGOS[algo], _stream_handle(dev, stream))
     _check(st, "ssd_chunk_scan_fwd")
     return y, final_state
+
+
+def ssd_chunk_scan_fwd_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                               Cm: torch.Tensor, D: torch.Tensor, init_state: Optional[torch.Tensor],
+                               chunk_size: int, y: torch.Tensor, final_state: Optional[torch.Tensor] = None, *,
+                               stream=None) -> None:
+    """The forward scan with the library's static per-device scratch: no
+    workspace, and nothing allocated here or in the library.  The caller
+    passes y (and final_state, or None to skip it).  Calls on one device
+    share the scratch and must not overlap.  Raises SSDError with status
+    SSD_ERR_TOO_LARGE for shapes whose workspace exceeds the scratch."""
+    lib = load_library()
+    if x.dim() != 4 or Bm.dim() != 4:
+        raise ValueError("x must be [B,L,H,P] and Bm [B,L,G,N]")
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    _need(x, "x", x.dtype, (Bsz, L, H, P), dev)
+    _need(dt, "dt", torch.float32, (Bsz, L, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(Bm, "Bm", x.dtype, (Bsz, L, G, N), dev)
+    _need(Cm, "Cm", x.dtype, (Bsz, L, G, N), dev)
+    _need(D, "D", torch.float32, (H,), dev)
+    _need(y, "y", x.dtype, (Bsz, L, H, P), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (Bsz, H, P, N), dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (Bsz, H, P, N), dev)
+    st = lib.ssd_chunk_scan_fwd_noalloc(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+        Bsz, L, H, P, G, N, chunk_size, _dtype_code(x.dtype), _stream_handle(dev, stream))
+    _check(st, "ssd_chunk_scan_fwd_noalloc")
 
 
 def ssd_chunk_scan_fwd_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,

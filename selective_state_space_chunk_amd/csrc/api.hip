@@ -3,6 +3,8 @@
 #include "libssd.h"
 #include "common.h"
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 namespace ssd {
@@ -204,6 +206,32 @@ ssd_status scan_impl(const void *x, const float *dt, const float *A, const void 
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+// Scratch of ssd_chunk_scan_fwd_noalloc: one array per device, created with
+// the library's code object on that device and held until the process ends.
+// Host code never uses the array's name as an address: the address on each
+// device comes from hipGetSymbolAddress, once per device, with that device
+// current.
+__device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,6 +243,8 @@ const char *ssd_status_string(ssd_status status) {
         case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape, chunk size, dtype or algorithm not supported";
         case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
         case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime or launch failure";
+        case SSD_ERR_TOO_LARGE:
+            return "SSD_ERR_TOO_LARGE: the call needs more scratch than the no-allocation entry point holds";
     }
     return "unknown ssd_status";
 }
@@ -253,6 +283,20 @@ ssd_status ssd_chunk_scan_fwd_algo(const void *x, const float *dt, const float *
                                    hipStream_t stream) {
     return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, workspace, workspace_bytes,
                      B, L, H, P, G, N, chunk_size, dtype, algo, stream);
+}
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A, const void *Bm,
+                                      const void *Cm, const float *D, const float *init_state, void *y,
+                                      float *final_state, int64_t B, int64_t L, int64_t H, int64_t P,
+                                      int64_t G, int64_t N, int64_t chunk_size, ssd_dtype dtype,
+                                      hipStream_t stream) {
+    const size_t need = ssd_chunk_scan_workspace_size(B, L, H, P, G, N, chunk_size, dtype);
+    if (need > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+    // need == 0 (a shape outside the support matrix): scan_impl reports why
+    void *ws = nullptr;
+    if (need > 0 && B > 0 && L > 0 && scratch_address(&ws) != hipSuccess) return SSD_ERR_HIP;
+    return scan_impl(x, dt, A, Bm, Cm, D, init_state, y, final_state, ws, ws ? SSD_NOALLOC_SCRATCH_BYTES : 0,
+                     B, L, H, P, G, N, chunk_size, dtype, SSD_ALGO_AUTO, stream);
 }
 
 size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,

@@ -38,6 +38,12 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_noalloc_scratch_size_matches_the_binding():
+    import selective_state_space_chunk_amd as ssd
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == ssd.NOALLOC_SCRATCH_BYTES
+
+
 def test_library_exports_every_declared_symbol(lib):
     import selective_state_space_chunk_amd as ssd
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
@@ -50,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     import selective_state_space_chunk_amd as ssd
-    for code in range(5):
+    for code in range(6):
         assert ssd.status_string(code).startswith("SSD_")
     assert "gfx950" in ssd.version()
 
