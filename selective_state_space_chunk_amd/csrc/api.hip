@@ -301,7 +301,7 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
 
 size_t ssd_chunk_scan_varlen_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                             int64_t N, int64_t chunk_size, ssd_dtype dtype) {
-    if (dtype != SSD_DTYPE_BF16) return 0;
+    if (dtype != SSD_DTYPE_BF16 || N > 128) return 0;
     const size_t base = ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, chunk_size, dtype, SSD_ALGO_PIPE);
     if (base == 0) return 0;
     return align_up(base) + varlen_extra(B, L, H);
@@ -322,7 +322,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
     if (((uintptr_t)seq_idx & 3u) != 0) return SSD_ERR_INVALID_ARG;
     if (chunk_size <= 0) return SSD_ERR_INVALID_ARG;
     if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !mfma_supported(P, N, chunk_size) ||
-        !pipe_supported(H, G, N))
+        !pipe_supported(H, G, N) || N > 128)
         return SSD_ERR_UNSUPPORTED;
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + chunk_size - 1) / chunk_size > 0x7fffffff) return SSD_ERR_UNSUPPORTED;

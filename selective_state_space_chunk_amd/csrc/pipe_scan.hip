@@ -39,7 +39,11 @@ template <int N>
 struct PipeSmem {
     __bf16 X[2][kSub * kP];        // x [j][p] (by t % 2), chunks swizzled (xsw)
     __bf16 Bt[2][kSub * N];        // Bm [j][n] (by t % 2), chunks swizzled (bsw)
-    __bf16 Ct[2][kSub * N];        // Cm [i][n] (by t % 2), chunks swizzled (csw)
+    // Cm [i][n] (by t % 2), chunks swizzled (csw).  At N = 256 there is room
+    // for one slot only: the compute waves read it in the first part of a
+    // step, and the prep waves refill it after a barrier in the middle.
+    static constexpr int kCSlots = N == 256 ? 1 : 2;
+    __bf16 Ct[kCSlots][ct_bytes<N> / 2];
     __bf16 Mm[2][kSub * kSub];     // masked decay matrix [i][j] (by t % 2), chunks swizzled (msw)
     WaveDecays wd[8];
     // y on its way to global memory as whole 128-byte rows: written by the
@@ -152,12 +156,25 @@ template <int N>
 __device__ __forceinline__ void stage_bc(PipeSmem<N> &sm, int par, const BulkBC<N> &sl, const LaneOffs<N> &o) {
     using O = LaneOffs<N>;
     unsigned char *Bb = reinterpret_cast<unsigned char *>(sm.Bt[par]);
-    unsigned char *Cb = reinterpret_cast<unsigned char *>(sm.Ct[par]);
+    unsigned char *Cb = reinterpret_cast<unsigned char *>(sm.Ct[par % PipeSmem<N>::kCSlots]);
 #pragma unroll
     for (int k = 0; k < N / 32; ++k) {
-        lds_st<uint4>(Bb + o.sb + k * (256 / O::CPR) * O::RB, sl.b[k]);
+        lds_st<uint4>(Bb + (o.sb ^ sb_flip<N>(k)) + k * (256 / O::CPR) * O::RB, sl.b[k]);
         lds_st<uint4>(Cb + o.sc[k], sl.c[k]);
     }
+}
+template <int N>
+__device__ __forceinline__ void stage_b(PipeSmem<N> &sm, int par, const BulkBC<N> &sl, const LaneOffs<N> &o) {
+    using O = LaneOffs<N>;
+    unsigned char *Bb = reinterpret_cast<unsigned char *>(sm.Bt[par]);
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) lds_st<uint4>(Bb + (o.sb ^ sb_flip<N>(k)) + k * (256 / O::CPR) * O::RB, sl.b[k]);
+}
+template <int N>
+__device__ __forceinline__ void stage_c(PipeSmem<N> &sm, const BulkBC<N> &sl, const LaneOffs<N> &o) {
+    unsigned char *Cb = reinterpret_cast<unsigned char *>(sm.Ct[0]);
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) lds_st<uint4>(Cb + o.sc[k], sl.c[k]);
 }
 
 
@@ -241,10 +258,47 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                                                    o.gx + k * step, 0, 0);
     };
 
-    // compute wave pq loads dt of tokens 16pq .. 16pq+15 (four lanes each)
+    // x and dt of the steps ahead are loaded, staged and published by the
+    // compute waves, or at N = 256 (whose compute waves hold twice the state
+    // and have no registers to spare) by the prep waves.  Wave pq of that role
+    // loads dt of tokens 16pq .. 16pq+15 (four lanes each).  xbulk[s % 2]
+    // holds x of step s from its load (issued at the end of step s-3) until
+    // it is staged at the end of step s-1; dq[t % 2] holds the dt quarter of
+    // step t+2 (loaded in step t-2), written to LDS in step t and replaced by
+    // that of t+4.
+    constexpr bool kPrepX = PipeSmem<N>::kCSlots == 1;
+    const bool x_wave = compute_wave != kPrepX;
     const int dq_tok = 16 * pq + (lane & 15);
     const int gdq = dq_tok * (int)(a.H * 4);
-    if (compute_wave) {
+    BulkX xbulk[2];
+    float dq[2];
+    // x of sub-block 0 staged; x of sub-blocks 1 and 2 and the dt quarters of
+    // sub-blocks 2 and 3 in flight
+    auto xd_prologue = [&]() __attribute__((always_inline)) {
+        const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1, t3 = T > 3 ? 3 : T - 1;
+        load_x_at<N>(xbulk[0], a, o, x_at(0), q_of(0));
+        dq[0] = load_dt_at(a, d_at(t2), q_of(t2), gdq);
+        dq[1] = load_dt_at(a, d_at(t3), q_of(t3), gdq);
+        stage_x<N>(sm, 0, xbulk[0], o);
+        load_x_at<N>(xbulk[1], a, o, x_at(t1), q_of(t1));
+        load_x_at<N>(xbulk[0], a, o, x_at(t2), q_of(t2));
+    };
+    // step t: this wave's dt quarter of step t+2 into LDS, that of t+4 into its register
+    auto xd_dt = [&](int t, int par) __attribute__((always_inline)) {
+        if (lane < 16) sm.dts[(t + 2) & 3][dq_tok] = dq[par];
+        const int td = t + 4 < T ? t + 4 : T - 1;
+        dq[par] = load_dt_at(a, d_at(td), q_of(td), gdq);
+    };
+    // step t: x of step t+1 into LDS, and x of step t+3 into its registers.
+    // Unconditional: a conditional stage leaves its loads unwaited on one
+    // path, and the loop head then waits for them on every path (the last
+    // step stages into a slot nobody reads).
+    auto xd_x = [&](int t, int par) __attribute__((always_inline)) {
+        stage_x<N>(sm, par ^ 1, xbulk[par ^ 1], o);
+        const int tx = t + 3 < T ? t + 3 : T - 1;
+        load_x_at<N>(xbulk[par ^ 1], a, o, x_at(tx), q_of(tx));
+    };
+    if (x_wave) {
         const int t1 = T > 1 ? 1 : 0;
         const float d0 = load_dt_at(a, d_at(0), q_of(0), gdq);
         const float d1 = load_dt_at(a, d_at(t1), q_of(t1), gdq);
@@ -261,23 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // columns p): lane holds n = 16t + 4lgrp + 0..3, p = 16pq + lrow.  The
         // outputs of sub-block t: lane holds token i = 16it + lrow,
         // p = 16pq + 4lgrp + 0..3.
-        // prologue: x of sub-block 0 staged; x of sub-blocks 1 and 2 and this
-        // wave's dt quarters of sub-blocks 2 and 3 in flight.  bulk[s % 2]
-        // holds x of step s from its load (issued at the end of step s-3)
-        // until it is staged at the end of step s-1; dq[t % 2] holds the dt
-        // quarter of step t+2 (loaded in step t-2), written to LDS in step t
-        // and replaced by that of t+4.
-        BulkX bulk[2];
-        float dq[2];
-        {
-            const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1, t3 = T > 3 ? 3 : T - 1;
-            load_x_at<N>(bulk[0], a, o, x_at(0), q_of(0));
-            dq[0] = load_dt_at(a, d_at(t2), q_of(t2), gdq);
-            dq[1] = load_dt_at(a, d_at(t3), q_of(t3), gdq);
-            stage_x<N>(sm, 0, bulk[0], o);
-            load_x_at<N>(bulk[1], a, o, x_at(t1), q_of(t1));
-            load_x_at<N>(bulk[0], a, o, x_at(t2), q_of(t2));
-        }
+        if constexpr (!kPrepX) xd_prologue();
         f32x4 Hacc[NT];
         const int lane_off = (16 * pq + lrow) * N + 4 * lgrp;
         {
@@ -319,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         auto step = [&](int t, int par) __attribute__((always_inline)) {
             const unsigned char *Xb = reinterpret_cast<const unsigned char *>(sm.X[par]);
             const unsigned char *Bb = reinterpret_cast<const unsigned char *>(sm.Bt[par]);
-            const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par]);
+            const unsigned char *Cb = reinterpret_cast<const unsigned char *>(sm.Ct[par % PipeSmem<N>::kCSlots]);
             const unsigned char *Mr = reinterpret_cast<const unsigned char *>(sm.Mm[par]);
             const float Ah2 = t >= nown ? Ahx2 : Ah2v;
             // decays of sub-block t (this wave's own copy)
@@ -341,13 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             }
             wd.w[lane] = wv;
             wd.rdec[lane] = rdv;
-            // this wave's dt quarter of step t+2 into LDS, that of t+4 into
-            // its register
-            {
-                if (lane < 16) sm.dts[(t + 2) & 3][dq_tok] = dq[par];
-                const int td = t + 4 < T ? t + 4 : T - 1;
-                dq[par] = load_dt_at(a, d_at(td), q_of(td), gdq);
-            }
+            if constexpr (!kPrepX) xd_dt(t, par);
             // the whole rows of y of step t-1 (written to YS by the four compute waves in step t-1)
             store_y(t - 1, par ^ 1);
 
@@ -355,8 +387,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             auto read_cf = [&](int ks, bf16x8 (&cf)[4]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    const bf16x4 c0 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][0] ^ csw_tile_bytes<N>(it)));
-                    const bf16x4 c1 = lds_ld<bf16x4>(Cb + it * 16 * O::RB + (o.ct[ks][1] ^ csw_tile_bytes<N>(it)));
+                    const unsigned char *Ci = Cb + it * (16 * O::RB + ct_pad<N>) + (ks / O::KSO) * 256;
+                    const bf16x4 c0 = lds_ld<bf16x4>(Ci + (o.ct[ks % O::KSO][0] ^ csw_tile_bytes<N>(it)));
+                    const bf16x4 c1 = lds_ld<bf16x4>(Ci + (o.ct[ks % O::KSO][1] ^ csw_tile_bytes<N>(it)));
                     cf[it] = bf16x8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                 }
             };
@@ -364,20 +397,25 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             auto read_bt = [&](int ks, int v4, bf16x8 (&bt)[4]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const bf16x4 lo = tr4(Bb + o.bt[4 * v4 + u] + ks * 32 * O::RB);
-                    const bf16x4 hi = tr4(Bb + o.bt[4 * v4 + u] + ks * 32 * O::RB + 4 * O::RB);
+                    const int nt = 4 * v4 + u;
+                    const unsigned char *Bn = Bb + o.bt[nt % O::NTO] + (nt / O::NTO) * 256 + ks * 32 * O::RB;
+                    const bf16x4 lo = tr4(Bn);
+                    const bf16x4 hi = tr4(Bn + 4 * O::RB);
                     bt[u] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
             };
             bf16x8 cf[2][4];
             read_cf(0, cf[0]);
             bf16x8 xf[2];
+            auto read_xf = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
-                const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
-                xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x4 lo = tr4(Xb + o.xtr + ks * 4096);
+                    const bf16x4 hi = tr4(Xb + o.xtr + ks * 4096 + 512);
+                    xf[ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            };
+            if constexpr (PipeSmem<N>::kCSlots == 2) read_xf();
             const f32x4 rd = {wd.rdec[lrow], wd.rdec[16 + lrow], wd.rdec[32 + lrow], wd.rdec[48 + lrow]};
             __builtin_amdgcn_sched_barrier(0);
 
@@ -385,22 +423,33 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
             f32x4 Y[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it) Y[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // masked-matrix fragments of the intra-block product: read during the
+            // last k-step of the inter-block term, or at N = 256 (whose larger
+            // state leaves no registers for them there) after it
             bf16x8 mf[4][2];
+            auto read_mf = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+                        if (!(kk == 1 && it < 2)) mf[it][kk] = lds_ld<bf16x8>(Mr + o.mm[kk] + it * 2048);
+            };
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 1 < KS) {
+                if (ks + 1 < KS)
                     read_cf(ks + 1, cf[(ks + 1) & 1]);
-                } else {
-#pragma unroll
-                    for (int it = 0; it < 4; ++it)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-                            if (!(kk == 1 && it < 2)) mf[it][kk] = lds_ld<bf16x8>(Mr + o.mm[kk] + it * 2048);
-                }
+                else if constexpr (PipeSmem<N>::kCSlots == 2)
+                    read_mf();
                 const bf16x8 ah = to_bf16x8(Hacc[2 * ks], Hacc[2 * ks + 1]);
 #pragma unroll
                 for (int it = 0; it < 4; ++it) Y[it] = mfma(ah, cf[ks & 1][it], Y[it]);
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            // one Cm slot (N = 256): done with it, the prep waves refill it
+            if constexpr (PipeSmem<N>::kCSlots == 1) {
+                __syncthreads();
+                read_mf();
+                read_xf();
             }
             constexpr int NG = NT / 4;   // groups of four n-tiles
             bf16x8 bt[2][4];
@@ -447,15 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
                 for (int u = 0; u < 4; ++u) Hacc[4 * v4 + u] = mfma(bt[r & 1][u], xw[ks], Hacc[4 * v4 + u]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // x of step t+1 into LDS, and x of step t+3 into its registers.
-            // Unconditional: a conditional stage leaves its loads unwaited on
-            // one path, and the loop head then waits for them on every path
-            // (the last step stages into a slot nobody reads).
-            stage_x<N>(sm, par ^ 1, bulk[par ^ 1], o);
-            {
-                const int tx = t + 3 < T ? t + 3 : T - 1;
-                load_x_at<N>(bulk[par ^ 1], a, o, x_at(tx), q_of(tx));
-            }
+            if constexpr (!kPrepX) xd_x(t, par);
             __syncthreads();
         };
         // steps [t0, t1) with the parity of each step known at compile time
@@ -548,6 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // flight, issued in the order a step issues them (G tiles, then Bm,
         // Cm), so that the loop is entered with the loads of its steady state
         uint2 gt[2][3];
+        if constexpr (kPrepX) xd_prologue();
         {
             const int t1 = T > 1 ? 1 : 0, t2 = T > 2 ? 2 : T - 1;
             load_g_at(gt[0], a, g_at(0), q_of(0), pq, lane);
@@ -563,6 +605,29 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
         // sub-block repeat it), so that the wait counts the compiler derives
         // at the loop head are those of the steady state.
         auto step = [&](int t, int par) __attribute__((always_inline)) {
+            if constexpr (kPrepX) {
+                // Bm of sub-block t+1 (its slot was last read in step t-1) and
+                // the loads of t+2, the dt and x duties; after the compute
+                // waves are done with Cm (the middle barrier), Cm of t+1 and
+                // the masked matrix of t+1, then the G tiles of t+3 into the
+                // slot just used
+                stage_b<N>(sm, par ^ 1, bulk[par ^ 1], o);
+                {
+                    const int tl = t + 2 < T ? t + 2 : T - 1;
+                    load_bc_at<N>(bulk[par], a, o, b_at(tl), q_of(tl));
+                }
+                xd_dt(t, par);
+                xd_x(t, par);
+                __syncthreads();
+                stage_c<N>(sm, bulk[par ^ 1], o);
+                build_m(t + 1, gt[par ^ 1], par ^ 1);
+                {
+                    const int tl = t + 3 < T ? t + 3 : T - 1;
+                    load_g_at(gt[par ^ 1], a, g_at(tl), q_of(tl), pq, lane);
+                }
+                __syncthreads();
+                return;
+            }
             // sub-block t+1 (its G tiles were loaded in step t-1, its dt is in
             // LDS), then the G tiles of t+3 into the same slot
             build_m(t + 1, gt[par ^ 1], par ^ 1);
@@ -811,13 +876,190 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     }
 }
 
+// The same segment states at N = 256, where the pair layout's LDS (two slots
+// of two sub-blocks of Bm) does not fit: one sub-block per step, and the
+// eight waves split the state instead of the tokens.  Wave w holds n-tiles
+// 4(w & 3) .. +3 and p-tiles 2(w >> 2), +1 (an x fragment serves four waves,
+// a Bm fragment two); no partial states to add up at the end.  Wave 0 loads
+// dt three steps ahead and scans it two steps ahead into a three-slot LDS
+// ring of weights and log2 decays; x is multiplied by its weights as it is
+// staged.  Register slot s % 2 holds sub-block s from its load (step s - 2)
+// until it is staged to LDS slot s % 2 at the end of step s - 1.
+template <int N, bool kV>
+__device__ __forceinline__ void seg_state_block_wide(const Args &a, int blk) {
+    __shared__ __align__(16) __bf16 lds_x[2][kSub * kP];
+    __shared__ __align__(16) __bf16 lds_bt[2][kSub * N];
+    __shared__ __align__(16) float lds_w[3][kSub];
+    __shared__ float lds_l[3];
+    using O = LaneOffs<N>;
+    constexpr int NTW = 4;        // n-tiles per wave
+    constexpr int KB = N / 64;    // Bm chunks staged per thread
+    const int xe = blk % a.nextra, q = blk / a.nextra;
+    const int64_t chain = a.nmain + xe;
+    const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
+    const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
+    const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
+    const float Ah2 = a.A[h] * kLog2e;
+    const int s0 = q * a.seglen, len = a.seglen;   // segments before the last are full and inside the sequence
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nq = wave & 3, pp = wave >> 2;
+    const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
+    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G);
+    const int xtr1 = lane_offsets<N>(tid, 2 * pp + 1, a.H, a.G).xtr;   // second p-tile
+    // staging: thread (u = tid % 256, half nh) stages x chunk nh (token
+    // u / 8 + 32 nh) and Bm chunks nh*KB .. +KB-1 of u
+    const int nh = tid >> 8;
+    const int my_token = ((tid & 255) >> 3) + 32 * nh;
+
+    auto sub_at = [&](int st) __attribute__((always_inline)) { return st < len ? st : len - 1; };
+    uint4 xr[2], br[2][KB];
+    auto load = [&](int st, int slot) __attribute__((always_inline)) {
+        const int k = sub_at(st);
+        const int qn = sub_tokens(a, s0 + k);
+        const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+        const rsrc_t rx = rsrc(a.x + (row0 * a.H + h) * kP, (int)(((int64_t)(qn - 1) * a.H * kP + kP) * 2));
+        xr[slot] = ld16(rx, o.gx + nh * (int)(32 * a.H * kP * 2));
+        const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, (int)(((int64_t)(qn - 1) * a.G * N + N) * 2));
+        const int step = (int)((256 / O::CPR) * a.G * N * 2);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) br[slot][kk] = ld16(rb, o.gb + (nh * KB + kk) * step);
+    };
+    // wave 0: dt of sub-block st (lane = token) into register slot `slot`
+    float dts[2];
+    auto load_dt = [&](int st, int slot) __attribute__((always_inline)) {
+        const int k = sub_at(st);
+        const int qn = sub_tokens(a, s0 + k);
+        const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
+        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
+        dts[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
+    };
+    // wave 0: weights and log2 decay of sub-block st into ring slot st % 3
+    auto weights = [&](int st, int slot) __attribute__((always_inline)) {
+        const float dr = dts[slot];
+        const float d = kV ? dt_mag(dr) : dr;
+        const float v = wave_scan(d * Ah2);
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        float w = ex2(l - v) * d, ls = l;
+        if constexpr (kV) {
+            // a reset: nothing before it reaches the end, and the decay is zero
+            const uint64_t m = reset_mask(dr);
+            if (m) {
+                if (lane < 63 - (int)__builtin_clzll(m)) w = 0.f;
+                ls = -__builtin_inff();
+            }
+        }
+        lds_w[st % 3][lane] = w;
+        if (lane == 0) lds_l[st % 3] = ls;
+    };
+    // x of sub-block st (register slot `slot`) times its weights, and Bm,
+    // into LDS slot `slot`
+    auto stage = [&](int st, int slot) __attribute__((always_inline)) {
+        unsigned char *Xb = reinterpret_cast<unsigned char *>(lds_x[slot]);
+        unsigned char *Bb = reinterpret_cast<unsigned char *>(lds_bt[slot]);
+        const float w = lds_w[st % 3][my_token];
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, xr[slot]);
+        f32x4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x0[e] = (float)xv[e] * w;
+            x1[e] = (float)xv[4 + e] * w;
+        }
+        lds_st<bf16x8>(Xb + o.sx + nh * 4096, to_bf16x8(x0, x1));
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int k = nh * KB + kk;
+            lds_st<uint4>(Bb + (o.sb ^ sb_flip<N>(k)) + k * (256 / O::CPR) * O::RB, br[slot][kk]);
+        }
+    };
+
+    // prologue: sub-blocks 0 and 1 loaded, weights of 0 and 1, dt of 2 in
+    // flight, sub-block 0 staged
+    load(0, 0);
+    load(1, 1);
+    if (wave == 0) {
+        load_dt(0, 0);
+        load_dt(1, 1);
+        weights(0, 0);
+        load_dt(2, 0);
+        weights(1, 1);
+    }
+    __syncthreads();
+    stage(0, 0);
+    __syncthreads();
+
+    f32x4 Hacc[NTW][2];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) Hacc[u][0] = Hacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float log2dec = 0.f;
+    auto step = [&](int st, int par) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float lsub = lds_l[st % 3];
+        log2dec += lsub;
+        // sub-block st+2 into the register slot staged at the end of the last step
+        load(st + 2, par);
+        if (wave == 0) {
+            load_dt(st + 3, par ^ 1);   // the slot whose sub-block (st+1) was scanned in the last step
+            weights(st + 2, par);
+        }
+        const float gam = ex2(lsub);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            Hacc[u][0] *= gam;
+            Hacc[u][1] *= gam;
+        }
+        const unsigned char *Xb = reinterpret_cast<const unsigned char *>(lds_x[par]);
+        const unsigned char *Bb = reinterpret_cast<const unsigned char *>(lds_bt[par]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 xw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int xo = (j ? xtr1 : o.xtr) + ks * 4096;
+                const bf16x4 lo = tr4(Xb + xo), hi = tr4(Xb + xo + 512);
+                xw[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int u = 0; u < NTW; ++u) {
+                // n-tile 4nq + u: o.bt holds the first eight (no run-time index into o)
+                const int bo = ((nq & 1) ? o.bt[4 + u] : o.bt[u]) + (nq >> 1) * 256;
+                const bf16x4 blo = tr4(Bb + bo + ks * 32 * O::RB);
+                const bf16x4 bhi = tr4(Bb + bo + ks * 32 * O::RB + 4 * O::RB);
+                const bf16x8 bt = bf16x8{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+                Hacc[u][0] = mfma(bt, xw[0], Hacc[u][0]);
+                Hacc[u][1] = mfma(bt, xw[1], Hacc[u][1]);
+            }
+        }
+        // unconditional (clamped) loads and stages: the same memory operations
+        // in every step, so that the wait counts need not cover a shorter path
+        stage(st + 1, par ^ 1);
+        __syncthreads();
+    };
+    int st = 0;
+    for (; st + 1 < len; st += 2) {
+        step(st, 0);
+        step(st + 1, 1);
+    }
+    if (st < len) step(st, 0);
+    float *dst = seg_state<N>(a, xe, q) + (32 * pp + lrow) * N + 16 * NTW * nq + 4 * lgrp;
+#pragma unroll
+    for (int u = 0; u < NTW; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<f32x4 *>(dst + 16 * j * N + 16 * u) = Hacc[u][j];
+    if (tid == 0) *seg_log2decay<N>(a, xe, q) = log2dec;
+}
+
 // The work that must precede pipe_kernel when there are segments, in one
 // launch so that the two parts share the device: workgroups below nsegwg
 // compute segment states, the others one sub-block's gram tiles each.
 template <int N, bool kV>
 __global__ __launch_bounds__(512) void prep_kernel(Args a, int nsegwg) {
     if ((int)blockIdx.x < nsegwg) {
-        seg_state_block<N, kV>(a, blockIdx.x);
+        if constexpr (N == 256)
+            seg_state_block_wide<N, kV>(a, blockIdx.x);
+        else
+            seg_state_block<N, kV>(a, blockIdx.x);
     } else {
         const int64_t k = (int64_t)blockIdx.x - nsegwg;
         gram_block<N, 8>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb,
@@ -896,7 +1138,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
 }  // namespace
 
 bool pipe_supported(int64_t H, int64_t G, int64_t N) {
-    if (!(N == 64 || N == 128)) return false;
+    if (!(N == 64 || N == 128 || N == 256)) return false;
     const int64_t lim = (int64_t)1 << 31;
     return (int64_t)kSub * H * kP * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
 }
@@ -905,6 +1147,7 @@ hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws) {
     switch (a.N) {
         case 64: return a.varlen ? launch<64, true>(a, ws) : launch<64, false>(a, ws);
         case 128: return a.varlen ? launch<128, true>(a, ws) : launch<128, false>(a, ws);
+        case 256: return a.varlen ? hipErrorInvalidValue : launch<256, false>(a, ws);
         default: return hipErrorInvalidValue;
     }
 }

@@ -36,23 +36,43 @@ struct WaveDecays {          // one wave's decays of the sub-block it works on
 };
 
 __device__ __forceinline__ int xsw(int r) { return ((r >> 1) & 1) * 2 + ((r >> 3) & 1) * 4; }
+// (rows of 256 or 512 bytes start on the same bank, so N = 256 uses the
+// N = 128 patterns, which only permute chunks within each 256-byte half)
 template <int N>
 __device__ __forceinline__ int bsw(int r) {
-    if constexpr (N == 128) return 2 * (r & 3) + 8 * ((r >> 3) & 1);
+    if constexpr (N >= 128) return 2 * (r & 3) + 8 * ((r >> 3) & 1);
     else return xsw(r);
 }
 // Cm rows: rows 16 apart get different chunk permutations, so that the
 // fragment reads of consecutive 16-row tiles never fall on the same banks
 // (the compiler would otherwise pair them into one two-address read whose
 // halves collide).
+// At N = 256 the rows of 16-row tile `it` are shifted by ct_pad * it bytes
+// instead (a padded layout): the same bank separation of consecutive tiles,
+// but the tile offset of a fragment read becomes an immediate, which saves the
+// compute waves 24 address registers.
 template <int N>
 __device__ __forceinline__ int csw(int r) {
-    if constexpr (N == 128) return (r & 15) ^ (((r >> 4) & 3) << 2);
+    if constexpr (N == 256) return r & 15;
+    else if constexpr (N == 128) return (r & 15) ^ (((r >> 4) & 3) << 2);
     else return ((r >> 1) & 7) ^ (((r >> 4) & 3) << 1);
 }
 // byte XOR that csw applies to the rows of 16-row tile `it` beyond row-in-tile bits
 template <int N>
-__device__ __forceinline__ constexpr int csw_tile_bytes(int it) { return (N == 128 ? 64 : 32) * (it & 3); }
+__device__ __forceinline__ constexpr int csw_tile_bytes(int it) {
+    return N == 256 ? 0 : (N == 128 ? 64 : 32) * (it & 3);
+}
+// bytes by which each 16-row tile of Cm is shifted (N = 256), and the bytes
+// of a staged Cm sub-block
+template <int N>
+constexpr int ct_pad = N == 256 ? 64 : 0;
+template <int N>
+constexpr int ct_bytes = kSub * N * 2 + 3 * ct_pad<N>;
+// Bm staging: chunk k of a thread lies 256/CPR rows below chunk 0; at N = 256
+// that is 8 rows, which flips bit 3 of the row and with it bsw's bit 3
+// (byte XOR 128) on odd k.  At N <= 128 the rows keep their swizzle.
+template <int N>
+__device__ __forceinline__ constexpr int sb_flip(int k) { return N == 256 ? 128 * (k & 1) : 0; }
 // masked decay matrix rows (128 bytes): chunk c of row r at c ^ msw(r)
 __device__ __forceinline__ int msw(int r) { return (r >> 1) & 7; }
 
@@ -127,14 +147,19 @@ struct LaneOffs {
     static constexpr int NT = N / 16, KS = N / 32;
     static constexpr int RB = N * 2;          // bytes per Bm / Cm row
     static constexpr int CPR = N / 8;         // 16-byte chunks per Bm / Cm row
+    // At N = 256 the pieces in the second 256 bytes of a row sit exactly 256
+    // bytes after those in the first (the swizzles permute chunks within each
+    // half), so only the first half's offsets are kept: KSO k-steps of Cm,
+    // NTO n-tiles of Bm; the rest add (index / KSO or NTO) * 256.
+    static constexpr int KSO = N == 256 ? KS / 2 : KS, NTO = N == 256 ? NT / 2 : NT;
     int xtr;          // X, transposing reads:    + ks*4096 (+512 for rows +4)
     int mm[2];        // Mm, fragment reads (by ks): + it*2048
     int mw;           // Mm, tile writes:         + 16 ti * 128, chunk bytes ^ 32 tj
-    int ct[KS][2];    // Ct, pieces n0 and n1:    + it*16*RB, chunk bytes ^ csw_tile_bytes(it)
-    int bt[NT];       // Bt, transposing reads:   + ks*32*RB (+4*RB for rows +4)
+    int ct[KSO][2];   // Ct, pieces n0 and n1:    + it*(16*RB + ct_pad), chunk bytes ^ csw_tile_bytes(it)
+    int bt[NTO];      // Bt, transposing reads:   + ks*32*RB (+4*RB for rows +4)
     int sx;           // x stage writes (state waves):       + k*4096
     int gx;           // x global loads (state waves):       + k*32*H*P*2
-    int sb;           // Bm stage writes (output waves):     + k*(256/CPR)*RB
+    int sb;           // Bm stage writes (output waves):     ^ sb_flip(k), + k*(256/CPR)*RB
     int sc[N / 32];   // Cm stage writes (output waves), by k
     int gb;           // Bm, Cm global loads (output waves): + k*(256/CPR)*G*N*2
     int gd;           // dt loads
@@ -152,14 +177,14 @@ __device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, 
     o.mm[1] = lrow * 128 + (((4 + lgrp) ^ msw(lrow)) * 16);
     o.mw = lrow * 128 + (((lgrp >> 1) ^ msw(lrow)) * 16) + (lgrp & 1) * 8;
 #pragma unroll
-    for (int ks = 0; ks < O::KS; ++ks)
+    for (int ks = 0; ks < O::KSO; ++ks)
 #pragma unroll
         for (int wh = 0; wh < 2; ++wh) {
             const int n = 32 * ks + 16 * wh + 4 * lgrp;
             o.ct[ks][wh] = lrow * O::RB + (((n >> 3) ^ csw<N>(lrow)) * 16) + (n & 7) * 2;   // tile 0
         }
 #pragma unroll
-    for (int t = 0; t < O::NT; ++t) {
+    for (int t = 0; t < O::NTO; ++t) {
         const int col = 16 * t + 4 * qa;
         o.bt[t] = r * O::RB + (((col >> 3) ^ bsw<N>(r)) * 16) + (col & 7) * 2;
     }
@@ -169,11 +194,11 @@ __device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, 
         o.sx = j * 128 + ((c ^ xsw(j)) * 16);   // row j + 32 has the same swizzle
         o.gx = (int)(((int64_t)j * H * kP + 8 * c) * 2);
         const int jb = u / O::CPR, cb = u % O::CPR;
-        o.sb = jb * O::RB + ((cb ^ bsw<N>(jb)) * 16);   // rows jb + 256k/CPR: same swizzle
+        o.sb = jb * O::RB + ((cb ^ bsw<N>(jb)) * 16);   // rows jb + 256k/CPR: see sb_flip
 #pragma unroll
         for (int k = 0; k < N / 32; ++k) {
             const int jk = jb + k * (256 / O::CPR);
-            o.sc[k] = jk * O::RB + ((cb ^ csw<N>(jk)) * 16);
+            o.sc[k] = jk * O::RB + (jk >> 4) * ct_pad<N> + ((cb ^ csw<N>(jk)) * 16);
         }
         o.gb = (int)(((int64_t)jb * G * N + 8 * cb) * 2);
     }

@@ -83,9 +83,10 @@ def test_workspace_size(lib):
     states = align(B * nc * H * P * N * 4) + align(B * H * nc * 4)
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, STAGED) == states + align(gram)
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, REFERENCE) == states
-    # N = 256 runs staged under AUTO; float32 runs the reference
+    # N = 256 runs the per-sequence scan under AUTO too; float32 runs the reference
     assert lib.ssd_chunk_scan_workspace_size(1, 1000, 4, P, 1, 256, 128, 1) == \
-        lib.ssd_chunk_scan_workspace_size_algo(1, 1000, 4, P, 1, 256, 128, 1, STAGED)
+        lib.ssd_chunk_scan_workspace_size_algo(1, 1000, 4, P, 1, 256, 128, 1, PIPE) == \
+        align(4 * 15 * (P * 256 + 1) * 4) + align(16 * 8192)
     assert lib.ssd_chunk_scan_workspace_size(1, 1000, 4, P, 1, 128, 128, 0) == \
         lib.ssd_chunk_scan_workspace_size_algo(1, 1000, 4, P, 1, 128, 128, 0, REFERENCE)
     # a short sequence is cut into at most its sub-blocks: two sub-blocks, one segment state
@@ -99,7 +100,6 @@ def test_workspace_size(lib):
     assert lib.ssd_chunk_scan_workspace_size(B, L, H, P, G, N, Q, 7) == 0
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, 9) == 0
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 0, PIPE) == 0      # float32
-    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, 256, Q, 1, PIPE) == 0    # N = 256
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, 32, G, N, Q, 1, STAGED) == 0   # P = 32
 
 

@@ -22,7 +22,10 @@ SMALL = [
     ("bf16_one_token", 2, 1, 4, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
     ("bf16_ragged_init", 2, 300, 4, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
     ("bf16_long_memory_q64", 1, 1000, 3, 64, 64, 1, 64, "bf16", False, "long_memory", MFMA_ALGOS),
-    ("bf16_no_decay_groups_n256", 2, 513, 4, 64, 256, 2, 128, "bf16", True, "no_decay", ["reference", "staged", "auto"]),
+    ("bf16_no_decay_groups_n256", 2, 513, 4, 64, 256, 2, 128, "bf16", True, "no_decay", MFMA_ALGOS),
+    ("bf16_n256_long_memory", 2, 1100, 4, 64, 256, 1, 256, "bf16", True, "long_memory", MFMA_ALGOS),
+    ("bf16_n256_decay_bursts_q64", 1, 900, 2, 64, 256, 1, 64, "bf16", True, "decay_bursts", MFMA_ALGOS),
+    ("bf16_n256_one_token", 2, 1, 2, 64, 256, 1, 256, "bf16", False, "default", MFMA_ALGOS),
     ("bf16_long_memory_n128_q128", 2, 777, 6, 64, 128, 3, 128, "bf16", True, "long_memory", MFMA_ALGOS),
     ("bf16_many_chunks", 1, 4100, 2, 64, 128, 1, 64, "bf16", True, "long_memory", MFMA_ALGOS),
     # stretches of very strong decay next to ordinary ones
@@ -229,7 +232,7 @@ def test_nothing_is_read_past_the_sequence_end(N, Q):
     for name in ("x", "dt", "Bm", "Cm"):
         dd[name] = padded(dd[name])
         assert dd[name].is_contiguous()
-    algos = ["reference", "staged"] + (["pipe"] if N <= 128 else [])
+    algos = ["reference", "staged", "pipe"]
     for algo in algos:
         announce(f"NaN past the end N{N} Q{Q} L{L} algo={algo}")
         y = torch.full_like(dd["x"], float("nan"))
@@ -250,6 +253,8 @@ BALANCED = [
     (2, 150, 320, 64, "default", True),
     (1, 257, 64 * 9 + 5, 128, "default", False),
     (1, 300, 65, 128, "long_memory", True),
+    (1, 300, 700, 256, "long_memory", True),
+    (2, 140, 64 * 5 + 3, 256, "default", False),
 ]
 
 
@@ -278,6 +283,9 @@ FEW_LONG = [
     # 767 sub-blocks over 256 workgroups: segments of 3 sub-blocks (a pair and
     # a lone one), the last ragged
     (1, 1, 767 * 64 - 5, 64, "default", True),
+    (1, 3, 5000, 256, "long_memory", True),
+    (1, 1, 64 * 40 + 9, 256, "default", True),
+    (2, 5, 3000, 256, "decay_bursts", True),
 ]
 
 

@@ -51,13 +51,13 @@ def test_no_alloc_matches_the_allocating_entry_point():
 
 def test_no_alloc_refuses_shapes_beyond_its_scratch():
     import selective_state_space_chunk_amd as ssd
-    # N = 256 runs the staged form, whose block states need 268 MB here
+    # float32 runs the reference kernels, whose block states need 33.6 MB here
     B, L, H, N = 1, 16384, 8, 256
-    need = ssd.ssd_chunk_scan_workspace_size(B, L, H, 64, 1, N, 256, torch.bfloat16)
+    need = ssd.ssd_chunk_scan_workspace_size(B, L, H, 64, 1, N, 256, torch.float32)
     assert need > ssd.NOALLOC_SCRATCH_BYTES
-    x = torch.zeros((B, L, H, 64), dtype=torch.bfloat16, device="cuda")
-    bm = torch.zeros((B, L, 1, N), dtype=torch.bfloat16, device="cuda")
-    announce(f"no-alloc refuses B{B} L{L} H{H} N{N} (workspace {need} bytes)")
+    x = torch.zeros((B, L, H, 64), dtype=torch.float32, device="cuda")
+    bm = torch.zeros((B, L, 1, N), dtype=torch.float32, device="cuda")
+    announce(f"no-alloc refuses fp32 B{B} L{L} H{H} N{N} (workspace {need} bytes)")
     with pytest.raises(ssd.SSDError) as ei:
         ssd.ssd_chunk_scan_fwd_noalloc(x, torch.zeros((B, L, H), device="cuda"), -torch.ones(H, device="cuda"),
                                        bm, bm, torch.zeros(H, device="cuda"), None, 256, torch.empty_like(x))
