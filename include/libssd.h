@@ -78,8 +78,9 @@ typedef enum {
 
 /* Which kernel sequence evaluates the chunk scan.  All give the same result
  * up to rounding.  SSD_ALGO_AUTO picks by shape and dtype: SSD_ALGO_PIPE
- * wherever it covers the shape, else SSD_ALGO_STAGED for the other bfloat16
- * shapes with P == 64, else SSD_ALGO_REFERENCE. */
+ * wherever it covers the shape (bfloat16, P in {64, 128}, N in {64, 128,
+ * 256}), else SSD_ALGO_STAGED where it does (bfloat16, P == 64), else
+ * SSD_ALGO_REFERENCE. */
 typedef enum {
     SSD_ALGO_AUTO = 0,
     SSD_ALGO_REFERENCE = 1,   /* float32 vector arithmetic, three kernels, every supported shape */
@@ -150,8 +151,9 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
  * workspace of ssd_chunk_scan_workspace_size_algo(..., algo) bytes.  An
  * algorithm that does not cover the shape or dtype returns
  * SSD_ERR_UNSUPPORTED: SSD_ALGO_STAGED and SSD_ALGO_PIPE need SSD_DTYPE_BF16
- * and P == 64; SSD_ALGO_STAGED takes N in {64, 128, 256}, SSD_ALGO_PIPE N in
- * {64, 128}.  SSD_ALGO_PIPE walks every (batch, head) sequence in 64-token
+ * and N in {64, 128, 256}; SSD_ALGO_STAGED takes P == 64, SSD_ALGO_PIPE P in
+ * {64, 128} (a head of 128 channels is scanned as two heads of 64 sharing
+ * dt, A and D).  SSD_ALGO_PIPE walks every (batch, head) sequence in 64-token
  * sub-blocks whatever chunk_size is (the result is the same up to rounding)
  * and spreads sequences over the device's compute units in time segments
  * when there are fewer of them than compute units, or fewer than twice as many.
@@ -199,7 +201,7 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
  * for every token and final_state (nullable) is the state after the row's
  * last token, that of its last sequence.  Other arguments and layouts as
  * ssd_chunk_scan_fwd; dt must be non-negative (its magnitude is used).
- * Covered: bfloat16, P = 64, N = 64 or 128 (else SSD_ERR_UNSUPPORTED).
+ * Covered: bfloat16, P = 64 or 128, N = 64 or 128 (else SSD_ERR_UNSUPPORTED).
  * The workspace (size from ssd_chunk_scan_varlen_workspace_size: that of
  * SSD_ALGO_PIPE plus B*L*H floats) is owned by the caller;
  * asynchronous on `stream`; no allocation.

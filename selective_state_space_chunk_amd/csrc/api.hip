@@ -12,7 +12,7 @@ hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws);
 bool mfma_supported(int64_t P, int64_t N, int64_t Q);
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q);
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws);
-bool pipe_supported(int64_t H, int64_t G, int64_t N);
+bool pipe_supported(int64_t H, int64_t P, int64_t G, int64_t N);
 bool block_prologue_supported(int64_t HP, int64_t GN, int64_t H, int64_t W);
 hipError_t launch_block_prologue(const void *zx, const float *conv_w, const float *conv_b, const float *dt_bias,
                                  void *x, void *Bm, void *Cm, float *dt, int64_t B, int64_t L, int64_t H,
@@ -65,18 +65,20 @@ constexpr int64_t kSegStates = 256;
 constexpr int64_t kMaxChains = 65535;
 
 // The algorithm a call runs: `algo` itself, or for SSD_ALGO_AUTO the
-// per-sequence scan wherever it covers the shape, the staged matrix-core scan
-// for the other bfloat16 shapes with P = 64, and the float32 reference
-// otherwise.  -1 when `algo` does not cover the shape or dtype.
+// per-sequence scan wherever it covers the shape (bfloat16, P = 64 or 128,
+// N = 64, 128 or 256), else the staged matrix-core scan where it does
+// (bfloat16, P = 64), else the float32 reference.  -1 when `algo` does not
+// cover the shape or dtype.
 int resolve(int64_t H, int64_t P, int64_t G, int64_t N, int64_t Q, ssd_dtype dtype, ssd_algo algo) {
-    const bool mfma_ok = dtype == SSD_DTYPE_BF16 && mfma_supported(P, N, Q);
+    const bool bf16 = dtype == SSD_DTYPE_BF16;
+    const bool staged_ok = bf16 && mfma_supported(P, N, Q);
+    const bool pipe_ok = bf16 && pipe_supported(H, P, G, N);
     switch (algo) {
         case SSD_ALGO_AUTO:
-            if (!mfma_ok) return SSD_ALGO_REFERENCE;
-            return pipe_supported(H, G, N) ? SSD_ALGO_PIPE : SSD_ALGO_STAGED;
+            return pipe_ok ? SSD_ALGO_PIPE : staged_ok ? SSD_ALGO_STAGED : SSD_ALGO_REFERENCE;
         case SSD_ALGO_REFERENCE: return SSD_ALGO_REFERENCE;
-        case SSD_ALGO_STAGED: return mfma_ok ? SSD_ALGO_STAGED : -1;
-        case SSD_ALGO_PIPE: return mfma_ok && pipe_supported(H, G, N) ? SSD_ALGO_PIPE : -1;
+        case SSD_ALGO_STAGED: return staged_ok ? SSD_ALGO_STAGED : -1;
+        case SSD_ALGO_PIPE: return pipe_ok ? SSD_ALGO_PIPE : -1;
     }
     return -1;
 }
@@ -99,9 +101,10 @@ Layout layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, 
         l.gram = off; off = align_up(off + gram_bytes(B, L, G, Q));
     }
     if (algo == SSD_ALGO_PIPE) {
-        const int64_t cut = B * H * (nsb > 1 ? nsb - 1 : 0);
+        // heads of 64 channels (a head of P = 128 is scanned as two)
+        const int64_t cut = B * H * (P / 64) * (nsb > 1 ? nsb - 1 : 0);
         const int64_t nseg = cut < kSegStates ? cut : kSegStates;
-        l.seg_floats = (size_t)(nseg * (P * N + 1));
+        l.seg_floats = (size_t)(nseg * (64 * N + 1));
         l.seg = off;  off = align_up(off + l.seg_floats * sizeof(float));
         l.gram = off; off = align_up(off + gram_bytes(B, L, G, 64));
     }
@@ -321,8 +324,7 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
     if (has_work && !seq_idx) return SSD_ERR_INVALID_ARG;
     if (((uintptr_t)seq_idx & 3u) != 0) return SSD_ERR_INVALID_ARG;
     if (chunk_size <= 0) return SSD_ERR_INVALID_ARG;
-    if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !mfma_supported(P, N, chunk_size) ||
-        !pipe_supported(H, G, N) || N > 128)
+    if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !pipe_supported(H, P, G, N) || N > 128)
         return SSD_ERR_UNSUPPORTED;
     if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
     if ((L + chunk_size - 1) / chunk_size > 0x7fffffff) return SSD_ERR_UNSUPPORTED;

@@ -67,7 +67,9 @@ struct Args {
     float *final_state;
     const __bf16 *gram;
     float *seg;              // segment states [nextra][nseg-1][P][N], then their log2 decays [nextra][nseg-1]
-    int64_t L, H, G, nsb;
+    int64_t L, H, G, nsb;    // H: heads of 64 channels (a head of P = 128 is two of them)
+    int64_t Hd;              // heads of dt, A and D (the caller's H)
+    int hs;                  // heads of 64 channels per caller head (P / 64)
     int nmain;               // sequences run whole, one per workgroup (0: every sequence is cut)
     int nextra;              // further sequences, each cut into nseg segments of seglen sub-blocks;
     int nseg, seglen;        //   segment q of extra sequence e runs on workgroup q*nextra + e
@@ -142,7 +144,7 @@ __device__ __forceinline__ void load_g_at(uint2 (&g)[3], const Args &a, int64_t 
 // dt of one token of a sub-block (element offset dof of its first row; token
 // offset gdq in bytes), 0 past its q tokens.
 __device__ __forceinline__ float load_dt_at(const Args &a, int64_t dof, int q, int gdq) {
-    const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.H + 1) * 4) : 0);
+    const rsrc_t rd = rsrc(a.dt + dof, q > 0 ? (int)(((int64_t)(q - 1) * a.Hd + 1) * 4) : 0);
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, gdq, 0, 0));
 }
 
@@ -206,7 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
-    const float Ah2v = a.A[h] * kLog2e, Dhv = a.D[h];
+    const int64_t dh = h / a.hs;   // the caller's head: dt, A and D
+    const float Ah2v = a.A[dh] * kLog2e, Dhv = a.D[dh];
     const bool has_x = (int)blockIdx.x < a.nextra * a.nseg;
     const int xe = has_x ? (int)blockIdx.x % a.nextra : 0;
     const int xq = has_x ? (int)blockIdx.x / a.nextra : 0;
@@ -214,7 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int64_t bx = __builtin_amdgcn_readfirstlane((int)(xchain / a.H));
     const int64_t hx = __builtin_amdgcn_readfirstlane((int)(xchain % a.H));
     const int64_t gx = __builtin_amdgcn_readfirstlane((int)(hx / (a.H / a.G)));
-    const float Ahx2 = a.A[hx] * kLog2e, Dhx = a.D[hx];
+    const int64_t dhx = hx / a.hs;
+    const float Ahx2 = a.A[dhx] * kLog2e, Dhx = a.D[dhx];
     const int seg0 = xq * a.seglen;
     const int xlen = has_x ? (nsub - seg0 < a.seglen ? nsub - seg0 : a.seglen) : 0;
     const int T = nown + xlen;
@@ -227,9 +231,9 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     // element offsets of step tau's first row in x / y, dt, Bm / Cm and the
     // gram tiles: the own sequence's base, or the segment's base shifted so
     // that the step index addresses it directly
-    const int64_t SX = kSub * a.H * kP, SD = kSub * a.H, SB = kSub * a.G * N, SG = kSub * kSub;
+    const int64_t SX = kSub * a.H * kP, SD = kSub * a.Hd, SB = kSub * a.G * N, SG = kSub * kSub;
     const int64_t xo0 = (b * a.L * a.H + h) * kP, xo1 = (bx * a.L * a.H + hx) * kP + (int64_t)(seg0 - nown) * SX;
-    const int64_t do0 = b * a.L * a.H + h, do1 = bx * a.L * a.H + hx + (int64_t)(seg0 - nown) * SD;
+    const int64_t do0 = b * a.L * a.Hd + dh, do1 = bx * a.L * a.Hd + dhx + (int64_t)(seg0 - nown) * SD;
     const int64_t bo0 = (b * a.L * a.G + g) * N, bo1 = (bx * a.L * a.G + gx) * N + (int64_t)(seg0 - nown) * SB;
     const int64_t go0 = (b * a.G + g) * a.nsb * SG, go1 = (bx * a.G + gx) * a.nsb * SG + (int64_t)(seg0 - nown) * SG;
     auto x_at = [&](int tau) { return (tau < nown ? xo0 : xo1) + tau * SX; };
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     const int pq = wave & 3;
     const bool compute_wave = wave < 4;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
+    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G, a.Hd);
     WaveDecays &wd = sm.wd[wave];
     // whole rows of y of step tau from YS[slot] to global memory (compute waves;
     // thread u = tid % 256: rows u/8 and u/8 + 32, chunk u%8)
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     constexpr bool kPrepX = PipeSmem<N>::kCSlots == 1;
     const bool x_wave = compute_wave != kPrepX;
     const int dq_tok = 16 * pq + (lane & 15);
-    const int gdq = dq_tok * (int)(a.H * 4);
+    const int gdq = dq_tok * (int)(a.Hd * 4);
     BulkX xbulk[2];
     float dq[2];
     // x of sub-block 0 staged; x of sub-blocks 1 and 2 and the dt quarters of
@@ -691,7 +695,8 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
-    const float Ah2 = a.A[h] * kLog2e;
+    const int64_t dh = h / a.hs;
+    const float Ah2 = a.A[dh] * kLog2e;
     const int s0 = q * a.seglen, len = a.seglen;   // segments before the last are full and inside the sequence
     const int nsteps = (len + 1) / 2;
 
@@ -699,7 +704,7 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wq = wave & 3, nq = wq & 1, pp = wq >> 1;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G);
+    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G, a.Hd);
     const int xtr1 = lane_offsets<N>(tid, 2 * pp + 1, a.H, a.G).xtr;   // second p-tile
     // staging: thread (u = tid % 256, half nh) stages x chunk nh (token
     // u / 8 + 32 nh) and Bm chunks nh*KB .. +KB-1 of u, of each sub-block
@@ -733,7 +738,7 @@ __device__ __forceinline__ void seg_state_block(const Args &a, int blk) {
             const int k = sub_at(st, c);
             const int qn = sub_tokens(a, s0 + k);
             const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
-            const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
+            const rsrc_t rd = rsrc(a.dt + row0 * a.Hd + dh, (int)(((int64_t)(qn - 1) * a.Hd + 1) * 4));
             dts[slot][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
         }
     };
@@ -899,14 +904,15 @@ __device__ __forceinline__ void seg_state_block_wide(const Args &a, int blk) {
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
-    const float Ah2 = a.A[h] * kLog2e;
+    const int64_t dh = h / a.hs;
+    const float Ah2 = a.A[dh] * kLog2e;
     const int s0 = q * a.seglen, len = a.seglen;   // segments before the last are full and inside the sequence
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nq = wave & 3, pp = wave >> 2;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G);
+    const LaneOffs<N> o = lane_offsets<N>(tid, 2 * pp, a.H, a.G, a.Hd);
     const int xtr1 = lane_offsets<N>(tid, 2 * pp + 1, a.H, a.G).xtr;   // second p-tile
     // staging: thread (u = tid % 256, half nh) stages x chunk nh (token
     // u / 8 + 32 nh) and Bm chunks nh*KB .. +KB-1 of u
@@ -932,7 +938,7 @@ __device__ __forceinline__ void seg_state_block_wide(const Args &a, int blk) {
         const int k = sub_at(st);
         const int qn = sub_tokens(a, s0 + k);
         const int64_t row0 = b * a.L + (int64_t)(s0 + k) * kSub;
-        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(qn - 1) * a.H + 1) * 4));
+        const rsrc_t rd = rsrc(a.dt + row0 * a.Hd + dh, (int)(((int64_t)(qn - 1) * a.Hd + 1) * 4));
         dts[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
     };
     // wave 0: weights and log2 decay of sub-block st into ring slot st % 3
@@ -1092,7 +1098,11 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     //  - at most half as many sequences as compute units: every sequence is
     //    cut into segments, one workgroup per segment;
     //  - otherwise one workgroup per sequence.
-    const int64_t chains = sa.B * sa.H;
+    // a head of P = 128 is scanned as two heads of 64 channels (the state
+    // rows p < 64 and p >= 64 never mix), sharing dt, A and D
+    const int hs = (int)(sa.P / kP);
+    const int64_t Hk = sa.H * hs;
+    const int64_t chains = sa.B * Hk;
     const int cus = device_cus();
     int nmain = (int)chains, nextra = 0, nseg = 1, seglen = (int)nsb;
     if (cus > 0 && chains > cus && chains < 2 * (int64_t)cus && nsb >= 2) {
@@ -1121,7 +1131,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     if (e != hipSuccess) return e;
     Args a{(const __bf16 *)sa.x, sa.dt, sa.A, (const __bf16 *)sa.Bm, (const __bf16 *)sa.Cm, sa.D,
            sa.init, (__bf16 *)sa.y, sa.final_state, (const __bf16 *)ws.gram, ws.seg,
-           sa.L, sa.H, sa.G, nsb, nmain, nextra, nseg, seglen};
+           sa.L, Hk, sa.G, nsb, sa.H, hs, nmain, nextra, nseg, seglen};
     if (nextra > 0 && nseg > 1) {
         const int nsegwg = nextra * (nseg - 1);
         prep_kernel<N, kV><<<dim3((unsigned)(nsegwg + nsb * sa.B * sa.G)), 512, 0, sa.stream>>>(a, nsegwg);
@@ -1137,10 +1147,10 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
 
 }  // namespace
 
-bool pipe_supported(int64_t H, int64_t G, int64_t N) {
-    if (!(N == 64 || N == 128 || N == 256)) return false;
+bool pipe_supported(int64_t H, int64_t P, int64_t G, int64_t N) {
+    if (!(N == 64 || N == 128 || N == 256) || !(P == 64 || P == 128)) return false;
     const int64_t lim = (int64_t)1 << 31;
-    return (int64_t)kSub * H * kP * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
+    return (int64_t)kSub * H * P * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
 }
 
 hipError_t launch_pipe_scan(const ScanArgs &a, const Workspace &ws) {

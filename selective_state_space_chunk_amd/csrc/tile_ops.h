@@ -166,8 +166,9 @@ struct LaneOffs {
     int gy;           // y stores:                + it*16*H*P*2
 };
 
+// H: heads of x and y (64 columns each); Hd: heads of dt (0: H).
 template <int N>
-__device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, int64_t G) {
+__device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, int64_t G, int64_t Hd = 0) {
     using O = LaneOffs<N>;
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4, qa = lane & 3, qq = (lane & 15) >> 2;
     O o;
@@ -202,7 +203,7 @@ __device__ __forceinline__ LaneOffs<N> lane_offsets(int tid, int pq, int64_t H, 
         }
         o.gb = (int)(((int64_t)jb * G * N + 8 * cb) * 2);
     }
-    o.gd = (int)((int64_t)lane * H * 4);
+    o.gd = (int)((int64_t)lane * (Hd ? Hd : H) * 4);
     o.gy = (int)(((int64_t)lrow * H * kP + 16 * pq + 4 * lgrp) * 2);
     return o;
 }

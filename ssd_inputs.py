@@ -82,6 +82,10 @@ WORKLOADS: Dict[str, Workload] = {
                           dtype="bf16", init=False, index=3),
     "long_n256": Workload("long_n256", B=1, L=65536, H=24, P=64, N=256, G=1, chunk=256,
                           dtype="bf16", init=False, index=3),
+    # the 2.7B layer's 5120 inner channels as 40 heads of the other head dim
+    # the pages give (P = 128)
+    "m2_2p7b_p128": Workload("m2_2p7b_p128", B=4, L=4096, H=40, P=128, N=128, G=1, chunk=256,
+                             dtype="bf16", init=True, index=5),
     # recurrent decode: 1024 consecutive single-token steps from a random state
     "decode_2p7b": Workload("decode_2p7b", B=256, L=1, H=80, P=64, N=128, G=1, chunk=256,
                             dtype="bf16", init=True, steps=1024, index=4),

@@ -101,6 +101,10 @@ def test_workspace_size(lib):
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 1, 9) == 0
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, P, G, N, Q, 0, PIPE) == 0      # float32
     assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, 32, G, N, Q, 1, STAGED) == 0   # P = 32
+    assert lib.ssd_chunk_scan_workspace_size_algo(B, L, H, 128, G, N, Q, 1, STAGED) == 0  # P = 128
+    # P = 128 runs the per-sequence scan as twice the heads of 64 channels
+    assert lib.ssd_chunk_scan_workspace_size(2, 640, 3, 128, 1, N, Q, 1) == \
+        align(2 * 6 * 9 * (64 * N + 1) * 4) + align(2 * 10 * 8192)
 
 
 def fake(addr):

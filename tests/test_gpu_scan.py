@@ -33,6 +33,10 @@ SMALL = [
     ("bf16_strong_decay_n64_groups", 1, 700, 4, 64, 64, 2, 64, "bf16", True, "strong_decay", MFMA_ALGOS),
     # long runs of ordinary decay
     ("bf16_default_long", 1, 3000, 2, 64, 128, 1, 256, "bf16", True, "default", MFMA_ALGOS),
+    # head dim 128 (two heads of 64 channels sharing dt, A and D on the matrix cores)
+    ("bf16_p128_ragged", 2, 700, 4, 128, 128, 1, 256, "bf16", True, "long_memory", ["reference", "pipe", "auto"]),
+    ("bf16_p128_n256_groups", 1, 600, 4, 128, 256, 2, 128, "bf16", True, "default", ["reference", "pipe"]),
+    ("bf16_p128_n64_bursts", 1, 1000, 6, 128, 64, 3, 64, "bf16", False, "decay_bursts", ["reference", "pipe"]),
 ]
 
 
@@ -51,7 +55,7 @@ def test_small_shapes_match_oracle(case):
         assert ef <= TOL[dtype], (algo, ef)
 
 
-WORKLOADS = ["tiny_fp32", "m2_130m", "m2_2p7b", "long_n128", "long_n256"]
+WORKLOADS = ["tiny_fp32", "m2_130m", "m2_2p7b", "long_n128", "long_n256", "m2_2p7b_p128"]
 
 
 @pytest.mark.parametrize("wname", WORKLOADS)
@@ -301,3 +305,27 @@ def test_few_long_sequences_are_cut_into_segments(case):
         ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
         print(f"    call {rep}: y err {ey:.3e}  final err {ef:.3e}", flush=True)
         assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+# Head dim 128 in the launch shapes of the per-sequence scan: few sequences
+# cut into segments, more sequences than compute units, one token.
+# (B, L, H, N, regime, init); P = 128
+P128 = [
+    (1, 3000, 2, 128, "long_memory", True),
+    (1, 700, 150, 64, "default", True),
+    (2, 5000, 3, 256, "long_memory", False),
+    (3, 1, 4, 128, "default", True),
+]
+
+
+@pytest.mark.parametrize("case", P128, ids=[f"B{c[0]}_L{c[1]}_H{c[2]}_N{c[3]}" for c in P128])
+def test_head_dim_128_launch_shapes(case):
+    B, L, H, N, regime, init = case
+    d = si.make_scan_inputs(B, L, H, 128, N, 1, dtype="bf16", init=init, seed=1900 + H + L, regime=regime)
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+    announce(f"P128 B{B} L{L} H{H} N{N} {regime} algo=pipe")
+    y, fin = gpu_scan(dd, 256, algo="pipe")
+    ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+    print(f"    y err {ey:.3e}  final err {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]

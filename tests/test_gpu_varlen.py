@@ -70,6 +70,20 @@ def test_varlen_matches_oracle(case):
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
 
 
+def test_varlen_head_dim_128():
+    # P = 128: every head scanned as two heads of 64 channels sharing dt (and
+    # its reset flags); the rows are cut into segments (6 such heads)
+    B, L, H, N = 1, 2500, 3, 128
+    d = si.make_scan_inputs(B, L, H, 128, N, 1, dtype="bf16", init=True, seed=4701)
+    seq = si.make_seq_idx(B, L, mean_len=300.0, seed=4702)
+    y_ref, f_ref = _oracle(d, seq)
+    announce(f"varlen P128: B{B} L{L} H{H} N{N}, sequences per row {[int(seq[b, -1]) + 1 for b in range(B)]}")
+    y, fin = _gpu(to_device(d, "bf16"), seq)
+    ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+    print(f"    y {ey:.3e}  final {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
+
+
 def test_varlen_full_size_sampled_heads():
     # the Mamba-2 2.7B layer shape with documents packed into each row
     B, L, H, N = 4, 4096, 80, 128
