@@ -42,11 +42,19 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_m2_2p7b.json")
 WORKLOAD_NAMES = {"m2_2p7b": "mamba2_2.7b_layer_ssd_chunk_scan", "m2_130m": "mamba2_130m_layer_ssd_chunk_scan",
                   "tiny_fp32": "tiny_fp32_ssd_chunk_scan", "long_n128": "long_sequence_n128_ssd_chunk_scan",
-                  "long_n256": "long_sequence_n256_ssd_chunk_scan"}
+                  "long_n256": "long_sequence_n256_ssd_chunk_scan",
+                  "m2_2p7b_p128": "mamba2_2.7b_layer_head_dim_128_ssd_chunk_scan"}
+# what each workload is, for the metric string of its line
+WORKLOAD_DESC = {"m2_2p7b": "Mamba-2 2.7B layer shape", "m2_130m": "Mamba-2 130M layer shape",
+                 "tiny_fp32": "tiny fp32 shape", "long_n128": "long-sequence shape, N=128",
+                 "long_n256": "long-sequence shape, N=256",
+                 "m2_2p7b_p128": "Mamba-2 2.7B layer channels as 40 heads of 128"}
+HEADLINE_METRIC = "SSD chunk-scan fwd tokens/s at Mamba-2 2.7B layer shape; % of roofline"
 # the sources whose kernels run in one scan launch at this workload
 SCAN_SOURCES = ["pipe_scan.hip", "tile_ops.h", "mfma_scan.hip", "api.hip", "common.h"]
-# and in one backward call
+# and in one backward call, and one decode step
 BWD_SOURCES = ["bwd_scan.hip", "api.hip", "common.h"]
+STEP_SOURCES = ["step.hip", "api.hip", "common.h"]
 BWD_KERNELS = ("state_scans", "chunk_grad", "reduce_head")
 
 
@@ -58,10 +66,18 @@ def scan_sources_digest(files=SCAN_SOURCES) -> str:
     return h.hexdigest()
 
 
-def scan_algorithmic(w):
+def per_sequence_scan(w):
+    """Whether the library's default path for this workload is the
+    per-sequence scan, which walks 64-token sub-blocks whatever the chunk."""
+    return w.dtype == "bf16" and w.P in (64, 128) and w.N in (64, 128, 256)
+
+
+def scan_algorithmic(w, q=None):
     """Bytes every input read once + outputs written once; flops of the block
-    decomposition (causal halves of the quadratic terms)."""
-    B, L, H, P, N, G, Q = w.B, w.L, w.H, w.P, w.N, w.G, w.chunk
+    decomposition into blocks of q tokens (default: the chunk size) with the
+    causal halves of the quadratic terms."""
+    B, L, H, P, N, G = w.B, w.L, w.H, w.P, w.N, w.G
+    Q = q or w.chunk
     e = 2 if w.dtype == "bf16" else 4
     nc = -(-L // Q)
     byts = (2 * B * L * H * P * e          # x in, y out
@@ -388,21 +404,23 @@ def cpu_baseline(w, budget_s=15.0):
 
 
 def copy_bandwidth(device, mb=512, reps=10):
-    """Measured device-copy bandwidth (GB/s, bytes read + written) of a plain
-    `mb`-megabyte copy, median of `reps` event-timed launches: the practical
-    ceiling the scan's achieved bandwidth is also reported against."""
+    """Measured bandwidth (GB/s, bytes read + written) of the library's own
+    streaming copy (ssd_stream_copy) of `mb` megabytes, median of `reps`
+    event-timed launches: what a kernel with no arithmetic moves here, the
+    practical ceiling the achieved bandwidths are also reported against."""
     import torch
-    n = int(mb * 1e6) // 4
+    import selective_state_space_chunk_amd as ssd
+    n = int(mb * 1e6) // 16 * 4
     src = torch.ones(n, dtype=torch.float32, device=device)
     dst = torch.empty_like(src)
     for _ in range(2):
-        dst.copy_(src)
+        ssd.ssd_stream_copy(dst, src)
     torch.cuda.synchronize(device)
     times = []
     for _ in range(reps):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        dst.copy_(src)
+        ssd.ssd_stream_copy(dst, src)
         e.record()
         torch.cuda.synchronize(device)
         times.append(s.elapsed_time(e))
@@ -434,6 +452,18 @@ def scan_traffic():
     return t.get("bytes_per_launch")
 
 
+def step_traffic():
+    """HBM bytes per decode step from the same summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("step_sources_sha256") != scan_sources_digest(STEP_SOURCES):
+        return None
+    return t.get("step_bytes_per_call")
+
+
 def bwd_traffic():
     """HBM bytes per backward call from the same summary, or None."""
     try:
@@ -447,13 +477,15 @@ def bwd_traffic():
 
 
 def calibrate_copy(mb, steps):
-    """Only a plain device-to-device copy of `mb` megabytes, `steps` times."""
+    """Only the library's streaming copy (stream_copy) of `mb` megabytes,
+    `steps` times: the reference kernel for scaling the counters."""
     import torch
-    n = int(mb * 1e6) // 4
+    import selective_state_space_chunk_amd as ssd
+    n = int(mb * 1e6) // 16 * 4
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(steps):
-        dst.copy_(src)
+        ssd.ssd_stream_copy(dst, src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": steps}))
 
@@ -527,6 +559,16 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
                                     "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
         btotal += fk * f_fetch + wk * f_write
     out["bwd_bytes_per_call"] = btotal if out["bwd_kernels"] else None
+    out["step_sources_sha256"] = scan_sources_digest(STEP_SOURCES)
+    out["step_kernels"] = {}
+    try:
+        fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", "step_kernel")
+        wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", "step_kernel")
+        out["step_kernels"]["step_kernel"] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
+                                              "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
+        out["step_bytes_per_call"] = fk * f_fetch + wk * f_write
+    except SystemExit:
+        out["step_bytes_per_call"] = None
     out["block_kernels"] = {}
     for name in ("prologue_kernel", "gated_norm_kernel"):
         try:
@@ -562,7 +604,7 @@ def main():
     ap.add_argument("--xcds", type=int, default=8)
     ap.add_argument("--workload", default="m2_2p7b",
                     help="scan workload to time (m2_2p7b is the headline; tiny_fp32, m2_130m, long_n128, "
-                         "long_n256 are the other scan shapes)")
+                         "long_n256 and m2_2p7b_p128 are the other scan shapes)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.copy_mb)
@@ -588,11 +630,18 @@ def main():
     wall, per = time_scan(w, args.steps, args.warmup, device)
     ms_step = wall * 1000.0 / args.steps
     kern_ms = sum(per) / len(per)
-    byts, flops = scan_algorithmic(w)
+    # the flops of the decomposition the kernels run: 64-token sub-blocks on
+    # the per-sequence scan, blocks of the chunk size otherwise
+    block = 64 if per_sequence_scan(w) else w.chunk
+    byts, flops = scan_algorithmic(w, block)
     achieved = byts / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.L
+    metric = HEADLINE_METRIC if headline else \
+        f"SSD chunk-scan fwd tokens/s at {WORKLOAD_DESC.get(w.name, w.name)}; % of roofline"
+    kernels = (f"gram tiles (gram_kernel, or prep_kernel<{w.N}> with the segment states) + pipe_kernel<{w.N}>"
+               if per_sequence_scan(w) else "staged or reference kernels")
     out = {
-        "metric": "SSD chunk-scan fwd tokens/s at Mamba-2 2.7B layer shape; % of roofline",
+        "metric": metric,
         "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -606,20 +655,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES.get(w.name, w.name), "batch": w.B, "seq_len": w.L,
                    "heads": w.H, "head_dim": w.P, "state": w.N, "groups": w.G, "chunk": w.chunk,
-                   "init_state": bool(w.init), "parallelism": "single_gpu"},
+                   "block_tokens": block, "init_state": bool(w.init), "parallelism": "single_gpu"},
         "kernel_ms": {"mean": kern_ms, "median": per[len(per) // 2], "p10": per[len(per) // 10],
                       "p90": per[(9 * len(per)) // 10]},
-        "roofline": {"bound": "hbm", "kernels": "prep_kernel<128> (segment states and gram tiles) + pipe_kernel<128> (one ssd_chunk_scan_fwd call)",
+        "roofline": {"bound": "hbm", "kernels": kernels + " (one ssd_chunk_scan_fwd call)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic() if headline else None,
-                     "algorithmic_bytes": byts, "algorithmic_flops": flops,
+                     "algorithmic_bytes": byts, "algorithmic_flops": flops, "flops_block_tokens": block,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
     copy_gbs = copy_bandwidth(device)
     out["roofline"]["copy_gbs"] = copy_gbs
     out["roofline"]["frac_of_copy"] = achieved / copy_gbs
-    if not headline:
-        del out["roofline"]["kernels"]
     if not args.no_decode:
         B, H, P, N, G = 256, 80, 64, 128, 1
         sp = time_step(B, H, P, N, G, max(20, args.steps // 2), 5, device)
@@ -627,12 +674,12 @@ def main():
         sb = step_algorithmic(B, H, P, N, G)
         out["decode"] = {"workload": "mamba2_2.7b_layer_ssd_step", "batch": B, "heads": H,
                          "head_dim": P, "state": N, "us_per_step": smean * 1000.0,
-                         "tokens_per_s": B / (smean * 1e-3),
+                         "tokens_per_s": B / (smean * 1e-3), "kernel": f"step_kernel<bf16, {P}, {N}>",
                          "roofline": {"bound": "hbm", "achieved": sb / (smean * 1e-3) / 1e9,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
-                                      "algorithmic_bytes": sb}}
+                                      "traffic": step_traffic(), "algorithmic_bytes": sb}}
     if not args.no_backward and headline:
         bp = time_backward(w, max(10, args.steps // 5), 3, device)
         bmean = sum(bp) / len(bp)

@@ -343,6 +343,15 @@ ssd_status ssd_step(float *state, const void *x, const float *dt, const float *A
                     int64_t B, int64_t H, int64_t P, int64_t G, int64_t N,
                     ssd_dtype dtype, hipStream_t stream);
 
+/*
+ * A plain device-to-device copy of `bytes` bytes: the bandwidth reference of
+ * the benchmark (what a kernel with no arithmetic streams on this device).
+ * src and dst are device pointers, 16-byte aligned, not overlapping; bytes a
+ * multiple of 16 (else SSD_ERR_INVALID_ARG).  Streamed in 4 KB pieces per
+ * workgroup with non-temporal loads and stores; asynchronous on `stream`.
+ */
+ssd_status ssd_stream_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
     lib.ssd_step.restype = ctypes.c_int
+    lib.ssd_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.ssd_stream_copy.restype = ctypes.c_int
     lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_varlen_workspace_size.restype = sz
     lib.ssd_chunk_scan_fwd_varlen.argtypes = [vp] * 11 + [sz] + [i64] * 7 + [ctypes.c_int, vp]
@@ -465,6 +467,17 @@ def ssd_chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, Bm: t
         chunk_size, code, _stream_handle(dev, stream))
     _check(st, "ssd_chunk_scan_bwd")
     return out
+
+
+def ssd_stream_copy(dst: torch.Tensor, src: torch.Tensor, *, stream=None) -> None:
+    """Plain device copy of src into dst (same size in bytes, contiguous): the
+    bandwidth reference the benchmark reports the kernels against."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must be contiguous tensors of the same size in bytes")
+    st = lib.ssd_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream_handle(src.device, stream))
+    _check(st, "ssd_stream_copy")
 
 
 def version() -> str:

@@ -28,6 +28,20 @@ def test_scan_bytes_at_the_2p7b_shape():
     assert bench.scan_algorithmic(w)[0] == xy + dt + bc + ad + states == 370_147_968
 
 
+def test_scan_flops_count_the_decomposition_that_runs():
+    # the per-sequence scan walks 64-token sub-blocks whatever the chunk size,
+    # so the flops the bench divides by are those of 64-token blocks
+    w = si.WORKLOADS["m2_2p7b"]
+    assert bench.per_sequence_scan(w) and bench.per_sequence_scan(si.WORKLOADS["long_n256"])
+    assert not bench.per_sequence_scan(si.WORKLOADS["tiny_fp32"])
+    B, L, H, P, N, q = 4, 4096, 80, 64, 128, 64
+    nc, tri = L // q, q * (q + 1) // 2
+    flops = (2 * B * nc * tri * N + 2 * B * nc * H * tri * P + 4 * B * L * H * P * N
+             + 2 * B * nc * H * P * N + 2 * B * L * H * P)
+    assert bench.scan_algorithmic(w, 64)[1] == flops
+    assert bench.scan_algorithmic(w)[1] > flops          # blocks of 256: larger quadratic terms
+
+
 def test_backward_and_block_bytes_at_the_2p7b_shape():
     w = si.WORKLOADS["m2_2p7b"]
     B, L, H, P, N = 4, 4096, 80, 64, 128
@@ -52,17 +66,19 @@ def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     copy_mb = 512.0
     # the copy reads and writes 512e6 bytes; its counters read 250,000 and 500,000 KiB
-    _counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copyBuffer", 250_000.0)])
-    _counter_csv(tmp_path / "cw", "WRITE_SIZE", [("copyBuffer", 500_000.0)])
+    _counter_csv(tmp_path / "cf", "FETCH_SIZE", [("stream_copy(unsigned int const*)", 250_000.0)])
+    _counter_csv(tmp_path / "cw", "WRITE_SIZE", [("stream_copy(unsigned int const*)", 500_000.0)])
     # two dispatches of each scan kernel, one of a backward kernel
     _counter_csv(tmp_path / "f", "FETCH_SIZE", [("void pipe_kernel<128, false>(Args)", 100.0),
                                                 ("void pipe_kernel<128, false>(Args)", 300.0),
                                                 ("void prep_kernel<128, false>(Args, int)", 10.0),
-                                                ("void chunk_grad<128>(BwdArgs)", 1000.0)])
+                                                ("void chunk_grad<128>(BwdArgs)", 1000.0),
+                                                ("void step_kernel<bf16, 64, 128>(float*)", 700.0)])
     _counter_csv(tmp_path / "w", "WRITE_SIZE", [("void pipe_kernel<128, false>(Args)", 50.0),
                                                 ("void pipe_kernel<128, false>(Args)", 50.0),
                                                 ("void prep_kernel<128, false>(Args, int)", 5.0),
-                                                ("void chunk_grad<128>(BwdArgs)", 400.0)])
+                                                ("void chunk_grad<128>(BwdArgs)", 400.0),
+                                                ("void step_kernel<bf16, 64, 128>(float*)", 600.0)])
     bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"), copy_mb)
     t = json.load(open(tmp_path / "traffic.json"))
     ff, fw = 512e6 / 250_000, 512e6 / 500_000
@@ -71,6 +87,7 @@ def test_counter_summary_scales_by_the_copy(tmp_path, monkeypatch):
     assert pipe["fetch_kib"] == pytest.approx(200.0) and pipe["write_kib"] == pytest.approx(50.0)   # per-dispatch means
     assert t["bytes_per_launch"] == pytest.approx(200.0 * ff + 50.0 * fw + 10.0 * ff + 5.0 * fw)
     assert t["bwd_bytes_per_call"] == pytest.approx(1000.0 * ff + 400.0 * fw)
+    assert t["step_bytes_per_call"] == pytest.approx(700.0 * ff + 600.0 * fw)
 
 
 def test_more_than_one_gpu_is_refused():

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "ssd_status_string", "ssd_chunk_scan_fwd_algo", "ssd_version",
               "ssd_chunk_scan_workspace_size_algo", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
               "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_varlen_workspace_size", "ssd_block_prologue",
-              "ssd_gated_norm", "ssd_selective_scan"):
+              "ssd_gated_norm", "ssd_selective_scan", "ssd_chunk_scan_fwd_noalloc", "ssd_stream_copy"):
         assert n in names
 
 
@@ -165,6 +165,15 @@ def test_step_rejects_bad_arguments_before_launch(lib):
     assert call(shape=(256, 80, 48, 1, 128)) == ssd.SSD_ERR_UNSUPPORTED
     assert call(dtype=3) == ssd.SSD_ERR_UNSUPPORTED
     assert call(shape=(0, 80, 64, 1, 128)) == ssd.SSD_OK                 # empty batch: no-op
+
+
+def test_stream_copy_rejects_bad_arguments_before_launch(lib):
+    import selective_state_space_chunk_amd as ssd
+    assert lib.ssd_stream_copy(fake(0x10000), fake(0x20000), 0, None) == ssd.SSD_OK          # nothing to copy
+    assert lib.ssd_stream_copy(None, fake(0x20000), 16, None) == ssd.SSD_ERR_INVALID_ARG
+    assert lib.ssd_stream_copy(fake(0x10008), fake(0x20000), 16, None) == ssd.SSD_ERR_INVALID_ARG   # misaligned
+    assert lib.ssd_stream_copy(fake(0x10000), fake(0x20000), 24, None) == ssd.SSD_ERR_INVALID_ARG   # not 16-byte units
+    assert lib.ssd_stream_copy(fake(0x10000), fake(0x10100), 4096, None) == ssd.SSD_ERR_INVALID_ARG  # overlapping
 
 
 def test_binding_refuses_to_run_without_library(monkeypatch):
