@@ -367,7 +367,7 @@ ssd_status ssd_block_prologue(const void *zxbcdt, const float *conv_w, const flo
     const void *ptrs[] = {zxbcdt, x, Bm, Cm};
     for (const void *p : ptrs)
         if (!aligned16(p)) return SSD_ERR_INVALID_ARG;
-    if ((L + 31) / 32 > 65535 || B > 65535) return SSD_ERR_UNSUPPORTED;
+    if ((L + 127) / 128 > 65535 || B > 65535) return SSD_ERR_UNSUPPORTED;   // the prologue grid: 128-token tiles
     const hipError_t e = launch_block_prologue(zxbcdt, conv_w, conv_b, dt_bias, x, Bm, Cm, dt, B, L, H, H * P,
                                                G * N, W, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

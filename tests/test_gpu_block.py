@@ -40,6 +40,8 @@ PRO = [
     ("short_rows_w4", 3, 5, 8, 16, 1, 16, 4),
     ("w2", 1, 70, 8, 32, 1, 32, 2),
     ("w1", 1, 33, 8, 32, 1, 32, 1),
+    # three 128-token tiles, the last ragged: the convolution's history crosses tile edges
+    ("tiles_ragged_w4", 2, 300, 8, 64, 1, 64, 4),
 ]
 
 
