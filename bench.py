@@ -144,17 +144,17 @@ def io_dtype(w):
     return torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
 
-def time_scan(w, steps, warmup, device):
+def time_scan(w, steps, warmup, device, algo="auto"):
     import torch
     import selective_state_space_chunk_amd as ssd
     sets = make_device_sets(w, 3, device)
-    nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
+    nbytes = ssd.ssd_chunk_scan_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w), algo)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def run(k):
         s = sets[k % len(sets)]
         ssd.ssd_chunk_scan_fwd(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], s["D"], s["init"], w.chunk,
-                               y=s["y"], final_state=s["final"], workspace_tensor=ws)
+                               y=s["y"], final_state=s["final"], workspace_tensor=ws, algo=algo)
 
     for k in range(warmup):
         run(k)
@@ -535,7 +535,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_fetch, "write_scale_bytes_per_kib": f_write, "kernels": {}}
     total = 0.0
-    for name in ("pipe_kernel", "prep_kernel", "gram_kernel", "scan_mfma", "ref_"):
+    for name in ("pipe_kernel", "prep_kernel"):
         try:
             fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", name)
             wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", name)
@@ -559,6 +559,19 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
                                     "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
         btotal += fk * f_fetch + wk * f_write
     out["bwd_bytes_per_call"] = btotal if out["bwd_kernels"] else None
+    # the staged form (an explicit choice, not the headline call), per kernel
+    out["staged_kernels"] = {}
+    for name, match in (("gram_kernel", "gram_kernel"),
+                        ("scan_mfma<kState>", "scan_mfmaILi128ELi256ELi0E"),      # N 128, chunk 256, mode 0
+                        ("scan_mfma<kOutput>", "scan_mfmaILi128ELi256ELi1E"),     # mode 1
+                        ("state_pass_kernel", "state_pass_kernel")):
+        try:
+            fk, nf = _pmc_kib(fetch_dir, "FETCH_SIZE", match)
+            wk, nw = _pmc_kib(write_dir, "WRITE_SIZE", match)
+        except SystemExit:
+            continue
+        out["staged_kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
+                                       "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
     out["step_sources_sha256"] = scan_sources_digest(STEP_SOURCES)
     out["step_kernels"] = {}
     try:
@@ -595,6 +608,7 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-s6", action="store_true")
+    ap.add_argument("--no-staged", action="store_true")
     ap.add_argument("--calibrate-copy", type=float, default=None, metavar="MB")
     ap.add_argument("--summarize-pmc", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -733,6 +747,24 @@ def main():
                      "roofline": {"bound": "alu", "achieved": updates / (m * 1e-3) / 1e12, "peak": peak / 1e12,
                                   "unit": "T state updates/s", "frac": updates / (m * 1e-3) / peak,
                                   "hbm_gbs": nbytes / (m * 1e-3) / 1e9, "algorithmic_bytes": nbytes}}
+    if not args.no_staged and headline and w.P == 64:
+        # the pages' own four-step form (block states in HBM, a separate state
+        # pass) at the same shape, as an explicit choice: not the headline value
+        _, sp = time_scan(w, max(10, args.steps // 5), 3, device, algo="staged")
+        smean = sum(sp) / len(sp)
+        nc = -(-w.L // w.chunk)
+        # the state pass reads every block's local state and the initial state,
+        # and writes every block's entering state and the final state
+        state_bytes = 2 * w.B * (nc + 1) * w.H * w.P * w.N * 4
+        out["staged"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_staged_form", "chunk": w.chunk,
+                         "us_per_call": smean * 1000.0, "us_median": sp[len(sp) // 2] * 1000.0,
+                         "tokens_per_s": tokens / (smean * 1e-3),
+                         "kernels": f"gram_kernel<{w.N}> + scan_mfma<{w.N}, {w.chunk}, kState> + state_pass_kernel + "
+                                    f"scan_mfma<{w.N}, {w.chunk}, kOutput>",
+                         "state_pass_bytes": state_bytes,
+                         "roofline": {"bound": "hbm", "achieved": byts / (smean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": byts / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "algorithmic_bytes": byts}}
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

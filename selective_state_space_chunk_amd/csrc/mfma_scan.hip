@@ -425,6 +425,48 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 2 : 1) void scan_mfma(
     }
 }
 
+// The state pass of the staged form: the state entering every block,
+// H_{c+1} = decay_c H_c + S_c, written over the block's own state S_c in place,
+// and the final state.  Sequential over the blocks, parallel over (b, h) and
+// the P*N elements: one thread per four elements (16-byte accesses), the four
+// block states of the next group of four blocks loaded before the current four
+// are written, so that loads overlap the chain instead of waiting one block at
+// a time.
+__global__ __launch_bounds__(256) void state_pass_kernel(float4 *__restrict__ states, const float *__restrict__ decay,
+                                                         const float4 *init, float4 *final_state, int64_t H,
+                                                         int64_t PN4, int nc) {
+    const int64_t bh = blockIdx.y;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= PN4) return;
+    float4 s = init ? init[bh * PN4 + e] : float4{0.f, 0.f, 0.f, 0.f};
+    const float *dk = decay + bh * nc;
+    auto at = [&](int c) { return states + ((b * nc + c) * H + h) * PN4 + e; };
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+        float4 loc[4];
+        float dd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            loc[j] = *at(c + j);
+            dd[j] = dk[c + j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *at(c + j) = s;                           // state entering block c + j
+            s = float4{dd[j] * s.x + loc[j].x, dd[j] * s.y + loc[j].y, dd[j] * s.z + loc[j].z,
+                       dd[j] * s.w + loc[j].w};
+        }
+    }
+    for (; c < nc; ++c) {
+        const float4 loc = *at(c);
+        const float d = dk[c];
+        *at(c) = s;
+        s = float4{d * s.x + loc.x, d * s.y + loc.y, d * s.z + loc.z, d * s.w + loc.w};
+    }
+    if (final_state) final_state[bh * PN4 + e] = s;   // the same thread read init[e]: aliasing is safe
+}
+
 template <int N, int Q, int MODE>
 hipError_t launch_mode(const ScanArgs &a, const Workspace &ws, dim3 grid) {
     const size_t smem = sizeof(Smem<N, Q>);
@@ -481,6 +523,16 @@ bool mfma_supported(int64_t P, int64_t N, int64_t Q) {
 size_t gram_bytes(int64_t B, int64_t L, int64_t G, int64_t Q) {
     const int64_t nc = (L + Q - 1) / Q;
     return (size_t)(B * G * nc * Q * kSub) * sizeof(__bf16);
+}
+
+hipError_t launch_state_pass(float *states, const float *decay, const float *init, float *final_state,
+                             int64_t B, int64_t H, int64_t PN, int nc, hipStream_t stream) {
+    const int64_t PN4 = PN / 4;   // P*N is a multiple of 4 (P, N >= 16)
+    const dim3 grid((unsigned)((PN4 + 255) / 256), (unsigned)(B * H));
+    state_pass_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<float4 *>(states), decay,
+                                                reinterpret_cast<const float4 *>(init),
+                                                reinterpret_cast<float4 *>(final_state), H, PN4, nc);
+    return hipGetLastError();
 }
 
 hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return dispatch(a, ws); }

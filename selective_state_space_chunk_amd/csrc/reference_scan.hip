@@ -172,13 +172,6 @@ hipError_t launch_typed(const ScanArgs &a, const Workspace &ws) {
 
 }  // namespace
 
-hipError_t launch_state_pass(float *states, const float *decay, const float *init, float *final_state,
-                             int64_t B, int64_t H, int64_t PN, int nc, hipStream_t stream) {
-    const dim3 pgrid((unsigned)((PN + kThreads - 1) / kThreads), (unsigned)(B * H));
-    ref_state_pass<<<pgrid, kThreads, 0, stream>>>(states, decay, init, final_state, H, PN, nc);
-    return hipGetLastError();
-}
-
 hipError_t launch_reference_scan(const ScanArgs &a, const Workspace &ws) {
     return a.bf16 ? launch_typed<bf16>(a, ws) : launch_typed<float>(a, ws);
 }
