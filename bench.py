@@ -694,18 +694,21 @@ def main():
                                       "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
                                       "traffic": step_traffic(), "algorithmic_bytes": sb}}
-    if not args.no_backward and headline:
+    if not args.no_backward and (headline or (w.P == 128 and w.N <= 128 and w.dtype == "bf16")):
+        # the backward at the layer shape, and at its head-dim-128 form
         bp = time_backward(w, max(10, args.steps // 5), 3, device)
         bmean = sum(bp) / len(bp)
         bb = bwd_algorithmic(w)
         out["backward"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_backward",
                            "us_per_call": bmean * 1000.0, "us_median": bp[len(bp) // 2] * 1000.0,
                            "tokens_per_s": tokens / (bmean * 1e-3),
-                           "kernels": "state_scans<128> (forward and adjoint states) + chunk_grad<128> + reduce_head",
+                           "kernels": f"state_scans<{w.N}> (forward and adjoint states) + chunk_grad<{w.N}> + "
+                                      "reduce_head",
                            "roofline": {"bound": "hbm", "achieved": bb / (bmean * 1e-3) / 1e9,
                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                         "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                        "traffic": bwd_traffic(), "algorithmic_bytes": bb}}
+                                        "traffic": bwd_traffic() if headline else None,
+                                        "algorithmic_bytes": bb}}
     if not args.no_varlen and headline:
         vp, nseq = time_varlen(w, max(10, args.steps // 2), 3, device)
         vmean = sum(vp) / len(vp)

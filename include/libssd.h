@@ -278,7 +278,7 @@ ssd_status ssd_selective_scan(const void *x, const void *dt, const float *A, con
 /*
  * Bytes of device workspace ssd_chunk_scan_bwd needs for this shape: the
  * state entering every 64-token sub-block and the gradient of the state
- * leaving it (two bfloat16 arrays of B*H*ceil(L/64)*64*N), plus float32
+ * leaving it (two bfloat16 arrays of B*H*ceil(L/64)*P*N), plus float32
  * parts of dA and dD per (batch row, head, sub-block).
  * Returns 0 when the backward does not cover the shape or dtype.  No
  * zero-filling is needed; calls sharing a workspace must be ordered on one
@@ -308,9 +308,9 @@ size_t ssd_chunk_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_
  *   dinit    [B, H, P, N]   float32  gradient of init_state, or NULL to skip
  *   workspace  device memory of at least ssd_chunk_scan_bwd_workspace_size(...) bytes
  *
- * Supported: dtype SSD_DTYPE_BF16, P == 64, N == 64 or 128, chunk_size as for
- * the forward (the result does not depend on it beyond rounding); anything
- * else returns SSD_ERR_UNSUPPORTED.  Products run on the matrix cores with
+ * Supported: dtype SSD_DTYPE_BF16, P == 64 or 128, N == 64 or 128, chunk_size
+ * as for the forward (the result does not depend on it beyond rounding);
+ * anything else returns SSD_ERR_UNSUPPORTED.  Products run on the matrix cores with
  * bfloat16 operands and float32 accumulation.  Outputs must not alias inputs.
  * Errors as for ssd_chunk_scan_fwd.  L == 0 or B == 0 writes dA = dD = 0 and
  * dinit = dfinal (or zeros).

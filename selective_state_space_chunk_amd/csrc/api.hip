@@ -26,11 +26,11 @@ hipError_t launch_gated_norm(const void *y, const void *z, int64_t zstride, cons
                              void *out, int64_t T, int64_t D, int64_t ngroups, float eps, int center,
                              hipStream_t stream);
 bool bwd_supported(int64_t P, int64_t N, int64_t H, int64_t G);
-size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t N);
+size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N);
 hipError_t launch_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
                            const float *D, const float *init, const void *dy, const float *dfinal, void *dx,
                            float *ddt, float *dA, void *dBm, void *dCm, float *dD, float *dinit, float *ws,
-                           int64_t B, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream);
+                           int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, hipStream_t stream);
 }
 
 namespace {
@@ -418,7 +418,7 @@ size_t ssd_chunk_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_
     if (B < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk_size <= 0) return 0;
     if (H % G != 0 || !shape_supported(P, N, chunk_size)) return 0;
     if (dtype != SSD_DTYPE_BF16 || !bwd_supported(P, N, H, G)) return 0;
-    return align_up(bwd_workspace_floats(B, L, H, N) * sizeof(float));
+    return align_up(bwd_workspace_floats(B, L, H, P, N) * sizeof(float));
 }
 
 ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm,
@@ -438,9 +438,10 @@ ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, co
     if (chunk_size <= 0) return SSD_ERR_INVALID_ARG;
     if (!shape_supported(P, N, chunk_size) || dtype != SSD_DTYPE_BF16 || !bwd_supported(P, N, H, G))
         return SSD_ERR_UNSUPPORTED;
-    if (B > kMaxChains || H > kMaxChains || B * H > kMaxChains) return SSD_ERR_UNSUPPORTED;
+    const int64_t Hk = H * (P / 64);   // heads of 64 channels
+    if (B > kMaxChains || Hk > kMaxChains || B * Hk > kMaxChains) return SSD_ERR_UNSUPPORTED;
     const int64_t nsb = (L + 63) / 64;
-    if (B * H * nsb > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (B * Hk * nsb > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (!has_work) {
         // no tokens: dA = dD = 0 and the initial state's gradient is dfinal (or 0)
         fill_or_copy<<<(unsigned)((H + 255) / 256), 256, 0, stream>>>(dA, nullptr, H);
@@ -451,11 +452,11 @@ ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, co
         }
         return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
-    const size_t need = align_up(bwd_workspace_floats(B, L, H, N) * sizeof(float));
+    const size_t need = align_up(bwd_workspace_floats(B, L, H, P, N) * sizeof(float));
     if (!workspace || workspace_bytes < need) return SSD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SSD_ERR_INVALID_ARG;
     const hipError_t e = launch_scan_bwd(x, dt, A, Bm, Cm, D, init_state, dy, dfinal, dx, ddt, dA, dBm, dCm,
-                                         dD, dinit, (float *)workspace, B, L, H, G, N, stream);
+                                         dD, dinit, (float *)workspace, B, L, H, P, G, N, stream);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

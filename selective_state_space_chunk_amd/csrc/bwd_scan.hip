@@ -1,7 +1,10 @@
 // Backward of the chunk scan on gfx950: the gradients of
 //   <dy, y> + <dfinal, final state>
-// with respect to x, dt, A, Bm, Cm, D and the initial state, for P = 64,
-// N in {64, 128}, bfloat16 x / Bm / Cm / y.
+// with respect to x, dt, A, Bm, Cm, D and the initial state, for P = 64 or
+// 128, N in {64, 128}, bfloat16 x / Bm / Cm / y.  A head of 128 channels is
+// taken as two heads of 64 (the state rows p < 64 and p >= 64 never mix) that
+// share dt, A and D; the gradients of those shared inputs are the sums over
+// the two halves.
 //
 // The recurrence is the one of the "Mamba-2" note (section "writing the SSM
 // as a matrix", one decay per head as in "reducing A to a number"), cut into
@@ -46,9 +49,11 @@ struct BwdArgs {
     float *dHs;   // [B*H, nsb, P*N] bf16  adjoint of the state leaving each sub-block
                   // (both in accumulator order: 4-value unit ((pq*NT + u)*64 + lane)
                   //  holds p = 16pq + lane%16, n = 16u + 4(lane/16) + 0..3)
-    float *dAp;   // [B*H, nsb]  each head's part of dA from each sub-block
-    float *dDp;   // [B*H, nsb]
-    int64_t B, L, H, G, nsb;
+    float *dAp;   // [B*Hd, nsb]  each head's part of dA from each sub-block
+    float *dDp;   // [B*Hd, nsb]
+    int64_t B, L, H, G, nsb;   // H: heads of 64 channels (x, dy, dx, states, init, dfinal, dinit)
+    int64_t Hd;                // the caller's heads (dt, ddt, A, D, dA, dD): H / hs
+    int hs;                    // heads of 64 channels per caller head (1 or 2)
 };
 
 __device__ __forceinline__ float ex2f(float v) { return __builtin_amdgcn_exp2f(v); }
@@ -107,12 +112,12 @@ __device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
     __shared__ __align__(16) __bf16 lb[kSub * N];
     using O = LaneOffs<N>;
     constexpr int NT = N / 16, KB = N / 32;
-    const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
-    const float Ah2 = a.A[h] * kLog2eB;
+    const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G), dh = h / a.hs;
+    const float Ah2 = a.A[dh] * kLog2eB;
     const int tid = threadIdx.x;
     const int pq = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
-    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G);
+    const LaneOffs<N> o = lane_offsets<N>(tid, pq, a.H, a.G, a.Hd);
     const __bf16 *U = kRev ? a.dy : a.x;
     const __bf16 *Mt = kRev ? a.Cm : a.Bm;
     const int nsb = (int)a.nsb;
@@ -134,7 +139,7 @@ __device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
         const int step = (int)((256 / O::CPR) * a.G * N * 2);
 #pragma unroll
         for (int k = 0; k < KB; ++k) mr[slot][k] = ld16(rm, o.gb + k * step);
-        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(q - 1) * a.H + 1) * 4));
+        const rsrc_t rd = rsrc(a.dt + row0 * a.Hd + dh, (int)(((int64_t)(q - 1) * a.Hd + 1) * 4));
         dtv[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o.gd, 0, 0));
     };
 
@@ -326,8 +331,9 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
             hv[k] = *reinterpret_cast<const uint4 *>(hs + 8 * (k * 256 + tid));
             dv[k] = *reinterpret_cast<const uint4 *>(ds + 8 * (k * 256 + tid));
         }
-        const rsrc_t rd = rsrc(a.dt + row0 * a.H + h, (int)(((int64_t)(q - 1) * a.H + 1) * 4));
-        dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lane * (int)(a.H * 4), 0, 0));
+        const int64_t dh = h / a.hs;
+        const rsrc_t rd = rsrc(a.dt + row0 * a.Hd + dh, (int)(((int64_t)(q - 1) * a.Hd + 1) * 4));
+        dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lane * (int)(a.Hd * 4), 0, 0));
     };
     load_head(g * hpg);
     __syncthreads();
@@ -343,9 +349,13 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dCacc[nt] = dBacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // wave 0 carries the first half's ddt and dA, dD parts of a head of 128
+    // channels to the second half (the halves are consecutive in the walk)
+    float ddt_half = 0.f, da_half = 0.f, dd_half = 0.f;
     for (int64_t hh = 0; hh < hpg; ++hh) {
-        const int64_t h = g * hpg + hh;
-        const float Ah = a.A[h], Ah2 = Ah * kLog2eB, Dh = a.D[h];
+        const int64_t h = g * hpg + hh, dh = h / a.hs;
+        const bool first_half = a.hs == 2 && (h & 1) == 0;
+        const float Ah = a.A[dh], Ah2 = Ah * kLog2eB, Dh = a.D[dh];
         // ---- stage this head; decays
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -514,11 +524,18 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
             const float pre = wave_scan(dl);
             const float rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), 63)) - pre + dl;
             const float g_dt = Ah * rs + zrc + ex2f(lend - sm.lam[k]) * qk;
-            if (k < q) a.ddt[(row0 + k) * a.H + h] = g_dt;
             const float da = wave_sum(sm.dtl[k] * rs);
-            if (k == 0) {
-                a.dAp[(b * a.H + h) * nsb + c] = da;
-                a.dDp[(b * a.H + h) * nsb + c] = sm.red[4] + sm.red[5] + sm.red[6] + sm.red[7];
+            const float ddp = sm.red[4] + sm.red[5] + sm.red[6] + sm.red[7];
+            if (first_half) {
+                ddt_half = g_dt;
+                da_half = da;
+                dd_half = ddp;
+            } else {
+                if (k < q) a.ddt[(row0 + k) * a.Hd + dh] = ddt_half + g_dt;
+                if (k == 0) {
+                    a.dAp[(b * a.Hd + dh) * nsb + c] = da_half + da;
+                    a.dDp[(b * a.Hd + dh) * nsb + c] = dd_half + ddp;
+                }
             }
         }
         __syncthreads();
@@ -547,8 +564,8 @@ __global__ __launch_bounds__(256) void reduce_head(BwdArgs a) {
     float sa = 0.f, sd = 0.f;
     for (int64_t k = threadIdx.x; k < a.B * a.nsb; k += blockDim.x) {
         const int64_t b = k / a.nsb, c = k % a.nsb;
-        sa += a.dAp[(b * a.H + h) * a.nsb + c];
-        sd += a.dDp[(b * a.H + h) * a.nsb + c];
+        sa += a.dAp[(b * a.Hd + h) * a.nsb + c];
+        sd += a.dDp[(b * a.Hd + h) * a.nsb + c];
     }
     part[0][threadIdx.x] = sa;
     part[1][threadIdx.x] = sd;
@@ -571,37 +588,40 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     const int64_t bhn = a.B * a.H;
     state_scans<N><<<dim3((unsigned)(2 * bhn)), 256, 0, stream>>>(a);
     chunk_grad<N><<<dim3((unsigned)(a.B * a.G * a.nsb)), 256, 0, stream>>>(a);
-    reduce_head<<<dim3((unsigned)a.H), 256, 0, stream>>>(a);
+    reduce_head<<<dim3((unsigned)a.Hd), 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool bwd_supported(int64_t P, int64_t N, int64_t H, int64_t G) {
-    if (P != 64 || !(N == 64 || N == 128)) return false;
+    if (!(P == 64 || P == 128) || !(N == 64 || N == 128)) return false;
     const int64_t lim = (int64_t)1 << 31;
-    return (int64_t)kSub * H * kP * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
+    return (int64_t)kSub * H * P * 2 < lim && (int64_t)kSub * G * N * 2 < lim && (int64_t)kSub * H * 4 < lim;
 }
 
 // Workspace of the backward, in floats: the states and adjoints (bfloat16,
-// two per float) and the per-(head, sub-block) parts of dA and dD.
-size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t N) {
-    const int64_t nsb = (L + kSub - 1) / kSub;
-    return (size_t)(B * H * nsb * kSub * N + 2 * B * H * nsb);
+// two per float) of every head of 64 channels, and the per-(head, sub-block)
+// parts of dA and dD.
+size_t bwd_workspace_floats(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
+    const int64_t nsb = (L + kSub - 1) / kSub, Hk = H * (P / kP);
+    return (size_t)(B * Hk * nsb * kSub * N + 2 * B * H * nsb);
 }
 
 hipError_t launch_scan_bwd(const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
                            const float *D, const float *init, const void *dy, const float *dfinal, void *dx,
                            float *ddt, float *dA, void *dBm, void *dCm, float *dD, float *dinit, float *ws,
-                           int64_t B, int64_t L, int64_t H, int64_t G, int64_t N, hipStream_t stream) {
+                           int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, hipStream_t stream) {
     const int64_t nsb = (L + kSub - 1) / kSub;
-    const int64_t big = B * H * nsb * kSub * N / 2;   // one bf16 state array, in floats
+    const int hs = (int)(P / kP);
+    const int64_t Hk = H * hs;
+    const int64_t big = B * Hk * nsb * kSub * N / 2;   // one bf16 state array, in floats
     BwdArgs a{(const __bf16 *)x, (const __bf16 *)dy, (const __bf16 *)Bm, (const __bf16 *)Cm,
               dt, A, D, init, dfinal,
               (__bf16 *)dx, (__bf16 *)dBm, (__bf16 *)dCm,
               ddt, dA, dD, dinit,
               ws, ws + big, ws + 2 * big, ws + 2 * big + B * H * nsb,
-              B, L, H, G, nsb};
+              B, L, Hk, G, nsb, H, hs};
     switch (N) {
         case 64: return launch<64>(a, stream);
         case 128: return launch<128>(a, stream);

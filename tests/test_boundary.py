@@ -191,7 +191,11 @@ def test_backward_workspace_size(lib):
     want = 2 * 2 * B * H * nsb * 64 * N + 4 * 2 * B * H * nsb
     want = (want + 255) // 256 * 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 1) == want
-    # not covered: float32, P != 64, N = 256
+    # heads of 128 channels: states of both halves, parts per head
+    want = 2 * 2 * B * H * nsb * 128 * N + 4 * 2 * B * H * nsb
+    want = (want + 255) // 256 * 256
+    assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, 128, G, N, Q, 1) == want
+    # not covered: float32, P not 64 or 128, N = 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, N, Q, 0) == 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, 32, G, N, Q, 1) == 0
     assert lib.ssd_chunk_scan_bwd_workspace_size(B, L, H, P, G, 256, Q, 1) == 0

@@ -72,6 +72,31 @@ def test_backward_matches_oracle(case):
         assert e <= TOL["bf16"], (k, e)
 
 
+# heads of 128 channels: each is taken as two heads of 64 sharing dt, A and D,
+# whose ddt, dA and dD are the sums over the two halves
+# (name, B, L, H, N, G, init, dfinal, regime)
+CASES_P128 = [
+    ("p128_one_block", 1, 64, 2, 128, 1, True, True, "default"),
+    ("p128_ragged", 2, 3 * 64 + 17, 3, 128, 1, True, True, "default"),
+    ("p128_groups_n64", 2, 150, 4, 64, 2, False, True, "long_memory"),
+    ("p128_forty_heads_one_group", 1, 260, 40, 128, 1, True, False, "default"),
+]
+
+
+@pytest.mark.parametrize("case", CASES_P128, ids=[c[0] for c in CASES_P128])
+def test_backward_head_dim_128(case):
+    name, B, L, H, N, G, init, dfin, regime = case
+    d = si.make_scan_inputs(B, L, H, 128, N, G, dtype="bf16", init=init, seed=3600 + L + H, regime=regime)
+    g = si.make_grad_inputs(B, L, H, 128, N, dtype="bf16", dfinal=dfin, seed=3700 + L)
+    ref = oracle_grads(d, g)
+    announce(f"bwd {name}: B{B} L{L} H{H} P128 N{N} G{G} init={init} dfinal={dfin} {regime}")
+    got = gpu_grads(to_device(d, "bf16"), grad_device(g))
+    for k in GRADS:
+        e = rel_err(to_np(got[k]), ref[k])
+        print(f"    {k}: {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (k, e)
+
+
 def test_backward_is_deterministic():
     d = si.make_scan_inputs(1, 300, 4, 64, 128, 1, dtype="bf16", init=True, seed=3301)
     g = si.make_grad_inputs(1, 300, 4, 64, 128, dtype="bf16", seed=3302)
