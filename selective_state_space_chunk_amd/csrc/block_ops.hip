@@ -25,6 +25,12 @@ __device__ __forceinline__ f32x8 ld_bf16x8(const __bf16 *p) {
     }
     return v;
 }
+// 16 bytes read once (non-temporal: they need not stay in the caches)
+__device__ __forceinline__ uint4 ld_stream(const __bf16 *p) {
+    typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
+    const u32x4n v = __builtin_nontemporal_load(reinterpret_cast<const u32x4n *>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+}
 __device__ __forceinline__ void st_bf16x8(__bf16 *p, const f32x8 &v) {
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     bf16x8_t o;
@@ -44,11 +50,12 @@ __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1p
 // current token, zero before token 0) plus bias and SiLU, into x, Bm, Cm;
 // dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 128 tokens of row
 // b from token 128 ty; lane k of channel tile cx takes channels 8(256 cx + k)
-// .. +7 for all 128 tokens, keeping the last W-1 inputs in registers.  The
-// last channel tile computes dt of the 128 tokens instead.  At the 2.7B layer
-// shape 128 tokens per workgroup took 94 us, against 112 us with 32 (whose
-// workgroups re-read 3 of every 32 rows for the convolution's history) and
-// 120 us with 256.
+// .. +7 for all 128 tokens, keeping the last W-1 inputs in registers and
+// loading the next 8 rows while the current 8 are computed.  The last channel
+// tile computes dt of the 128 tokens instead.  At the 2.7B layer shape 128
+// tokens per workgroup took 94 us, against 112 us with 32 (whose workgroups
+// re-read 3 of every 32 rows for the convolution's history) and 120 us with
+// 256; loading ahead took it to 92 us.
 struct ProArgs {
     const __bf16 *zx;
     const float *conv_w, *conv_b, *dt_bias;
@@ -61,7 +68,7 @@ struct ProArgs {
 constexpr int kTok = 128;
 
 template <int W>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prologue_kernel(ProArgs a) {
+__global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
     const int64_t b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * kTok;
     const int nt = (int)(a.L - t0 < kTok ? a.L - t0 : kTok);
@@ -112,12 +119,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
         const uint32_t w = e < 2 ? (e == 0 ? u.x : u.y) : (e == 2 ? u.z : u.w);
         return w;
     };
+    uint4 nxt[R];   // the rows of the next round
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int t = u < nt ? u : nt - 1;   // clamped: every load in bounds
+        nxt[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
+    }
     for (int tt = 0; tt < nt; tt += R) {
         uint4 cur[R];
 #pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int t = tt + u < nt ? tt + u : nt - 1;   // clamped: every load in bounds
-            cur[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
+        for (int u = 0; u < R; ++u) cur[u] = nxt[u];
+        if (tt + R < nt) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int t = tt + R + u < nt ? tt + R + u : nt - 1;   // clamped: every load in bounds
+                nxt[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
+            }
         }
 #pragma unroll
         for (int u = 0; u < R; ++u) {
@@ -150,7 +167,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
 // and the group sums are wave reductions with no barrier.  The loaded y and z
 // stay raw bfloat16 words until used: 122 registers instead of 185 at D =
 // 5120, four waves per SIMD instead of two (110 against 125 us at the 2.7B
-// layer shape).  The sums run in a fixed order, so results are deterministic.
+// layer shape), and are loaded non-temporally (98 against 109 us).  The sums
+// run in a fixed order, so results are deterministic.
 struct NormArgs {
     const __bf16 *y, *z;
     const float *w, *bias;
@@ -200,8 +218,8 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a) {
         const int ch = lane + 64 * k;
         grp[k] = ch < nch ? ch / gch : -1;
         const int cl = ch < nch ? ch : nch - 1;   // clamped: every load in bounds
-        yr[k] = *reinterpret_cast<const uint4 *>(a.y + t * a.D + 8 * cl);
-        zr[k] = *reinterpret_cast<const uint4 *>(a.z + t * a.zstride + 8 * cl);
+        yr[k] = ld_stream(a.y + t * a.D + 8 * cl);
+        zr[k] = ld_stream(a.z + t * a.zstride + 8 * cl);
     }
     f32x8 v[KC];
     float part[KC];
