@@ -230,15 +230,18 @@ __global__ __launch_bounds__(256) void state_scans(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Gradients of one sub-block for all heads of a group: one workgroup (four
-// waves) per (batch, group, sub-block), walking the group's heads with the
-// next head's inputs loaded during the current one.  Bm, Cm and Gm = Cm Bm^T
-// are shared by the heads and formed once; dBm and dCm are summed over the
-// heads in the matrix-core accumulators and written once.  Tiles sit in LDS
-// row-major with padded rows (S64 = 72, SN = N + 8 bfloat16).  A fragment
-// whose 8 k values run along a stored row is one 16-byte read; one whose k
-// values run down a column comes from two transposing reads (ds_read_b64_tr_b16).
-// Wave w computes rows 16w..16w+15 of every 64-row output.
+// 3. Gradients of one sub-block for all heads of a group: one workgroup
+// (eight waves) per (batch, group, sub-block), walking the group's heads with
+// the next head's inputs loaded during the current one.  Bm, Cm and
+// Gm = Cm Bm^T are shared by the heads and formed once; dBm and dCm are summed
+// over the heads in the matrix-core accumulators and written once.  Tiles sit
+// in LDS row-major with padded rows (S64 = 72, SN = N + 8 bfloat16).  A
+// fragment whose 8 k values run along a stored row is one 16-byte read; one
+// whose k values run down a column comes from two transposing reads
+// (ds_read_b64_tr_b16).  Wave (w, hf), w = 0..3, hf = 0..1, computes rows
+// 16w..16w+15 of every 64-row output and half of its column tiles, so that two
+// waves share each SIMD and hide each other's latencies; the row sums the
+// halves both contribute to meet in LDS.
 template <int N>
 struct GradSmem {
     static constexpr int S64 = 72, SN = N + 8;
@@ -251,8 +254,9 @@ struct GradSmem {
     __bf16 MT[64 * S64];     // M^T [j][i]
     __bf16 QT[64 * S64];     // Q^T [j][i]
     float lam[64], dtl[64], ww[64], ee[64];
-    float zrow[64], zcolw[16][64], zrcolw[16][64], qv[64], uv[64];   // column parts per (wave, lane row)
-    float red[8];
+    float zcolw[16][64], zrcolw[16][64];               // column parts per (row wave, lane row)
+    float zrow[2][64], qv[2][64], uv[2][64];           // row parts per column half
+    float red[16];
 };
 
 // The four values a lane's accumulator covers, (r0 + 4 lgrp + r, c0 + lrow) for
@@ -279,17 +283,18 @@ __device__ __forceinline__ bf16x8 frag_col(const __bf16 *base, int r0, int strid
 __device__ __forceinline__ float red16(float v) { return row_sum16(v); }   // sum over the 16 lanes of a group
 
 template <int N>
-__global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
+__global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
     __shared__ __align__(16) GradSmem<N> sm;
     constexpr int S64 = GradSmem<N>::S64, SN = GradSmem<N>::SN;
-    constexpr int NT = N / 16, KN = N / 32, CPR = N / 8, KB = N / 32;
-    constexpr int HCH = 64 * N / 8 / 256;   // 16-byte chunks of a bf16 [64][N] state per thread
+    constexpr int NT = N / 16, NH = NT / 2, KN = N / 32, CPR = N / 8;
+    constexpr int BPASS = 64 * CPR / 512;   // 16-byte chunks of a bf16 [64][N] tile per thread
     const int64_t nsb = a.nsb;
     const int64_t bg = blockIdx.x / nsb;
     const int c = (int)(blockIdx.x % nsb);
     const int64_t b = bg / a.G, g = bg % a.G, hpg = a.H / a.G;
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = w8 & 3, hf = w8 >> 2;   // row block, column half
     const int lane = tid & 63, lrow = lane & 15, lgrp = lane >> 4;
     const int64_t t0 = (int64_t)c * kSub;
     const int q = a.L - t0 < kSub ? (int)(a.L - t0) : kSub;
@@ -302,34 +307,32 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         const rsrc_t rb = rsrc(a.Bm + (row0 * a.G + g) * N, bytes);
         const rsrc_t rc = rsrc(a.Cm + (row0 * a.G + g) * N, bytes);
 #pragma unroll
-        for (int k = 0; k < KB; ++k) {
-            const int r = br + k * (256 / CPR);
+        for (int k = 0; k < BPASS; ++k) {
+            const int r = br + k * (512 / CPR);
             const int off = (int)(((int64_t)r * a.G * N + 8 * bc) * 2);
             *reinterpret_cast<uint4 *>(sm.B + r * SN + 8 * bc) = ld16(rb, off);
             *reinterpret_cast<uint4 *>(sm.C + r * SN + 8 * bc) = ld16(rc, off);
         }
     }
-    // this head's inputs: x, dy (two chunks each), dt, H and dH' (bf16, accumulator order)
+    // this head's inputs: one chunk of x and of dy, dt, and BPASS chunks of H
+    // and dH' (bf16, accumulator order)
     const int xr = tid >> 3, xc = tid & 7;
-    uint4 xv[2], yv[2], hv[HCH], dv[HCH];
+    uint4 xv, yv, hv[BPASS], dv[BPASS];
     float dtv;
     auto load_head = [&](int64_t h) __attribute__((always_inline)) {
         const int bytes = (int)(((int64_t)(q - 1) * a.H * kP + kP) * 2);
         const rsrc_t rx = rsrc(a.x + (row0 * a.H + h) * kP, bytes);
         const rsrc_t ry = rsrc(a.dy + (row0 * a.H + h) * kP, bytes);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int off = (int)(((int64_t)(xr + 32 * k) * a.H * kP + 8 * xc) * 2);
-            xv[k] = ld16(rx, off);
-            yv[k] = ld16(ry, off);
-        }
+        const int off = (int)(((int64_t)xr * a.H * kP + 8 * xc) * 2);
+        xv = ld16(rx, off);
+        yv = ld16(ry, off);
         const int64_t slot = ((b * a.H + h) * nsb + c) * (kP * N);
         const __bf16 *hs = reinterpret_cast<const __bf16 *>(a.Hs) + slot;
         const __bf16 *ds = reinterpret_cast<const __bf16 *>(a.dHs) + slot;
 #pragma unroll
-        for (int k = 0; k < HCH; ++k) {
-            hv[k] = *reinterpret_cast<const uint4 *>(hs + 8 * (k * 256 + tid));
-            dv[k] = *reinterpret_cast<const uint4 *>(ds + 8 * (k * 256 + tid));
+        for (int k = 0; k < BPASS; ++k) {
+            hv[k] = *reinterpret_cast<const uint4 *>(hs + 8 * (k * 512 + tid));
+            dv[k] = *reinterpret_cast<const uint4 *>(ds + 8 * (k * 512 + tid));
         }
         const int64_t dh = h / a.hs;
         const rsrc_t rd = rsrc(a.dt + row0 * a.Hd + dh, (int)(((int64_t)(q - 1) * a.Hd + 1) * 4));
@@ -337,17 +340,18 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
     };
     load_head(g * hpg);
     __syncthreads();
-    f32x4 gm[4];
+    f32x4 gm[2];   // Gm tiles (rows 16w.., columns 16jt..) of this wave's column half
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        gm[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 2; ++e) {
+        const int jt = 2 * hf + e;
+        gm[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk)
-            gm[jt] = mfma(frag_row(sm.C, 16 * w, SN, 32 * kk, lrow, lgrp), frag_row(sm.B, 16 * jt, SN, 32 * kk, lrow, lgrp), gm[jt]);
+            gm[e] = mfma(frag_row(sm.C, 16 * w, SN, 32 * kk, lrow, lgrp), frag_row(sm.B, 16 * jt, SN, 32 * kk, lrow, lgrp), gm[e]);
     }
-    f32x4 dCacc[NT], dBacc[NT];
+    f32x4 dCacc[NH], dBacc[NH];   // column tiles NH hf .. NH hf + NH - 1
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) dCacc[nt] = dBacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < NH; ++e) dCacc[e] = dBacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // wave 0 carries the first half's ddt and dA, dD parts of a head of 128
     // channels to the second half (the halves are consecutive in the walk)
@@ -357,17 +361,14 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         const bool first_half = a.hs == 2 && (h & 1) == 0;
         const float Ah = a.A[dh], Ah2 = Ah * kLog2eB, Dh = a.D[dh];
         // ---- stage this head; decays
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            *reinterpret_cast<uint4 *>(sm.X + (xr + 32 * k) * S64 + 8 * xc) = xv[k];
-            *reinterpret_cast<uint4 *>(sm.Y + (xr + 32 * k) * S64 + 8 * xc) = yv[k];
-        }
+        *reinterpret_cast<uint4 *>(sm.X + xr * S64 + 8 * xc) = xv;
+        *reinterpret_cast<uint4 *>(sm.Y + xr * S64 + 8 * xc) = yv;
         float hdot = 0.f;
 #pragma unroll
-        for (int k = 0; k < HCH; ++k) {
+        for (int k = 0; k < BPASS; ++k) {
             // two 4-value units of the state in accumulator order: unit U holds
             // p = 16 pq + l % 16, n = 16 u + 4 (l / 16) .. + 3 for U = (pq NT + u) 64 + l
-            const int U = 2 * (k * 256 + tid);
+            const int U = 2 * (k * 512 + tid);
             const int l = U % 64, u = (U / 64) % NT, pq = U / (64 * NT);
             const int p = 16 * pq + (l & 15), n = 16 * u + 4 * (l >> 4);
             *reinterpret_cast<uint2 *>(sm.H + p * SN + n) = uint2{hv[k].x, hv[k].y};
@@ -380,24 +381,26 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         }
         const float lam = wave_scan(dtv * Ah2);
         const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
-        if (w == 0) {
+        if (w8 == 0) {
             sm.lam[lane] = lam;
             sm.dtl[lane] = dtv;
             sm.ww[lane] = ex2f(lend - lam) * dtv;
             sm.ee[lane] = ex2f(lam);
         }
         hdot = wave_sum(hdot);
-        if (lane == 0) sm.red[w] = hdot;
+        if (lane == 0) sm.red[w8] = hdot;
         // the next head's inputs (the last head loads itself again)
         load_head(hh + 1 < hpg ? h + 1 : h);
         __syncthreads();
 
-        // ---- S = dy x^T for rows i of this wave; M^T, Q^T; sums for d/dLambda and ddt
+        // ---- S = dy x^T for rows i of this wave, column tiles of its half;
+        // M^T, Q^T; sums for d/dLambda and ddt
         float lam_i[4], zr[4] = {0.f, 0.f, 0.f, 0.f}, dd = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) lam_i[r] = sm.lam[16 * w + 4 * lgrp + r];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int e = 0; e < 2; ++e) {
+            const int jt = 2 * hf + e;
             f32x4 sd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -409,9 +412,9 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * lgrp + r;
                 const float E = j <= i ? ex2f(lam_i[r] - lam_j) : 0.f;
-                mv[r] = gm[jt][r] * E * dtj + (i == j ? Dh : 0.f);
+                mv[r] = gm[e][r] * E * dtj + (i == j ? Dh : 0.f);
                 qv[r] = sd[r] * E * dtj;
-                const float zrv = sd[r] * gm[jt][r] * E;
+                const float zrv = sd[r] * gm[e][r] * E;
                 zr[r] += zrv * dtj;
                 zc += zrv * dtj;
                 zrc += zrv;
@@ -425,19 +428,21 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float v = red16(zr[r]);
-            if (lrow == 0) sm.zrow[16 * w + 4 * lgrp + r] = v;
+            if (lrow == 0) sm.zrow[hf][16 * w + 4 * lgrp + r] = v;
         }
         dd = wave_sum(dd);
-        if (lane == 0) sm.red[4 + w] = dd;
+        if (lane == 0) sm.red[8 + w8] = dd;
         __syncthreads();
 
-        // ---- dx = M^T dy + w (Bm dH'^T), rows j; q_j = x_j . (dH' Bm_j)
+        // ---- dx = M^T dy + w (Bm dH'^T), rows j, column tiles pt of this
+        // half; q_j = x_j . (dH' Bm_j)
         {
             float qs[4] = {0.f, 0.f, 0.f, 0.f}, wj[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) wj[r] = sm.ww[16 * w + 4 * lgrp + r];
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
+            for (int e = 0; e < 2; ++e) {
+                const int pt = 2 * hf + e;
                 f32x4 dxa = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
@@ -457,16 +462,20 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = red16(qs[r]);
-                if (lrow == 0) sm.qv[16 * w + 4 * lgrp + r] = v;
+                if (lrow == 0) sm.qv[hf][16 * w + 4 * lgrp + r] = v;
             }
         }
+        // (the phases are kept apart: interleaved, their operands would not fit
+        // the registers of two waves per SIMD)
+        __builtin_amdgcn_sched_barrier(0);
         // ---- dCm rows i += exp(Lambda_i) dy H + Q Bm; u_i = Cm_i . (exp(Lambda_i) H^T dy_i)
         {
             float us[4] = {0.f, 0.f, 0.f, 0.f}, ei[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) ei[r] = sm.ee[16 * w + 4 * lgrp + r];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int e = 0; e < NH; ++e) {
+                const int nt = NH * hf + e;
                 f32x4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -478,22 +487,24 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const float ci = ei[r] * c1[r];
                     us[r] += (float)cin[r] * ci;
-                    dCacc[nt][r] += ci + c2[r];
+                    dCacc[e][r] += ci + c2[r];
                 }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = red16(us[r]);
-                if (lrow == 0) sm.uv[16 * w + 4 * lgrp + r] = v;
+                if (lrow == 0) sm.uv[hf][16 * w + 4 * lgrp + r] = v;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- dBm rows j += w_j x dH' + Q^T Cm
         {
             float wj[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) wj[r] = sm.ww[16 * w + 4 * lgrp + r];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int e = 0; e < NH; ++e) {
+                const int nt = NH * hf + e;
                 f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -501,13 +512,13 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
                     b2 = mfma(frag_row(sm.QT, 16 * w, S64, 32 * kk, lrow, lgrp), frag_col(sm.C, 16 * nt, SN, 32 * kk, lrow, lgrp), b2);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dBacc[nt][r] += wj[r] * b1[r] + b2[r];
+                for (int r = 0; r < 4; ++r) dBacc[e][r] += wj[r] * b1[r] + b2[r];
             }
         }
         __syncthreads();
 
         // ---- d/dLambda per token, ddt, and this head's parts of dA, dD (wave 0)
-        if (w == 0) {
+        if (w8 == 0) {
             const int k = lane;
             float zc = 0.f, zrc = 0.f;
 #pragma unroll
@@ -515,17 +526,21 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
                 zc += sm.zcolw[m][k];
                 zrc += sm.zrcolw[m][k];
             }
-            const float wk = sm.ww[k], qk = sm.qv[k];
-            float dl = sm.uv[k] + sm.zrow[k] - zc - wk * qk;
+            const float wk = sm.ww[k], qk = sm.qv[0][k] + sm.qv[1][k];
+            float dl = (sm.uv[0][k] + sm.uv[1][k]) + (sm.zrow[0][k] + sm.zrow[1][k]) - zc - wk * qk;
             const float wq = wave_sum(wk * qk);
-            const float hd = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+            float hd = 0.f, ddp = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                hd += sm.red[m];
+                ddp += sm.red[8 + m];
+            }
             if (k == 63) dl += ex2f(lend) * hd + wq;
             // rs_k = sum over i >= k of dl_i = total - (prefix through k) + dl_k
             const float pre = wave_scan(dl);
             const float rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), 63)) - pre + dl;
             const float g_dt = Ah * rs + zrc + ex2f(lend - sm.lam[k]) * qk;
             const float da = wave_sum(sm.dtl[k] * rs);
-            const float ddp = sm.red[4] + sm.red[5] + sm.red[6] + sm.red[7];
             if (first_half) {
                 ddt_half = g_dt;
                 da_half = da;
@@ -540,16 +555,16 @@ __global__ __launch_bounds__(256) void chunk_grad(BwdArgs a) {
         }
         __syncthreads();
     }
-    // ---- dCm, dBm of the group (all its heads)
+    // ---- dCm, dBm of the group (all its heads), this wave's column tiles
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int n = 16 * nt + lrow;
+    for (int e = 0; e < NH; ++e) {
+        const int n = 16 * (NH * hf + e) + lrow;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * w + 4 * lgrp + r;
             if (i < q) {
-                a.dCm[((row0 + i) * a.G + g) * N + n] = (__bf16)dCacc[nt][r];
-                a.dBm[((row0 + i) * a.G + g) * N + n] = (__bf16)dBacc[nt][r];
+                a.dCm[((row0 + i) * a.G + g) * N + n] = (__bf16)dCacc[e][r];
+                a.dBm[((row0 + i) * a.G + g) * N + n] = (__bf16)dBacc[e][r];
             }
         }
     }
@@ -587,7 +602,7 @@ template <int N>
 hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     const int64_t bhn = a.B * a.H;
     state_scans<N><<<dim3((unsigned)(2 * bhn)), 256, 0, stream>>>(a);
-    chunk_grad<N><<<dim3((unsigned)(a.B * a.G * a.nsb)), 256, 0, stream>>>(a);
+    chunk_grad<N><<<dim3((unsigned)(a.B * a.G * a.nsb)), 512, 0, stream>>>(a);
     reduce_head<<<dim3((unsigned)a.Hd), 256, 0, stream>>>(a);
     return hipGetLastError();
 }
