@@ -183,8 +183,12 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
 }
 
 // One state per lane, for N = 8 or 16: the lanes of a channel form one
-// DPP row (16 lanes) or half-row (8), so y of a token is a row sum without
-// LDS.  A workgroup takes CW = 256 / N channels of one batch row, so there
+// DPP row (16 lanes) or half-row (8), so y is summed over them with DPP, no
+// LDS.  The sums of N tokens are taken together (a transposing reduction:
+// log2 N exchange steps that halve the values each lane holds, ending with
+// lane n holding token n's sum), about 3 operations per token where a
+// separate row sum per token took 4 and a store from one lane (727 against
+// 612 us at the Mamba-1 2.8B shape).  A workgroup takes CW = 256 / N channels of one batch row, so there
 // are many small workgroups (Dch / CW per row): five per compute unit at the
 // Mamba-1 2.8B shape, every SIMD with the same load.  x, dt, Bm and Cm of a
 // chunk are staged transposed in fp32 ([channel or state][token]), so a lane
@@ -193,13 +197,40 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
 }
+// p[t], t < N, held by each of the N lanes of a channel: lane n gets the sum
+// over those lanes of p[n].  Each step pairs a lane with one that differs in
+// the next bit of n (and in the bits below it): the lane keeps the half of its
+// values that its bit names, adds the partner's values for that half, and
+// sends the other half; after log2 N steps one value is left, for token n.
 template <int N>
-__device__ __forceinline__ float lanes_sum(float v) {   // over the N lanes of a channel
-    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_mov<0x141>(v);   // row_half_mirror: the 8 lanes
-    if constexpr (N == 16) v += dpp_mov<0x140>(v);   // row_mirror: the 16 lanes
-    return v;
+__device__ __forceinline__ float lanes_transpose_sum(float (&p)[N], int n) {
+    if constexpr (N == 16) {
+        const bool hi = n & 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float keep = hi ? p[8 + j] : p[j], send = hi ? p[j] : p[8 + j];
+            p[j] = keep + dpp_mov<0x140>(send);   // row_mirror: lane 15 - n
+        }
+    }
+    {
+        const bool hi = n & 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float keep = hi ? p[4 + j] : p[j], send = hi ? p[j] : p[4 + j];
+            p[j] = keep + dpp_mov<0x141>(send);   // row_half_mirror: lane 7 - n of the 8
+        }
+    }
+    {
+        const bool hi = n & 2;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float keep = hi ? p[2 + j] : p[j], send = hi ? p[j] : p[2 + j];
+            p[j] = keep + dpp_mov<0x1B>(send);    // quad_perm [3,2,1,0]
+        }
+    }
+    const bool hi = n & 1;
+    const float keep = hi ? p[1] : p[0], send = hi ? p[0] : p[1];
+    return keep + dpp_mov<0xB1>(send);            // quad_perm [1,0,3,2]
 }
 
 template <int N, bool kZoh>
@@ -286,25 +317,29 @@ __global__ __launch_bounds__(256) void s6_lane_kernel(S6Args a) {
         const int buf = k & 1;
         const int nt = (int)(L - (int64_t)k * kT < kT ? L - (int64_t)k * kT : kT);
 #pragma unroll
-        for (int t4 = 0; t4 < kT; t4 += 4) {
-            const float4 x4 = *reinterpret_cast<const float4 *>(&xt[buf][ci][t4]);
-            const float4 d4 = *reinterpret_cast<const float4 *>(&dtt[buf][ci][t4]);
-            const float4 b4 = *reinterpret_cast<const float4 *>(&bt[buf][n][t4]);
-            const float4 c4 = *reinterpret_cast<const float4 *>(&ct[buf][n][t4]);
-            const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
-            const float bs[4] = {b4.x, b4.y, b4.z, b4.w}, cs[4] = {c4.x, c4.y, c4.z, c4.w};
+        for (int tg = 0; tg < kT; tg += N) {
+            float p[N];   // C h of tokens tg .. tg + N - 1 for this lane's state
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float av = __builtin_amdgcn_exp2f(ds[e] * A2);
-                if constexpr (kZoh) {
-                    const float coef = __builtin_fmaf(zf, ds[e], __builtin_fmaf(av, invA, -invA));
-                    h = __builtin_fmaf(av, h, coef * (bs[e] * xs[e]));
-                } else {
-                    h = __builtin_fmaf(av, h, (ds[e] * xs[e]) * bs[e]);
+            for (int t4 = 0; t4 < N; t4 += 4) {
+                const float4 x4 = *reinterpret_cast<const float4 *>(&xt[buf][ci][tg + t4]);
+                const float4 d4 = *reinterpret_cast<const float4 *>(&dtt[buf][ci][tg + t4]);
+                const float4 b4 = *reinterpret_cast<const float4 *>(&bt[buf][n][tg + t4]);
+                const float4 c4 = *reinterpret_cast<const float4 *>(&ct[buf][n][tg + t4]);
+                const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float bs[4] = {b4.x, b4.y, b4.z, b4.w}, cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float av = __builtin_amdgcn_exp2f(ds[e] * A2);
+                    if constexpr (kZoh) {
+                        const float coef = __builtin_fmaf(zf, ds[e], __builtin_fmaf(av, invA, -invA));
+                        h = __builtin_fmaf(av, h, coef * (bs[e] * xs[e]));
+                    } else {
+                        h = __builtin_fmaf(av, h, (ds[e] * xs[e]) * bs[e]);
+                    }
+                    p[t4 + e] = cs[e] * h;
                 }
-                const float yv = lanes_sum<N>(cs[e] * h);
-                if (n == 0) yt[t4 + e][ci] = yv;
             }
+            yt[tg + n][ci] = lanes_transpose_sum<N>(p, n);
         }
         __syncthreads();
         // y rows of the chunk: CW channels (plus D x) per token, 16 bytes per thread
