@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssd {
 
 namespace {
@@ -233,8 +235,11 @@ __device__ __forceinline__ float lanes_transpose_sum(float (&p)[N], int n) {
     return keep + dpp_mov<0xB1>(send);            // quad_perm [1,0,3,2]
 }
 
+// At most 96 registers at N = 16 and 128 at N = 8 (five and four waves per
+// SIMD): at N = 16 the five workgroups a compute unit gets at the Mamba-1
+// 2.8B shape then run at once.
 template <int N, bool kZoh>
-__global__ __launch_bounds__(256) void s6_lane_kernel(S6Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(N == 16 ? 5 : 4))) void s6_lane_kernel(S6Args a) {
     constexpr int CW = 256 / N;          // channels per workgroup
     constexpr int TS = kT + 4;           // row of the transposed tiles (fp32)
     constexpr int XU = kT * CW / 8;      // 16-byte units of the x (and dt) tile
@@ -312,56 +317,71 @@ __global__ __launch_bounds__(256) void s6_lane_kernel(S6Args a) {
     load(0);
     stage(0);
     if (nchunks > 1) load(kT);
-    __syncthreads();
-    for (int k = 0; k < nchunks; ++k) {
-        const int buf = k & 1;
-        const int nt = (int)(L - (int64_t)k * kT < kT ? L - (int64_t)k * kT : kT);
+    const bool any_zero = __syncthreads_or(kZoh && Av == 0.f);
+    // a state with A = 0 anywhere in the workgroup needs the limit term of the
+    // zero-order hold; without one the update is one operation shorter.  The
+    // choice is uniform over the workgroup, so each copy of the unrolled chunk
+    // loop runs with no branch inside.
+    auto chunks = [&](auto limit) __attribute__((always_inline)) {
+        constexpr bool kLimit = decltype(limit)::value;
+        for (int k = 0; k < nchunks; ++k) {
+            const int buf = k & 1;
+            const int nt = (int)(L - (int64_t)k * kT < kT ? L - (int64_t)k * kT : kT);
 #pragma unroll
-        for (int tg = 0; tg < kT; tg += N) {
-            float p[N];   // C h of tokens tg .. tg + N - 1 for this lane's state
+            for (int tg = 0; tg < kT; tg += N) {
+                float p[N];   // C h of tokens tg .. tg + N - 1 for this lane's state
 #pragma unroll
-            for (int t4 = 0; t4 < N; t4 += 4) {
-                const float4 x4 = *reinterpret_cast<const float4 *>(&xt[buf][ci][tg + t4]);
-                const float4 d4 = *reinterpret_cast<const float4 *>(&dtt[buf][ci][tg + t4]);
-                const float4 b4 = *reinterpret_cast<const float4 *>(&bt[buf][n][tg + t4]);
-                const float4 c4 = *reinterpret_cast<const float4 *>(&ct[buf][n][tg + t4]);
-                const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
-                const float bs[4] = {b4.x, b4.y, b4.z, b4.w}, cs[4] = {c4.x, c4.y, c4.z, c4.w};
+                for (int t4 = 0; t4 < N; t4 += 4) {
+                    const float4 x4 = *reinterpret_cast<const float4 *>(&xt[buf][ci][tg + t4]);
+                    const float4 d4 = *reinterpret_cast<const float4 *>(&dtt[buf][ci][tg + t4]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&bt[buf][n][tg + t4]);
+                    const float4 c4 = *reinterpret_cast<const float4 *>(&ct[buf][n][tg + t4]);
+                    const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ds[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const float bs[4] = {b4.x, b4.y, b4.z, b4.w}, cs[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float av = __builtin_amdgcn_exp2f(ds[e] * A2);
-                    if constexpr (kZoh) {
-                        const float coef = __builtin_fmaf(zf, ds[e], __builtin_fmaf(av, invA, -invA));
-                        h = __builtin_fmaf(av, h, coef * (bs[e] * xs[e]));
-                    } else {
-                        h = __builtin_fmaf(av, h, (ds[e] * xs[e]) * bs[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const float av = __builtin_amdgcn_exp2f(ds[e] * A2);
+                        if constexpr (kZoh && kLimit) {
+                            const float coef = __builtin_fmaf(zf, ds[e], __builtin_fmaf(av, invA, -invA));
+                            h = __builtin_fmaf(av, h, coef * (bs[e] * xs[e]));
+                        } else if constexpr (kZoh) {
+                            // (av - 1) / A Bm x as (av - 1) g, g = Bm x / A, in one rounding
+                            const float gx = (invA * bs[e]) * xs[e];
+                            h = __builtin_fmaf(av, h, __builtin_fmaf(av, gx, -gx));
+                        } else {
+                            h = __builtin_fmaf(av, h, (ds[e] * xs[e]) * bs[e]);
+                        }
+                        p[t4 + e] = cs[e] * h;
                     }
-                    p[t4 + e] = cs[e] * h;
                 }
+                yt[tg + n][ci] = lanes_transpose_sum<N>(p, n);
             }
-            yt[tg + n][ci] = lanes_transpose_sum<N>(p, n);
-        }
-        __syncthreads();
-        // y rows of the chunk: CW channels (plus D x) per token, 16 bytes per thread
-        for (int u = tid; u < kT * CW / 8; u += 256) {
-            const int r = u / (CW / 8), col = (u % (CW / 8)) * 8;
-            if (r < nt) {
-                typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-                bf16x8_t ov;
+            __syncthreads();
+            // y rows of the chunk: CW channels (plus D x) per token, 16 bytes per thread
+            for (int u = tid; u < kT * CW / 8; u += 256) {
+                const int r = u / (CW / 8), col = (u % (CW / 8)) * 8;
+                if (r < nt) {
+                    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+                    bf16x8_t ov;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float dd = a.D ? a.D[c0 + col + e] : 0.f;
-                    ov[e] = (__bf16)__builtin_fmaf(dd, xt[buf][col + e][r], yt[r][col + e]);
+                    for (int e = 0; e < 8; ++e) {
+                        const float dd = a.D ? a.D[c0 + col + e] : 0.f;
+                        ov[e] = (__bf16)__builtin_fmaf(dd, xt[buf][col + e][r], yt[r][col + e]);
+                    }
+                    *reinterpret_cast<bf16x8_t *>(a.y + (b * L + (int64_t)k * kT + r) * a.Dch + c0 + col) = ov;
                 }
-                *reinterpret_cast<bf16x8_t *>(a.y + (b * L + (int64_t)k * kT + r) * a.Dch + c0 + col) = ov;
             }
+            if (k + 1 < nchunks) {
+                stage(buf ^ 1);
+                if (k + 2 < nchunks) load((int64_t)(k + 2) * kT);
+            }
+            __syncthreads();
         }
-        if (k + 1 < nchunks) {
-            stage(buf ^ 1);
-            if (k + 2 < nchunks) load((int64_t)(k + 2) * kT);
-        }
-        __syncthreads();
-    }
+    };
+    if (any_zero)
+        chunks(std::true_type{});
+    else
+        chunks(std::false_type{});
     if (a.final_state) a.final_state[(b * a.Dch + c) * N + n] = h;
 }
 
