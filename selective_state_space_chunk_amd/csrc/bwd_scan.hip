@@ -253,10 +253,15 @@ struct GradSmem {
     __bf16 dH[64 * SN];      // dH' [p][n]
     __bf16 MT[64 * S64];     // M^T [j][i]
     __bf16 QT[64 * S64];     // Q^T [j][i]
+    __bf16 DX[64 * S64];     // dx [j][p] of the head, on its way to global memory as whole rows
     float lam[64], dtl[64], ww[64], ee[64];
     float zcolw[16][64], zrcolw[16][64];               // column parts per (row wave, lane row)
     float zrow[2][64], qv[2][64], uv[2][64];           // row parts per column half
     float red[16];
+    // ddt of up to kDdtHeads consecutive heads [token][head], written to
+    // global memory together as runs of consecutive heads per token row
+    static constexpr int kDdtHeads = 16;
+    float ddt[64][kDdtHeads + 1];
 };
 
 // The four values a lane's accumulator covers, (r0 + 4 lgrp + r, c0 + lrow) for
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
     // wave 0 carries the first half's ddt and dA, dD parts of a head of 128
     // channels to the second half (the halves are consecutive in the walk)
     float ddt_half = 0.f, da_half = 0.f, dd_half = 0.f;
+    const int64_t dh0 = g * hpg / a.hs;   // the group's first caller head
     for (int64_t hh = 0; hh < hpg; ++hh) {
         const int64_t h = g * hpg + hh, dh = h / a.hs;
         const bool first_half = a.hs == 2 && (h & 1) == 0;
@@ -456,7 +462,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * w + 4 * lgrp + r;
                     qs[r] += (float)xj[r] * vv[r];
-                    if (j < q) a.dx[((row0 + j) * a.H + h) * kP + p] = (__bf16)(dxa[r] + wj[r] * vv[r]);
+                    sm.DX[j * S64 + p] = (__bf16)(dxa[r] + wj[r] * vv[r]);
                 }
             }
 #pragma unroll
@@ -517,6 +523,10 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         }
         __syncthreads();
 
+        // ---- dx of the head: 64 rows of 128 bytes, 16 bytes per thread
+        if (xr < q)
+            *reinterpret_cast<uint4 *>(a.dx + ((row0 + xr) * a.H + h) * kP + 8 * xc) =
+                *reinterpret_cast<const uint4 *>(sm.DX + xr * S64 + 8 * xc);
         // ---- d/dLambda per token, ddt, and this head's parts of dA, dD (wave 0)
         if (w8 == 0) {
             const int k = lane;
@@ -546,7 +556,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
                 da_half = da;
                 dd_half = ddp;
             } else {
-                if (k < q) a.ddt[(row0 + k) * a.Hd + dh] = ddt_half + g_dt;
+                sm.ddt[k][(dh - dh0) % GradSmem<N>::kDdtHeads] = ddt_half + g_dt;
                 if (k == 0) {
                     a.dAp[(b * a.Hd + dh) * nsb + c] = da_half + da;
                     a.dDp[(b * a.Hd + dh) * nsb + c] = dd_half + ddp;
@@ -554,6 +564,20 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             }
         }
         __syncthreads();
+        // ---- ddt of the last kDdtHeads heads (or of the group's last ones)
+        {
+            constexpr int KD = GradSmem<N>::kDdtHeads;
+            const int64_t done = dh - dh0 + 1;   // caller heads of the group finished
+            const bool last = hh + 1 == hpg;
+            if ((!first_half && done % KD == 0) || last) {
+                const int nh = (int)(done % KD == 0 ? KD : done % KD);
+                const int64_t base = dh0 + done - nh;
+                for (int e = tid; e < 64 * KD; e += 512) {
+                    const int k = e / KD, m = e % KD;
+                    if (k < q && m < nh) a.ddt[(row0 + k) * a.Hd + base + m] = sm.ddt[k][m];
+                }
+            }
+        }
     }
     // ---- dCm, dBm of the group (all its heads), this wave's column tiles
 #pragma unroll
