@@ -190,11 +190,11 @@ __global__ __launch_bounds__(256) void s6_kernel(S6Args a) {
 // log2 N exchange steps that halve the values each lane holds, ending with
 // lane n holding token n's sum), about 3 operations per token where a
 // separate row sum per token took 4 and a store from one lane (727 against
-// 612 us at the Mamba-1 2.8B shape).  A workgroup takes CW = 256 / N channels of one batch row, so there
-// are many small workgroups (Dch / CW per row): five per compute unit at the
-// Mamba-1 2.8B shape, every SIMD with the same load.  x, dt, Bm and Cm of a
-// chunk are staged transposed in fp32 ([channel or state][token]), so a lane
-// reads four tokens per LDS load.
+// 612 us at the Mamba-1 2.8B shape).  A workgroup takes CW = 256 / N
+// channels of one batch row, so there are many small workgroups (Dch / CW
+// per row): five per compute unit at the Mamba-1 2.8B shape, every SIMD with
+// the same load.  x, dt, Bm and Cm of a chunk are staged transposed in fp32
+// ([channel or state][token]), so a lane reads four tokens per LDS load.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, true));
