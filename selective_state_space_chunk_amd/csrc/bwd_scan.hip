@@ -47,8 +47,9 @@ struct BwdArgs {
     float *ddt, *dA, *dD, *dinit;              // dinit nullable
     float *Hs;    // [B*H, nsb, P*N] bf16  state entering each sub-block
     float *dHs;   // [B*H, nsb, P*N] bf16  adjoint of the state leaving each sub-block
-                  // (both in accumulator order: 4-value unit ((pq*NT + u)*64 + lane)
-                  //  holds p = 16pq + lane%16, n = 16u + 4(lane/16) + 0..3)
+                  // (both in accumulator order, two tiles per lane and store: the
+                  //  16-byte unit ((pq*NT/2 + v)*64 + lane) holds p = 16pq + lane%16,
+                  //  n = 32v + 4(lane/16) + 0..3, then n + 16 .. + 19)
     float *dAp;   // [B*Hd, nsb]  each head's part of dA from each sub-block
     float *dDp;   // [B*Hd, nsb]
     int64_t B, L, H, G, nsb;   // H: heads of 64 channels (x, dy, dx, states, init, dfinal, dinit)
@@ -155,8 +156,10 @@ __device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
     }
     load(0, 0);
     load(1, 1);
-    // states go out in accumulator order, 512 contiguous bytes per store
-    __bf16 *sbase = reinterpret_cast<__bf16 *>(kRev ? a.dHs : a.Hs) + bh * a.nsb * (kP * N) + 4 * (pq * NT * 64 + lane);
+    // states go out in accumulator order, two n-tiles per lane: 1 KB of
+    // contiguous bytes per store
+    __bf16 *sbase = reinterpret_cast<__bf16 *>(kRev ? a.dHs : a.Hs) + bh * a.nsb * (kP * N) +
+                    8 * (pq * (NT / 2) * 64 + lane);
     const int row_k0 = tid >> 3;   // staged rows row_k0 and row_k0 + 32 of u
     auto step = [&](int s, int par) __attribute__((always_inline)) {
         const int c = kRev ? nsb - 1 - s : s;
@@ -165,9 +168,10 @@ __device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
         const float om = kRev ? ex2f(v) : ex2f(lend - v) * dtv[par];
         const float gam = ex2f(lend);
 #pragma unroll
-        for (int u = 0; u < NT; ++u)
-            *reinterpret_cast<uint2 *>(sbase + (int64_t)c * (kP * N) + 4 * 64 * u) =
-                uint2{pack2(Hacc[u][0], Hacc[u][1]), pack2(Hacc[u][2], Hacc[u][3])};
+        for (int v = 0; v < NT / 2; ++v)
+            *reinterpret_cast<uint4 *>(sbase + (int64_t)c * (kP * N) + 8 * 64 * v) =
+                uint4{pack2(Hacc[2 * v][0], Hacc[2 * v][1]), pack2(Hacc[2 * v][2], Hacc[2 * v][3]),
+                      pack2(Hacc[2 * v + 1][0], Hacc[2 * v + 1][1]), pack2(Hacc[2 * v + 1][2], Hacc[2 * v + 1][3])};
         // u weighted by om, and Mt, into LDS
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -372,15 +376,16 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         float hdot = 0.f;
 #pragma unroll
         for (int k = 0; k < BPASS; ++k) {
-            // two 4-value units of the state in accumulator order: unit U holds
-            // p = 16 pq + l % 16, n = 16 u + 4 (l / 16) .. + 3 for U = (pq NT + u) 64 + l
-            const int U = 2 * (k * 512 + tid);
-            const int l = U % 64, u = (U / 64) % NT, pq = U / (64 * NT);
-            const int p = 16 * pq + (l & 15), n = 16 * u + 4 * (l >> 4);
+            // one 16-byte unit of the state in accumulator order: unit U =
+            // (pq NT/2 + v) 64 + l holds p = 16 pq + l % 16, n = 32 v + 4 (l / 16)
+            // .. + 3 and n + 16 .. + 19
+            const int U = k * 512 + tid;
+            const int l = U % 64, v = (U / 64) % (NT / 2), pq = U / (64 * (NT / 2));
+            const int p = 16 * pq + (l & 15), n = 32 * v + 4 * (l >> 4);
             *reinterpret_cast<uint2 *>(sm.H + p * SN + n) = uint2{hv[k].x, hv[k].y};
-            *reinterpret_cast<uint2 *>(sm.H + (p + 1) * SN + n) = uint2{hv[k].z, hv[k].w};
+            *reinterpret_cast<uint2 *>(sm.H + p * SN + n + 16) = uint2{hv[k].z, hv[k].w};
             *reinterpret_cast<uint2 *>(sm.dH + p * SN + n) = uint2{dv[k].x, dv[k].y};
-            *reinterpret_cast<uint2 *>(sm.dH + (p + 1) * SN + n) = uint2{dv[k].z, dv[k].w};
+            *reinterpret_cast<uint2 *>(sm.dH + p * SN + n + 16) = uint2{dv[k].z, dv[k].w};
             const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv[k]), d8 = __builtin_bit_cast(bf16x8, dv[k]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) hdot += (float)h8[e] * (float)d8[e];
