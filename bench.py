@@ -118,9 +118,18 @@ def step_algorithmic(B, H, P, N, G, e=2):
     return byts
 
 
+_SETS = {}
+
+
 def make_device_sets(w, nsets, device):
+    """Seeded input sets of workload w, resident on the device; made once per
+    (workload, count, device) and shared by the measurements that use them
+    (each writes only outputs of its own)."""
     import torch
     import ssd_inputs as si
+    key = (w.name, nsets, str(device))
+    if key in _SETS:
+        return _SETS[key]
     sets = []
     for k in range(nsets):
         d = si.make_scan_inputs(w.B, w.L, w.H, w.P, w.N, w.G, dtype=w.dtype, init=w.init,
@@ -136,7 +145,55 @@ def make_device_sets(w, nsets, device):
         td["y"] = torch.empty_like(td["x"])
         td["final"] = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device=device)
         sets.append(td)
+    _SETS[key] = sets
     return sets
+
+
+def add_grad_inputs(w, sets, device):
+    """dy and dfinal of each input set (seeded), for the backward."""
+    import torch
+    import ssd_inputs as si
+    for k, s in enumerate(sets):
+        if "dy" not in s:
+            g = si.make_grad_inputs(w.B, w.L, w.H, w.P, w.N, dtype=w.dtype, seed=w.seed + 100 * k + 7)
+            s["dy"] = torch.from_numpy(g["dy"]).to(device=device, dtype=io_dtype(w))
+            s["dfinal"] = torch.from_numpy(g["dfinal"]).to(device=device)
+
+
+def add_varlen_inputs(w, sets, device):
+    """Document boundaries of each input set: rows packed with documents of
+    log-normal length (median VARLEN_MEAN_LEN tokens, the last one cut at
+    the row's end); returns the number of documents per set."""
+    import torch
+    import ssd_inputs as si
+    for k, s in enumerate(sets):
+        if "seq" not in s:
+            seq = si.make_seq_idx(w.B, w.L, mean_len=VARLEN_MEAN_LEN, seed=w.seed + 100 * k + 9)
+            s["nseq"] = int(sum(seq[b, -1] + 1 for b in range(w.B)))
+            s["seq"] = torch.from_numpy(seq).to(device)
+            s["yv"] = torch.empty_like(s["x"])
+            s["fv"] = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device=device)
+    return [s["nseq"] for s in sets]
+
+
+_STEP = {}
+
+
+def step_inputs(B, H, P, N, G, device):
+    """The decode state and four tokens' inputs (seeded), resident on the
+    device; made once per shape."""
+    import torch
+    import ssd_inputs as si
+    key = (B, H, P, N, G, str(device))
+    if key not in _STEP:
+        st = torch.from_numpy(si.make_step_state(B, H, P, N, seed=si.SEED_BASE + 4)).to(device)
+        ins = []
+        for t in range(4):
+            s = si.make_step_inputs(B, H, P, N, G, step=t, dtype="bf16", seed=si.SEED_BASE + 4)
+            ins.append({k: torch.from_numpy(v).to(device, dtype=torch.bfloat16 if k in ("x", "Bm", "Cm")
+                                                   else torch.float32) for k, v in s.items()})
+        _STEP[key] = (st, ins, [torch.empty_like(i["x"]) for i in ins])
+    return _STEP[key]
 
 
 def io_dtype(w):
@@ -159,17 +216,22 @@ def time_scan(w, steps, warmup, device, algo="auto"):
     for k in range(warmup):
         run(k)
     torch.cuda.synchronize(device)
-    # per-launch events on the stream the library launches on (the current stream)
+    # the timed steps: back to back, the wall clock around them
+    t0 = time.perf_counter()
+    for k in range(steps):
+        run(k)
+    torch.cuda.synchronize(device)
+    wall = time.perf_counter() - t0
+    # then the same number of calls again, each between two events on the
+    # stream the library launches on (the current stream): the kernels' own
+    # time, without the gaps the event markers add between calls
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize(device)
-    t0 = time.perf_counter()
     for k in range(steps):
         starts[k].record()
         run(k)
         ends[k].record()
     torch.cuda.synchronize(device)
-    wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms
     return wall, per
 
@@ -177,14 +239,7 @@ def time_scan(w, steps, warmup, device, algo="auto"):
 def time_step(B, H, P, N, G, steps, warmup, device):
     import torch
     import selective_state_space_chunk_amd as ssd
-    import ssd_inputs as si
-    st = torch.from_numpy(si.make_step_state(B, H, P, N, seed=si.SEED_BASE + 4)).to(device)
-    ins = []
-    for t in range(4):
-        s = si.make_step_inputs(B, H, P, N, G, step=t, dtype="bf16", seed=si.SEED_BASE + 4)
-        ins.append({k: torch.from_numpy(v).to(device, dtype=torch.bfloat16 if k in ("x", "Bm", "Cm")
-                                               else torch.float32) for k, v in s.items()})
-    ys = [torch.empty_like(i["x"]) for i in ins]
+    st, ins, ys = step_inputs(B, H, P, N, G, device)
     for k in range(warmup):
         i = ins[k % 4]
         ssd.ssd_step(st, i["x"], i["dt"], i["A"], i["Bm"], i["Cm"], i["D"], y=ys[k % 4])
@@ -206,10 +261,7 @@ def time_backward(w, steps, warmup, device):
     import selective_state_space_chunk_amd as ssd
     import ssd_inputs as si
     sets = make_device_sets(w, 3, device)
-    for k, s in enumerate(sets):
-        g = si.make_grad_inputs(w.B, w.L, w.H, w.P, w.N, dtype=w.dtype, seed=w.seed + 100 * k + 7)
-        s["dy"] = torch.from_numpy(g["dy"]).to(device=device, dtype=io_dtype(w))
-        s["dfinal"] = torch.from_numpy(g["dfinal"]).to(device=device)
+    add_grad_inputs(w, sets, device)
     nbytes = ssd.ssd_chunk_scan_bwd_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
@@ -295,13 +347,7 @@ def time_varlen(w, steps, warmup, device):
     import selective_state_space_chunk_amd as ssd
     import ssd_inputs as si
     sets = make_device_sets(w, 3, device)
-    nseq = []
-    for k, s in enumerate(sets):
-        seq = si.make_seq_idx(w.B, w.L, mean_len=VARLEN_MEAN_LEN, seed=w.seed + 100 * k + 9)
-        nseq.append(int(sum(seq[b, -1] + 1 for b in range(w.B))))
-        s["seq"] = torch.from_numpy(seq).to(device)
-        s["yv"] = torch.empty_like(s["x"])
-        s["fv"] = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device=device)
+    nseq = add_varlen_inputs(w, sets, device)
     nbytes = ssd.ssd_chunk_scan_varlen_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk, io_dtype(w))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
@@ -403,17 +449,18 @@ def cpu_baseline(w, budget_s=15.0):
                       f"tokens/s = runs*sequences*L/s / H"}
 
 
-def copy_bandwidth(device, mb=512, reps=10):
+def copy_bandwidth(device, mb=512, reps=10, warm=200):
     """Measured bandwidth (GB/s, bytes read + written) of the library's own
     streaming copy (ssd_stream_copy) of `mb` megabytes, median of `reps`
-    event-timed launches: what a kernel with no arithmetic moves here, the
+    event-timed launches after `warm` untimed ones (~30 ms, the clock ramp
+    of an idle device): what a kernel with no arithmetic moves here, the
     practical ceiling the achieved bandwidths are also reported against."""
     import torch
     import selective_state_space_chunk_amd as ssd
     n = int(mb * 1e6) // 16 * 4
     src = torch.ones(n, dtype=torch.float32, device=device)
     dst = torch.empty_like(src)
-    for _ in range(2):
+    for _ in range(warm):
         ssd.ssd_stream_copy(dst, src)
     torch.cuda.synchronize(device)
     times = []
@@ -641,15 +688,122 @@ def main():
         raise SystemExit(f"unknown scan workload {args.workload!r}")
     w = si.WORKLOADS[args.workload]
     headline = args.workload == "m2_2p7b"
-    wall, per = time_scan(w, args.steps, args.warmup, device)
-    ms_step = wall * 1000.0 / args.steps
-    kern_ms = sum(per) / len(per)
     # the flops of the decomposition the kernels run: 64-token sub-blocks on
     # the per-sequence scan, blocks of the chunk size otherwise
     block = 64 if per_sequence_scan(w) else w.chunk
     byts, flops = scan_algorithmic(w, block)
-    achieved = byts / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.L
+    do_backward = not args.no_backward and (headline or (w.P == 128 and w.N <= 128 and w.dtype == "bf16"))
+    # Every input is made first and kept resident; the measurements then run
+    # back to back with no host work between them, the headline call last.
+    # After an idle spell the device's clocks ramp up over the first ~200
+    # calls (~30 ms) of sustained load (the headline call takes ~230 us cold
+    # and ~146 us in steady state), so a call timed a few calls after the
+    # host-side setup would measure the ramp rather than the kernel.
+    make_device_sets(w, 3, device)
+    if not args.no_decode:
+        step_inputs(256, 80, 64, 128, 1, device)
+    if do_backward:
+        add_grad_inputs(w, make_device_sets(w, 3, device), device)
+    if not args.no_varlen and headline:
+        add_varlen_inputs(w, make_device_sets(w, 3, device), device)
+    torch.cuda.synchronize(device)
+    extra = {}
+    copy_gbs = copy_bandwidth(device)
+    if not args.no_decode:
+        B, H, P, N, G = 256, 80, 64, 128, 1
+        sp = time_step(B, H, P, N, G, max(20, args.steps // 2), 5, device)
+        smean = sum(sp) / len(sp)
+        sb = step_algorithmic(B, H, P, N, G)
+        extra["decode"] = {"workload": "mamba2_2.7b_layer_ssd_step", "batch": B, "heads": H,
+                           "head_dim": P, "state": N, "us_per_step": smean * 1000.0,
+                           "tokens_per_s": B / (smean * 1e-3), "kernel": f"step_kernel<bf16, {P}, {N}>",
+                           "roofline": {"bound": "hbm", "achieved": sb / (smean * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
+                                        "traffic": step_traffic(), "algorithmic_bytes": sb}}
+    if do_backward:
+        # the backward at the layer shape, and at its head-dim-128 form
+        bp = time_backward(w, max(10, args.steps // 5), 3, device)
+        bmean = sum(bp) / len(bp)
+        bb = bwd_algorithmic(w)
+        extra["backward"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_backward",
+                             "us_per_call": bmean * 1000.0, "us_median": bp[len(bp) // 2] * 1000.0,
+                             "tokens_per_s": tokens / (bmean * 1e-3),
+                             "kernels": f"state_scans<{w.N}> (forward and adjoint states) + chunk_grad<{w.N}> + "
+                                        "reduce_head",
+                             "roofline": {"bound": "hbm", "achieved": bb / (bmean * 1e-3) / 1e9,
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                          "traffic": bwd_traffic() if headline else None,
+                                          "algorithmic_bytes": bb}}
+    if not args.no_block and headline:
+        tp, tn = time_block(w, max(10, args.steps // 2), 3, device)
+        pb, nb = block_algorithmic(w)
+
+        def leg(ts, nbytes, kernel):
+            m = sum(ts) / len(ts)
+            return {"kernel": kernel, "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
+                    "roofline": {"bound": "hbm", "achieved": nbytes / (m * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": nbytes}}
+        extra["block"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name).replace("_ssd_chunk_scan", "_block_steps"),
+                          "conv_width": CONV_WIDTH, "norm": "group norm, 1 group, eps 1e-5",
+                          "prologue": leg(tp, pb, f"prologue_kernel<{CONV_WIDTH}>"),
+                          "gated_norm": leg(tn, nb, "gated_norm_kernel")}
+    if not args.no_s6 and headline:
+        ts = time_s6(max(10, args.steps // 2), 3, device)
+        m = sum(ts) / len(ts)
+        sh = S6_SHAPE
+        toks = sh["batch"] * sh["seq_len"]
+        updates = toks * sh["channels"] * sh["state"]
+        peak = VALU_LANE_SLOTS / S6_SLOTS_PER_UPDATE
+        nbytes = 3 * toks * sh["channels"] * 2 + 2 * toks * sh["state"] * 2 + 2 * sh["batch"] * sh["channels"] * sh["state"] * 4
+        extra["s6"] = {"workload": "mamba1_2.8b_layer_selective_scan", "config": dict(sh, discretisation="zero-order hold"),
+                       "kernel": "s6_lane_kernel<16, true>", "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
+                       "tokens_per_s": toks / (m * 1e-3),
+                       "roofline": {"bound": "alu", "achieved": updates / (m * 1e-3) / 1e12, "peak": peak / 1e12,
+                                    "unit": "T state updates/s", "frac": updates / (m * 1e-3) / peak,
+                                    "hbm_gbs": nbytes / (m * 1e-3) / 1e9, "algorithmic_bytes": nbytes}}
+    if not args.no_staged and headline and w.P == 64:
+        # the pages' own four-step form (block states in HBM, a separate state
+        # pass) at the same shape, as an explicit choice: not the headline value
+        _, sp = time_scan(w, max(10, args.steps // 5), 3, device, algo="staged")
+        smean = sum(sp) / len(sp)
+        nc = -(-w.L // w.chunk)
+        # the state pass reads every block's local state and the initial state,
+        # and writes every block's entering state and the final state
+        state_bytes = 2 * w.B * (nc + 1) * w.H * w.P * w.N * 4
+        extra["staged"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_staged_form", "chunk": w.chunk,
+                           "us_per_call": smean * 1000.0, "us_median": sp[len(sp) // 2] * 1000.0,
+                           "tokens_per_s": tokens / (smean * 1e-3),
+                           "kernels": f"gram_kernel<{w.N}> + scan_mfma<{w.N}, {w.chunk}, kState> + state_pass_kernel + "
+                                      f"scan_mfma<{w.N}, {w.chunk}, kOutput>",
+                           "state_pass_bytes": state_bytes,
+                           "roofline": {"bound": "hbm", "achieved": byts / (smean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                        "unit": "GB/s", "frac": byts / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": byts}}
+    if not args.no_varlen and headline:
+        # timed last before the headline call, whose kernels it shares but for
+        # the reset masks, over enough calls (~30 ms) to hold the device at
+        # its sustained clocks
+        vp, nseq = time_varlen(w, max(200, args.steps // 2), 3, device)
+        vmean = sum(vp) / len(vp)
+        vb = scan_algorithmic(w)[0] + w.B * w.L * 4      # + seq_idx
+        extra["varlen"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_packed_documents",
+                           "documents_per_call": nseq, "median_document_tokens": VARLEN_MEAN_LEN,
+                           "us_per_call": vmean * 1000.0, "us_median": vp[len(vp) // 2] * 1000.0,
+                           "tokens_per_s": tokens / (vmean * 1e-3),
+                           "kernels": "mark_resets + prep_kernel<128, true> + pipe_kernel<128, true>",
+                           "roofline": {"bound": "hbm", "achieved": vb / (vmean * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": vb / (vmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "algorithmic_bytes": vb}}
+    wall, per = time_scan(w, args.steps, args.warmup, device)
+    ms_step = wall * 1000.0 / args.steps
+    kern_ms = sum(per) / len(per)
+    achieved = byts / (kern_ms * 1e-3) / 1e9
     metric = HEADLINE_METRIC if headline else \
         f"SSD chunk-scan fwd tokens/s at {WORKLOAD_DESC.get(w.name, w.name)}; % of roofline"
     kernels = (f"gram tiles (gram_kernel, or prep_kernel<{w.N}> with the segment states) + pipe_kernel<{w.N}>"
@@ -678,96 +832,10 @@ def main():
                      "algorithmic_bytes": byts, "algorithmic_flops": flops, "flops_block_tokens": block,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
-    copy_gbs = copy_bandwidth(device)
     out["roofline"]["copy_gbs"] = copy_gbs
     out["roofline"]["frac_of_copy"] = achieved / copy_gbs
-    if not args.no_decode:
-        B, H, P, N, G = 256, 80, 64, 128, 1
-        sp = time_step(B, H, P, N, G, max(20, args.steps // 2), 5, device)
-        smean = sum(sp) / len(sp)
-        sb = step_algorithmic(B, H, P, N, G)
-        out["decode"] = {"workload": "mamba2_2.7b_layer_ssd_step", "batch": B, "heads": H,
-                         "head_dim": P, "state": N, "us_per_step": smean * 1000.0,
-                         "tokens_per_s": B / (smean * 1e-3), "kernel": f"step_kernel<bf16, {P}, {N}>",
-                         "roofline": {"bound": "hbm", "achieved": sb / (smean * 1e-3) / 1e9,
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": sb / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                      "frac_of_copy": sb / (smean * 1e-3) / 1e9 / copy_gbs,
-                                      "traffic": step_traffic(), "algorithmic_bytes": sb}}
-    if not args.no_backward and (headline or (w.P == 128 and w.N <= 128 and w.dtype == "bf16")):
-        # the backward at the layer shape, and at its head-dim-128 form
-        bp = time_backward(w, max(10, args.steps // 5), 3, device)
-        bmean = sum(bp) / len(bp)
-        bb = bwd_algorithmic(w)
-        out["backward"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_backward",
-                           "us_per_call": bmean * 1000.0, "us_median": bp[len(bp) // 2] * 1000.0,
-                           "tokens_per_s": tokens / (bmean * 1e-3),
-                           "kernels": f"state_scans<{w.N}> (forward and adjoint states) + chunk_grad<{w.N}> + "
-                                      "reduce_head",
-                           "roofline": {"bound": "hbm", "achieved": bb / (bmean * 1e-3) / 1e9,
-                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                        "frac": bb / (bmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                        "traffic": bwd_traffic() if headline else None,
-                                        "algorithmic_bytes": bb}}
-    if not args.no_varlen and headline:
-        vp, nseq = time_varlen(w, max(10, args.steps // 2), 3, device)
-        vmean = sum(vp) / len(vp)
-        vb = scan_algorithmic(w)[0] + w.B * w.L * 4      # + seq_idx
-        out["varlen"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_packed_documents",
-                         "documents_per_call": nseq, "median_document_tokens": VARLEN_MEAN_LEN,
-                         "us_per_call": vmean * 1000.0, "us_median": vp[len(vp) // 2] * 1000.0,
-                         "tokens_per_s": tokens / (vmean * 1e-3),
-                         "kernels": "mark_resets + prep_kernel<128, true> + pipe_kernel<128, true>",
-                         "roofline": {"bound": "hbm", "achieved": vb / (vmean * 1e-3) / 1e9,
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": vb / (vmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                      "algorithmic_bytes": vb}}
-    if not args.no_block and headline:
-        tp, tn = time_block(w, max(10, args.steps // 2), 3, device)
-        pb, nb = block_algorithmic(w)
-
-        def leg(ts, nbytes, kernel):
-            m = sum(ts) / len(ts)
-            return {"kernel": kernel, "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
-                    "roofline": {"bound": "hbm", "achieved": nbytes / (m * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                                 "unit": "GB/s", "frac": nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                 "algorithmic_bytes": nbytes}}
-        out["block"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name).replace("_ssd_chunk_scan", "_block_steps"),
-                        "conv_width": CONV_WIDTH, "norm": "group norm, 1 group, eps 1e-5",
-                        "prologue": leg(tp, pb, f"prologue_kernel<{CONV_WIDTH}>"),
-                        "gated_norm": leg(tn, nb, "gated_norm_kernel")}
-    if not args.no_s6 and headline:
-        ts = time_s6(max(10, args.steps // 2), 3, device)
-        m = sum(ts) / len(ts)
-        sh = S6_SHAPE
-        toks = sh["batch"] * sh["seq_len"]
-        updates = toks * sh["channels"] * sh["state"]
-        peak = VALU_LANE_SLOTS / S6_SLOTS_PER_UPDATE
-        nbytes = 3 * toks * sh["channels"] * 2 + 2 * toks * sh["state"] * 2 + 2 * sh["batch"] * sh["channels"] * sh["state"] * 4
-        out["s6"] = {"workload": "mamba1_2.8b_layer_selective_scan", "config": dict(sh, discretisation="zero-order hold"),
-                     "kernel": "s6_lane_kernel<16, true>", "us_per_call": m * 1000.0, "us_median": ts[len(ts) // 2] * 1000.0,
-                     "tokens_per_s": toks / (m * 1e-3),
-                     "roofline": {"bound": "alu", "achieved": updates / (m * 1e-3) / 1e12, "peak": peak / 1e12,
-                                  "unit": "T state updates/s", "frac": updates / (m * 1e-3) / peak,
-                                  "hbm_gbs": nbytes / (m * 1e-3) / 1e9, "algorithmic_bytes": nbytes}}
-    if not args.no_staged and headline and w.P == 64:
-        # the pages' own four-step form (block states in HBM, a separate state
-        # pass) at the same shape, as an explicit choice: not the headline value
-        _, sp = time_scan(w, max(10, args.steps // 5), 3, device, algo="staged")
-        smean = sum(sp) / len(sp)
-        nc = -(-w.L // w.chunk)
-        # the state pass reads every block's local state and the initial state,
-        # and writes every block's entering state and the final state
-        state_bytes = 2 * w.B * (nc + 1) * w.H * w.P * w.N * 4
-        out["staged"] = {"workload": WORKLOAD_NAMES.get(w.name, w.name) + "_staged_form", "chunk": w.chunk,
-                         "us_per_call": smean * 1000.0, "us_median": sp[len(sp) // 2] * 1000.0,
-                         "tokens_per_s": tokens / (smean * 1e-3),
-                         "kernels": f"gram_kernel<{w.N}> + scan_mfma<{w.N}, {w.chunk}, kState> + state_pass_kernel + "
-                                    f"scan_mfma<{w.N}, {w.chunk}, kOutput>",
-                         "state_pass_bytes": state_bytes,
-                         "roofline": {"bound": "hbm", "achieved": byts / (smean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": byts / (smean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                      "algorithmic_bytes": byts}}
+    out["timed_after"] = ["copy"] + list(extra)
+    out.update(extra)
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
