@@ -95,3 +95,22 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_inputs_are_made_once_and_shared():
+    # the bench makes every input before its first measurement; later calls
+    # find them instead of drawing them again (on the host here, a small shape)
+    import torch
+    w = si.WORKLOADS["tiny_fp32"]
+    dev = torch.device("cpu")
+    a = bench.make_device_sets(w, 2, dev)
+    assert bench.make_device_sets(w, 2, dev) is a
+    bench.add_grad_inputs(w, a, dev)
+    dy = [s["dy"] for s in a]
+    bench.add_grad_inputs(w, a, dev)
+    assert all(s["dy"] is d for s, d in zip(a, dy))
+    n = bench.add_varlen_inputs(w, a, dev)
+    assert n == bench.add_varlen_inputs(w, a, dev) and all(k >= 1 for k in n)
+    assert all(s["yv"] is not s["y"] and s["yv"] is not s["x"] for s in a)
+    st, ins, ys = bench.step_inputs(2, 2, 16, 16, 1, dev)
+    assert bench.step_inputs(2, 2, 16, 16, 1, dev)[0] is st and len(ins) == len(ys) == 4
