@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ssd {
 
 typedef __bf16 bf16;
@@ -83,14 +85,15 @@ struct Workspace {
 // per device (the attribute is held per device).  `done` is the call site's
 // own record of the devices already set.
 constexpr int kMaxDevices = 64;
-inline hipError_t allow_lds(const void *kern, size_t bytes, bool (&done)[kMaxDevices]) {
+inline hipError_t allow_lds(const void *kern, size_t bytes, std::atomic<bool> (&done)[kMaxDevices]) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (done[dev]) return hipSuccess;
+    if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    // threads that race here all set the same attribute
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) done[dev] = true;
+    if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
     return e;
 }
 

@@ -471,7 +471,7 @@ template <int N, int Q, int MODE>
 hipError_t launch_mode(const ScanArgs &a, const Workspace &ws, dim3 grid) {
     const size_t smem = sizeof(Smem<N, Q>);
     auto kern = scan_mfma<N, Q, MODE>;
-    static bool configured[kMaxDevices] = {};
+    static std::atomic<bool> configured[kMaxDevices] = {};
     const hipError_t e = allow_lds((const void *)kern, smem, configured);
     if (e != hipSuccess) return e;
     kern<<<grid, kThreads, smem, a.stream>>>(

@@ -1075,15 +1075,15 @@ __global__ __launch_bounds__(512) void prep_kernel(Args a, int nsegwg) {
 
 // Number of compute units of the current device (cached per device).
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int N, bool kV>
@@ -1126,7 +1126,7 @@ hipError_t launch(const ScanArgs &sa, const Workspace &ws) {
     const int nwg = nmain > 0 ? nmain : nextra * nseg;
     const size_t smem = sizeof(PipeSmem<N>);
     auto kern = pipe_kernel<N, kV>;
-    static bool configured[kMaxDevices] = {};
+    static std::atomic<bool> configured[kMaxDevices] = {};
     e = allow_lds((const void *)kern, smem, configured);
     if (e != hipSuccess) return e;
     Args a{(const __bf16 *)sa.x, sa.dt, sa.A, (const __bf16 *)sa.Bm, (const __bf16 *)sa.Cm, sa.D,
