@@ -51,11 +51,13 @@ __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1p
 // dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 128 tokens of row
 // b from token 128 ty; lane k of channel tile cx takes channels 8(256 cx + k)
 // .. +7 for all 128 tokens, keeping the last W-1 inputs in registers and
-// loading the next 8 rows while the current 8 are computed.  The last channel
+// loading the next 4 rows while the current 4 are computed.  The last channel
 // tile computes dt of the 128 tokens instead.  At the 2.7B layer shape 128
 // tokens per workgroup took 94 us, against 112 us with 32 (whose workgroups
 // re-read 3 of every 32 rows for the convolution's history) and 120 us with
-// 256; loading ahead took it to 92 us.
+// 256; loading ahead took it to 92 us.  The rows are read once, so they are
+// loaded non-temporally (83 against 89 us), and rounds of 4 rows instead of 8
+// hold 120 registers instead of 193 (81 against 83 us).
 struct ProArgs {
     const __bf16 *zx;
     const float *conv_w, *conv_b, *dt_bias;
@@ -108,12 +110,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
         dstride = a.GN;
     }
     // rows are kept as raw bfloat16 words and widened where they are used
-    constexpr int R = 8;   // tokens per round: their loads go out together
+    constexpr int R = 4;   // tokens per round: their loads go out together
     uint4 hist[W > 1 ? W - 1 : 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int64_t t = t0 - (W - 1) + j;
-        hist[j] = t >= 0 ? *reinterpret_cast<const uint4 *>(src + t * a.row) : uint4{0u, 0u, 0u, 0u};
+        hist[j] = t >= 0 ? ld_stream(src + t * a.row) : uint4{0u, 0u, 0u, 0u};
     }
     auto widen = [](const uint4 &u, int e) {
         const uint32_t w = e < 2 ? (e == 0 ? u.x : u.y) : (e == 2 ? u.z : u.w);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         const int t = u < nt ? u : nt - 1;   // clamped: every load in bounds
-        nxt[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
+        nxt[u] = ld_stream(src + (t0 + t) * a.row);
     }
     for (int tt = 0; tt < nt; tt += R) {
         uint4 cur[R];
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const int t = tt + R + u < nt ? tt + R + u : nt - 1;   // clamped: every load in bounds
-                nxt[u] = *reinterpret_cast<const uint4 *>(src + (t0 + t) * a.row);
+                nxt[u] = ld_stream(src + (t0 + t) * a.row);
             }
         }
 #pragma unroll
