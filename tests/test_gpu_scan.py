@@ -307,6 +307,31 @@ def test_few_long_sequences_are_cut_into_segments(case):
         assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
+# The other two launch regimes of the pipe algorithm on a device of C compute
+# units (256 on MI355X): at least 2C (batch, head) sequences, one workgroup
+# each in several rounds; between C/2 and C sequences, one workgroup each
+# with some compute units idle.  (B, H, L, N, regime, init)
+ONE_PER_SEQUENCE = [
+    (2, 300, 200, 64, "default", True),
+    (4, 160, 64 * 2 + 3, 128, "decay_bursts", False),
+    (1, 200, 300, 128, "long_memory", True),
+    (2, 97, 64 * 3 + 1, 256, "default", True),
+]
+
+
+@pytest.mark.parametrize("case", ONE_PER_SEQUENCE, ids=[f"B{c[0]}_H{c[1]}_L{c[2]}_N{c[3]}" for c in ONE_PER_SEQUENCE])
+def test_one_workgroup_per_sequence_regimes(case):
+    B, H, L, N, regime, init = case
+    d = si.make_scan_inputs(B, L, H, 64, N, 1, dtype="bf16", init=init, seed=2300 + H + L, regime=regime)
+    y_ref, f_ref = oracle_scan(d)
+    dd = to_device(d, "bf16")
+    announce(f"one per sequence B{B} H{H} L{L} N{N} {regime} algo=pipe")
+    y, fin = gpu_scan(dd, 256, algo="pipe")
+    ey, ef = rel_err(to_np(y), y_ref), rel_err(to_np(fin), f_ref)
+    print(f"    y err {ey:.3e}  final err {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
 # Head dim 128 in the launch shapes of the per-sequence scan: few sequences
 # cut into segments, more sequences than compute units, one token.
 # (B, L, H, N, regime, init); P = 128
