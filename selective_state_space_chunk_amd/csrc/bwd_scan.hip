@@ -102,6 +102,15 @@ __device__ __forceinline__ float row_sum16(float v) {
     v += dpp<0x140>(v);   // row_mirror
     return v;
 }
+// sum over the four 16-lane rows of a wave (lanes l, l + 16, l + 32, l + 48),
+// the same value in all four, by the row-swapping permutes (no LDS): halves
+// first, then adjacent rows
+__device__ __forceinline__ float rows_sum4(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 // sum over the wave, the same value in every lane (fixed order: deterministic)
 __device__ __forceinline__ float wave_sum(float v) {
     const int r = __float_as_int(row_sum16(v));
@@ -272,7 +281,7 @@ struct GradSmem {
     __bf16 QT[64 * S64];     // Q^T [j][i]
     __bf16 DX[64 * S64];     // dx [j][p] of the head, on its way to global memory as whole rows
     float lam[64], dtl[64], ww[64], ee[64];
-    float zcolw[16][64], zrcolw[16][64];               // column parts per (row wave, lane row)
+    float zcolw[4][64], zrcolw[4][64];                 // column parts per row wave
     float zrow[2][64], qv[2][64], uv[2][64];           // row parts per column half
     float red[16];
     // ddt of up to kDdtHeads consecutive heads [token][head], written to
@@ -446,8 +455,12 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             }
             *reinterpret_cast<uint2 *>(sm.MT + j * S64 + 16 * w + 4 * lgrp) = uint2{pack2(mv[0], mv[1]), pack2(mv[2], mv[3])};
             *reinterpret_cast<uint2 *>(sm.QT + j * S64 + 16 * w + 4 * lgrp) = uint2{pack2(qv[0], qv[1]), pack2(qv[2], qv[3])};
-            sm.zcolw[4 * w + lgrp][j] = zc;
-            sm.zrcolw[4 * w + lgrp][j] = zrc;
+            zc = rows_sum4(zc);
+            zrc = rows_sum4(zrc);
+            if (lgrp == 0) {
+                sm.zcolw[w][j] = zc;
+                sm.zrcolw[w][j] = zrc;
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -550,7 +563,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             const int k = lane;
             float zc = 0.f, zrc = 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
+            for (int m = 0; m < 4; ++m) {
                 zc += sm.zcolw[m][k];
                 zrc += sm.zrcolw[m][k];
             }
