@@ -81,10 +81,6 @@ __device__ __forceinline__ void settle(f32x4 (&H)[NT]) {
     for (int u = 0; u < NT; ++u) asm volatile("" ::"v"(H[u]));
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int m) {
-    const int lane = __lane_id();
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (lane ^ m), __float_as_int(v)));
-}
 __device__ __forceinline__ float lane_get(float v, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(v)));
 }
