@@ -86,13 +86,17 @@ __device__ __forceinline__ void tile_of(int k, int &it, int &jt) {
     jt = k - (it * (it + 1)) / 2;
 }
 
-// Gram kernel: one workgroup per (sub-block, batch * group); see tile::gram_block.
+// Gram kernel: one workgroup per (sub-block, batch * group), one wave per
+// causal tile (ten), so that every tile's loads are in flight at once; see
+// tile::gram_block.  With four waves taking two or three tiles in turn the
+// gram launch of the 130M-layer shape took ~2.4 us more per call.
+constexpr int kGramThreads = 640;
 template <int N>
-__global__ __launch_bounds__(kThreads) void gram_kernel(const __bf16 *__restrict__ Bm,
-                                                        const __bf16 *__restrict__ Cm,
-                                                        __bf16 *__restrict__ gram, int64_t L,
-                                                        int64_t G, int64_t nsb) {
-    tile::gram_block<N>(Bm, Cm, gram, L, G, nsb, blockIdx.x, blockIdx.y, threadIdx.x);
+__global__ __launch_bounds__(kGramThreads) void gram_kernel(const __bf16 *__restrict__ Bm,
+                                                            const __bf16 *__restrict__ Cm,
+                                                            __bf16 *__restrict__ gram, int64_t L,
+                                                            int64_t G, int64_t nsb) {
+    tile::gram_block<N, kGramThreads / 64>(Bm, Cm, gram, L, G, nsb, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -484,7 +488,7 @@ template <int N, int Q>
 hipError_t run(const ScanArgs &a, const Workspace &ws) {
     const int nc = (int)((a.L + Q - 1) / Q);
     const int64_t nsb = (int64_t)nc * (Q / kSub);
-    gram_kernel<N><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+    gram_kernel<N><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kGramThreads, 0, a.stream>>>(
         (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -540,15 +544,15 @@ hipError_t launch_staged_scan(const ScanArgs &a, const Workspace &ws) { return d
 hipError_t launch_gram(const ScanArgs &a, const Workspace &ws, int64_t nsb) {
     switch (a.N) {
         case 64:
-            gram_kernel<64><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+            gram_kernel<64><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kGramThreads, 0, a.stream>>>(
                 (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
             break;
         case 128:
-            gram_kernel<128><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+            gram_kernel<128><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kGramThreads, 0, a.stream>>>(
                 (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
             break;
         case 256:
-            gram_kernel<256><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kThreads, 0, a.stream>>>(
+            gram_kernel<256><<<dim3((unsigned)nsb, (unsigned)(a.B * a.G)), kGramThreads, 0, a.stream>>>(
                 (const __bf16 *)a.Bm, (const __bf16 *)a.Cm, (__bf16 *)ws.gram, a.L, a.G, nsb);
             break;
         default: return hipErrorInvalidValue;
