@@ -223,25 +223,41 @@ __device__ __forceinline__ void gram_block(const __bf16 *__restrict__ Bm, const 
     const int64_t b = bg / G, g = bg % G;
     const int64_t t_base = sbg * kSub;
     __bf16 *out = gram + (bg * nsb + sbg) * (int64_t)(kSub * kSub);
-    for (int k = wave; k < 10; k += NW) {
-        int it, jt;
-        tile_of(k, it, jt);
-        const int64_t tj = t_base + 16 * jt + lrow, ti = t_base + 16 * it + lrow;
-        const __bf16 *brow = Bm + ((b * L + tj) * G + g) * N;
-        const __bf16 *crow = Cm + ((b * L + ti) * G + g) * N;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // a wave's tiles k = wave, wave + NW, ...: every operand loaded first, so
+    // that all of them are in flight at once, then the products
+    constexpr int MT = (10 + NW - 1) / NW;
+    bf16x8 ab[MT][N / 32], bc[MT][N / 32];
 #pragma unroll
-        for (int ks = 0; ks < N / 32; ++ks) {
-            const int n0 = 32 * ks + 8 * lgrp;
-            bf16x8 ab = {}, bc = {};
-            if (tj < L) ab = *reinterpret_cast<const bf16x8 *>(brow + n0);
-            if (ti < L) bc = *reinterpret_cast<const bf16x8 *>(crow + n0);
-            acc = mfma(ab, bc, acc);          // rows j, column i
+    for (int m = 0; m < MT; ++m) {
+        const int k = wave + m * NW;
+        if (k < 10) {
+            int it, jt;
+            tile_of(k, it, jt);
+            const int64_t tj = t_base + 16 * jt + lrow, ti = t_base + 16 * it + lrow;
+            const __bf16 *brow = Bm + ((b * L + tj) * G + g) * N;
+            const __bf16 *crow = Cm + ((b * L + ti) * G + g) * N;
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks) {
+                const int n0 = 32 * ks + 8 * lgrp;
+                ab[m][ks] = bf16x8{};
+                bc[m][ks] = bf16x8{};
+                if (tj < L) ab[m][ks] = *reinterpret_cast<const bf16x8 *>(brow + n0);
+                if (ti < L) bc[m][ks] = *reinterpret_cast<const bf16x8 *>(crow + n0);
+            }
         }
-        uint2 pk;
-        pk.x = pack2(acc[0], acc[1]);
-        pk.y = pack2(acc[2], acc[3]);
-        *reinterpret_cast<uint2 *>(out + (k * 64 + lane) * 4) = pk;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int k = wave + m * NW;
+        if (k < 10) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks) acc = mfma(ab[m][ks], bc[m][ks], acc);   // rows j, column i
+            uint2 pk;
+            pk.x = pack2(acc[0], acc[1]);
+            pk.y = pack2(acc[2], acc[3]);
+            *reinterpret_cast<uint2 *>(out + (k * 64 + lane) * 4) = pk;
+        }
     }
 }
 
