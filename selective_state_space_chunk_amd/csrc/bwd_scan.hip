@@ -58,6 +58,7 @@ struct BwdArgs {
 };
 
 __device__ __forceinline__ float ex2f(float v) { return __builtin_amdgcn_exp2f(v); }
+typedef __bf16 bf16x2_dot __attribute__((ext_vector_type(2)));
 
 // 16 bytes of the stored states and adjoints, written non-temporally by the
 // state scans and read the same way by the sub-block gradients: each is
@@ -404,9 +405,13 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             *reinterpret_cast<uint2 *>(sm.H + p * SN + n + 16) = uint2{hv[k].z, hv[k].w};
             *reinterpret_cast<uint2 *>(sm.dH + p * SN + n) = uint2{dv[k].x, dv[k].y};
             *reinterpret_cast<uint2 *>(sm.dH + p * SN + n + 16) = uint2{dv[k].z, dv[k].w};
-            const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv[k]), d8 = __builtin_bit_cast(bf16x8, dv[k]);
+            // <H, dH'> over the unit: four bfloat16 pair dot products into fp32
+            const uint32_t hw[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+            const uint32_t dw[4] = {dv[k].x, dv[k].y, dv[k].z, dv[k].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hdot += (float)h8[e] * (float)d8[e];
+            for (int e = 0; e < 4; ++e)
+                hdot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_dot, hw[e]),
+                                                       __builtin_bit_cast(bf16x2_dot, dw[e]), hdot, false);
         }
         const float lam = wave_scan(dtv * Ah2);
         const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
