@@ -251,6 +251,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(N == 16 ? 5
     __shared__ __align__(16) float bt[2][N][TS];
     __shared__ __align__(16) float ct[2][N][TS];
     __shared__ __align__(16) float yt[kT][CW];
+    // D of the workgroup's channels, read from LDS where y leaves (in
+    // registers it would spill past the five-wave cap; read from global
+    // memory in every chunk it put a load's latency on each chunk: 514
+    // against 477 us at the Mamba-1 2.8B shape)
+    __shared__ float dsh[CW];
     const int64_t b = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * CW;
     const int tid = threadIdx.x;
@@ -317,6 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(N == 16 ? 5
     load(0);
     stage(0);
     if (nchunks > 1) load(kT);
+    if (tid < CW) dsh[tid] = a.D ? a.D[c0 + tid] : 0.f;
     const bool any_zero = __syncthreads_or(kZoh && Av == 0.f);
     // a state with A = 0 anywhere in the workgroup needs the limit term of the
     // zero-order hold; without one the update is one operation shorter.  The
@@ -365,8 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(N == 16 ? 5
                     bf16x8_t ov;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float dd = a.D ? a.D[c0 + col + e] : 0.f;
-                        ov[e] = (__bf16)__builtin_fmaf(dd, xt[buf][col + e][r], yt[r][col + e]);
+                        ov[e] = (__bf16)__builtin_fmaf(dsh[col + e], xt[buf][col + e][r], yt[r][col + e]);
                     }
                     *reinterpret_cast<bf16x8_t *>(a.y + (b * L + (int64_t)k * kT + r) * a.Dch + c0 + col) = ov;
                 }
