@@ -245,7 +245,9 @@ __device__ __forceinline__ void state_scan_body(const BwdArgs &a, int64_t bh) {
 template <int N>
 __global__ __launch_bounds__(256) void state_scans(BwdArgs a) {
     const int64_t bhn = a.B * a.H;
-    const int64_t blk = blockIdx.x;
+    // logical index, contiguous within each XCD, so that the chains of one
+    // batch row, which read the same Bm (or Cm) and dt rows, share an L2
+    const int64_t blk = xcd_chain(blockIdx.x, gridDim.x);
     if (blk < bhn)
         state_scan_body<N, false>(a, blk);
     else
@@ -277,10 +279,15 @@ struct GradSmem {
     __bf16 MT[64 * S64];     // M^T [j][i]
     __bf16 QT[64 * S64];     // Q^T [j][i]
     __bf16 DX[64 * S64];     // dx [j][p] of the head, on its way to global memory as whole rows
-    float lam[64], dtl[64], ww[64], ee[64];
-    float zcolw[4][64], zrcolw[4][64];                 // column parts per row wave
-    float zrow[2][64], qv[2][64], uv[2][64];           // row parts per column half
-    float red[16];
+    // What the dLambda / ddt tail of a head needs, kept for a batch of
+    // kBatch consecutive heads so that the eight waves run the batch's tails
+    // side by side once it is complete, instead of one wave running each
+    // head's tail while the others wait
+    static constexpr int kBatch = 8;
+    float lam[kBatch][64], dtl[kBatch][64], ww[kBatch][64], ee[64];
+    float zcolw[kBatch][4][64], zrcolw[kBatch][4][64];    // column parts per row wave
+    float zrow[kBatch][2][64], qv[kBatch][2][64], uv[kBatch][2][64];   // row parts per column half
+    float red[kBatch][16];
     // ddt of up to kDdtHeads consecutive heads [token][head], written to
     // global memory together as runs of consecutive heads per token row
     static constexpr int kDdtHeads = 16;
@@ -381,13 +388,11 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < NH; ++e) dCacc[e] = dBacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // wave 0 carries the first half's ddt and dA, dD parts of a head of 128
-    // channels to the second half (the halves are consecutive in the walk)
-    float ddt_half = 0.f, da_half = 0.f, dd_half = 0.f;
+    constexpr int KB = GradSmem<N>::kBatch;
     const int64_t dh0 = g * hpg / a.hs;   // the group's first caller head
     for (int64_t hh = 0; hh < hpg; ++hh) {
         const int64_t h = g * hpg + hh, dh = h / a.hs;
-        const bool first_half = a.hs == 2 && (h & 1) == 0;
+        const int sl = (int)(hh % KB);   // the head's place in its batch
         const float Ah = a.A[dh], Ah2 = Ah * kLog2eB, Dh = a.D[dh];
         // ---- stage this head; decays
         *reinterpret_cast<uint4 *>(sm.X + xr * S64 + 8 * xc) = xv;
@@ -416,13 +421,13 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         const float lam = wave_scan(dtv * Ah2);
         const float lend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
         if (w8 == 0) {
-            sm.lam[lane] = lam;
-            sm.dtl[lane] = dtv;
-            sm.ww[lane] = ex2f(lend - lam) * dtv;
+            sm.lam[sl][lane] = lam;
+            sm.dtl[sl][lane] = dtv;
+            sm.ww[sl][lane] = ex2f(lend - lam) * dtv;
             sm.ee[lane] = ex2f(lam);
         }
         hdot = wave_sum(hdot);
-        if (lane == 0) sm.red[w8] = hdot;
+        if (lane == 0) sm.red[sl][w8] = hdot;
         // the next head's inputs (the last head loads itself again)
         load_head(hh + 1 < hpg ? h + 1 : h);
         __syncthreads();
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         // M^T, Q^T; sums for d/dLambda and ddt
         float lam_i[4], zr[4] = {0.f, 0.f, 0.f, 0.f}, dd = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lam_i[r] = sm.lam[16 * w + 4 * lgrp + r];
+        for (int r = 0; r < 4; ++r) lam_i[r] = sm.lam[sl][16 * w + 4 * lgrp + r];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int jt = 2 * hf + e;
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             for (int kk = 0; kk < 2; ++kk)
                 sd = mfma(frag_row(sm.Y, 16 * w, S64, 32 * kk, lrow, lgrp), frag_row(sm.X, 16 * jt, S64, 32 * kk, lrow, lgrp), sd);
             const int j = 16 * jt + lrow;
-            const float lam_j = sm.lam[j], dtj = sm.dtl[j];
+            const float lam_j = sm.lam[sl][j], dtj = sm.dtl[sl][j];
             float mv[4], qv[4], zc = 0.f, zrc = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -459,17 +464,17 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
             zc = rows_sum4(zc);
             zrc = rows_sum4(zrc);
             if (lgrp == 0) {
-                sm.zcolw[w][j] = zc;
-                sm.zrcolw[w][j] = zrc;
+                sm.zcolw[sl][w][j] = zc;
+                sm.zrcolw[sl][w][j] = zrc;
             }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float v = red16(zr[r]);
-            if (lrow == 0) sm.zrow[hf][16 * w + 4 * lgrp + r] = v;
+            if (lrow == 0) sm.zrow[sl][hf][16 * w + 4 * lgrp + r] = v;
         }
         dd = wave_sum(dd);
-        if (lane == 0) sm.red[8 + w8] = dd;
+        if (lane == 0) sm.red[sl][8 + w8] = dd;
         __syncthreads();
 
         // ---- dx = M^T dy + w (Bm dH'^T), rows j, column tiles pt of this
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         {
             float qs[4] = {0.f, 0.f, 0.f, 0.f}, wj[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wj[r] = sm.ww[16 * w + 4 * lgrp + r];
+            for (int r = 0; r < 4; ++r) wj[r] = sm.ww[sl][16 * w + 4 * lgrp + r];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int pt = 2 * hf + e;
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = red16(qs[r]);
-                if (lrow == 0) sm.qv[hf][16 * w + 4 * lgrp + r] = v;
+                if (lrow == 0) sm.qv[sl][hf][16 * w + 4 * lgrp + r] = v;
             }
         }
         // (the phases are kept apart: interleaved, their operands would not fit
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float v = red16(us[r]);
-                if (lrow == 0) sm.uv[hf][16 * w + 4 * lgrp + r] = v;
+                if (lrow == 0) sm.uv[sl][hf][16 * w + 4 * lgrp + r] = v;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         {
             float wj[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wj[r] = sm.ww[16 * w + 4 * lgrp + r];
+            for (int r = 0; r < 4; ++r) wj[r] = sm.ww[sl][16 * w + 4 * lgrp + r];
 #pragma unroll
             for (int e = 0; e < NH; ++e) {
                 const int nt = NH * hf + e;
@@ -559,49 +564,58 @@ __global__ __launch_bounds__(512) void chunk_grad(BwdArgs a) {
         if (xr < q)
             *reinterpret_cast<uint4 *>(a.dx + ((row0 + xr) * a.H + h) * kP + 8 * xc) =
                 *reinterpret_cast<const uint4 *>(sm.DX + xr * S64 + 8 * xc);
-        // ---- d/dLambda per token, ddt, and this head's parts of dA, dD (wave 0)
-        if (w8 == 0) {
-            const int k = lane;
-            float zc = 0.f, zrc = 0.f;
+        // ---- once a batch is complete: d/dLambda per token, ddt, and the
+        // parts of dA, dD of its heads, one caller head per wave (the two
+        // halves of a head of 128 channels are consecutive, in one batch, and
+        // their ddt, dA and dD parts are summed: the gradient of an input
+        // shared by both halves)
+        if (sl == KB - 1 || hh + 1 == hpg) {
+            const int64_t hb = hh - sl;   // the batch's first head (in the group)
+            const int nb = sl + 1;
+            if (w8 * (int)a.hs < nb) {
+                const int k = lane;
+                float gsum = 0.f, dasum = 0.f, ddsum = 0.f;
+                for (int u = 0; u < (int)a.hs; ++u) {
+                    const int s = w8 * (int)a.hs + u;
+                    const float Au = a.A[(g * hpg + hb + s) / a.hs];
+                    const float lendu = sm.lam[s][63];
+                    float zc = 0.f, zrc = 0.f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                zc += sm.zcolw[m][k];
-                zrc += sm.zrcolw[m][k];
-            }
-            const float wk = sm.ww[k], qk = sm.qv[0][k] + sm.qv[1][k];
-            float dl = (sm.uv[0][k] + sm.uv[1][k]) + (sm.zrow[0][k] + sm.zrow[1][k]) - zc - wk * qk;
-            const float wq = wave_sum(wk * qk);
-            float hd = 0.f, ddp = 0.f;
+                    for (int m = 0; m < 4; ++m) {
+                        zc += sm.zcolw[s][m][k];
+                        zrc += sm.zrcolw[s][m][k];
+                    }
+                    const float wk = sm.ww[s][k], qk = sm.qv[s][0][k] + sm.qv[s][1][k];
+                    float dl = (sm.uv[s][0][k] + sm.uv[s][1][k]) + (sm.zrow[s][0][k] + sm.zrow[s][1][k]) - zc - wk * qk;
+                    const float wq = wave_sum(wk * qk);
+                    float hd = 0.f, ddp = 0.f;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                hd += sm.red[m];
-                ddp += sm.red[8 + m];
-            }
-            if (k == 63) dl += ex2f(lend) * hd + wq;
-            // rs_k = sum over i >= k of dl_i = total - (prefix through k) + dl_k
-            const float pre = wave_scan(dl);
-            const float rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), 63)) - pre + dl;
-            const float g_dt = Ah * rs + zrc + ex2f(lend - sm.lam[k]) * qk;
-            const float da = wave_sum(sm.dtl[k] * rs);
-            if (first_half) {
-                ddt_half = g_dt;
-                da_half = da;
-                dd_half = ddp;
-            } else {
-                sm.ddt[k][(dh - dh0) % GradSmem<N>::kDdtHeads] = ddt_half + g_dt;
+                    for (int m = 0; m < 8; ++m) {
+                        hd += sm.red[s][m];
+                        ddp += sm.red[s][8 + m];
+                    }
+                    if (k == 63) dl += ex2f(lendu) * hd + wq;
+                    // rs_k = sum over i >= k of dl_i = total - (prefix through k) + dl_k
+                    const float pre = wave_scan(dl);
+                    const float rs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre), 63)) - pre + dl;
+                    gsum += Au * rs + zrc + ex2f(lendu - sm.lam[s][k]) * qk;
+                    dasum += wave_sum(sm.dtl[s][k] * rs);
+                    ddsum += ddp;
+                }
+                const int64_t dhu = (g * hpg + hb) / a.hs + w8;   // this wave's caller head
+                sm.ddt[k][(dhu - dh0) % GradSmem<N>::kDdtHeads] = gsum;
                 if (k == 0) {
-                    a.dAp[(b * a.Hd + dh) * nsb + c] = da_half + da;
-                    a.dDp[(b * a.Hd + dh) * nsb + c] = dd_half + ddp;
+                    a.dAp[(b * a.Hd + dhu) * nsb + c] = dasum;
+                    a.dDp[(b * a.Hd + dhu) * nsb + c] = ddsum;
                 }
             }
-        }
-        __syncthreads();
-        // ---- ddt of the last kDdtHeads heads (or of the group's last ones)
-        {
+            __syncthreads();
+            // ---- ddt of the last kDdtHeads caller heads (or of the group's last ones)
             constexpr int KD = GradSmem<N>::kDdtHeads;
+            static_assert(KD % KB == 0, "a ddt flush ends with a batch");
             const int64_t done = dh - dh0 + 1;   // caller heads of the group finished
             const bool last = hh + 1 == hpg;
-            if ((!first_half && done % KD == 0) || last) {
+            if (done % KD == 0 || last) {
                 const int nh = (int)(done % KD == 0 ? KD : done % KD);
                 const int64_t base = dh0 + done - nh;
                 for (int e = tid; e < 64 * KD; e += 512) {
