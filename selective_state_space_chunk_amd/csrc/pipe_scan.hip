@@ -204,15 +204,20 @@ __global__ __launch_bounds__(kThreads, 1) void pipe_kernel(Args a) {
     // seg0..seg0+xlen-1)
     const int nsub = (int)((a.L + kSub - 1) / kSub);
     const int nown = a.nmain > 0 ? nsub : 0;
-    const int64_t chain = a.nmain > 0 ? xcd_chain(blockIdx.x, a.nmain) : (int64_t)blockIdx.x % a.nextra;
+    // logical workgroup index, contiguous within each XCD: the heads of a
+    // batch row (own sequences) and the heads of one segment (extra
+    // sequences), which share Bm, Cm, dt and the gram tiles, then sit behind
+    // one L2 instead of all eight
+    const int64_t lid = xcd_chain(blockIdx.x, gridDim.x);
+    const int64_t chain = a.nmain > 0 ? lid : lid % a.nextra;
     const int64_t b = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
     const int64_t h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
     const int64_t g = __builtin_amdgcn_readfirstlane((int)(h / (a.H / a.G)));
     const int64_t dh = h / a.hs;   // the caller's head: dt, A and D
     const float Ah2v = a.A[dh] * kLog2e, Dhv = a.D[dh];
-    const bool has_x = (int)blockIdx.x < a.nextra * a.nseg;
-    const int xe = has_x ? (int)blockIdx.x % a.nextra : 0;
-    const int xq = has_x ? (int)blockIdx.x / a.nextra : 0;
+    const bool has_x = lid < (int64_t)a.nextra * a.nseg;
+    const int xe = has_x ? (int)(lid % a.nextra) : 0;
+    const int xq = has_x ? (int)(lid / a.nextra) : 0;
     const int64_t xchain = has_x ? a.nmain + xe : chain;
     const int64_t bx = __builtin_amdgcn_readfirstlane((int)(xchain / a.H));
     const int64_t hx = __builtin_amdgcn_readfirstlane((int)(xchain % a.H));
@@ -1062,10 +1067,13 @@ __device__ __forceinline__ void seg_state_block_wide(const Args &a, int blk) {
 template <int N, bool kV>
 __global__ __launch_bounds__(512) void prep_kernel(Args a, int nsegwg) {
     if ((int)blockIdx.x < nsegwg) {
+        // the segment states of one segment index, which share Bm and dt
+        // rows, on as few XCDs as possible (a bijection of 0 .. nsegwg-1)
+        const int blk = (int)xcd_chain(blockIdx.x, nsegwg);
         if constexpr (N == 256)
-            seg_state_block_wide<N, kV>(a, blockIdx.x);
+            seg_state_block_wide<N, kV>(a, blk);
         else
-            seg_state_block<N, kV>(a, blockIdx.x);
+            seg_state_block<N, kV>(a, blk);
     } else {
         const int64_t k = (int64_t)blockIdx.x - nsegwg;
         gram_block<N, 8>(a.Bm, a.Cm, const_cast<__bf16 *>(a.gram), a.L, a.G, a.nsb, k % a.nsb, k / a.nsb,
