@@ -486,11 +486,19 @@ def cpu_model():
     return None
 
 
-def scan_traffic():
+def traffic_file(workload="m2_2p7b"):
+    """The counter summary of a scan workload (the headline's holds the
+    backward, decode and block-step figures too)."""
+    if workload == "m2_2p7b":
+        return TRAFFIC_FILE
+    return os.path.join(os.path.dirname(TRAFFIC_FILE), f"traffic_{workload}.json")
+
+
+def scan_traffic(workload="m2_2p7b"):
     """HBM bytes per scan launch from the committed counter summary, or None
     when there is none or the kernel sources changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -573,12 +581,12 @@ def summarize_mfma(folder, cus, xcds):
     print(json.dumps(out, indent=1))
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb):
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb, workload="m2_2p7b"):
     copy_bytes = int(copy_mb * 1e6) // 4 * 4
     cf, _ = _pmc_kib(copy_fetch_dir, "FETCH_SIZE", "copy")
     cw, _ = _pmc_kib(copy_write_dir, "WRITE_SIZE", "copy")
     f_fetch, f_write = copy_bytes / cf, copy_bytes / cw      # bytes per counted KiB
-    out = {"workload": "m2_2p7b", "sources_sha256": scan_sources_digest(),
+    out = {"workload": workload, "sources_sha256": scan_sources_digest(),
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_fetch, "write_scale_bytes_per_kib": f_write, "kernels": {}}
     total = 0.0
@@ -638,8 +646,9 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mb)
             continue
         out["block_kernels"][name] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
                                       "read_bytes": fk * f_fetch, "write_bytes": wk * f_write}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    path = traffic_file(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -668,7 +677,7 @@ def main():
                          "long_n256 and m2_2p7b_p128 are the other scan shapes)")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.copy_mb)
+        summarize_pmc(*args.summarize_pmc, args.copy_mb, args.workload)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.cus, args.xcds)
@@ -828,7 +837,7 @@ def main():
                       "p90": per[(9 * len(per)) // 10]},
         "roofline": {"bound": "hbm", "kernels": kernels + " (one ssd_chunk_scan_fwd call)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic() if headline else None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": scan_traffic(args.workload),
                      "algorithmic_bytes": byts, "algorithmic_flops": flops, "flops_block_tokens": block,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
