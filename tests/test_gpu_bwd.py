@@ -55,6 +55,9 @@ CASES = [
     ("twenty_four_heads_one_group", 2, 140, 24, 128, 1, True, False, "default"),
     ("five_heads_one_group", 2, 200, 5, 128, 1, True, True, "default"),
     ("three_heads_per_group", 1, 180, 6, 64, 2, True, True, "long_memory"),
+    # the dLambda / ddt tails run once per batch of eight heads: a full batch
+    # followed by a partial one
+    ("thirteen_heads_one_group", 1, 150, 13, 128, 1, True, True, "default"),
 ]
 
 
@@ -80,6 +83,8 @@ CASES_P128 = [
     ("p128_ragged", 2, 3 * 64 + 17, 3, 128, 1, True, True, "default"),
     ("p128_groups_n64", 2, 150, 4, 64, 2, False, True, "long_memory"),
     ("p128_forty_heads_one_group", 1, 260, 40, 128, 1, True, False, "default"),
+    # ten heads of 64: a batch of four heads of 128, then a batch of one
+    ("p128_five_heads_one_group", 1, 150, 5, 128, 1, True, True, "default"),
 ]
 
 
