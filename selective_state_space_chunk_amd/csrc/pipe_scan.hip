@@ -72,7 +72,8 @@ struct Args {
     int hs;                  // heads of 64 channels per caller head (P / 64)
     int nmain;               // sequences run whole, one per workgroup (0: every sequence is cut)
     int nextra;              // further sequences, each cut into nseg segments of seglen sub-blocks;
-    int nseg, seglen;        //   segment q of extra sequence e runs on workgroup q*nextra + e
+    int nseg, seglen;        //   segment q of extra sequence e runs on the workgroup whose logical
+                             //   index (xcd_chain of its block index) is q*nextra + e
 };
 
 // Segment-state buffers in Args::seg.
