@@ -48,7 +48,7 @@ __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1p
 // dt (H)], bfloat16.  The C = HP + 2GN middle channels go through a causal
 // depthwise convolution of width W (taps conv_w[c][k], tap W-1 on the
 // current token, zero before token 0) plus bias and SiLU, into x, Bm, Cm;
-// dt = softplus(dt_raw + dt_bias).  Workgroup (cx, ty, b): 128 tokens of row
+// dt = softplus(dt_raw + dt_bias).  Workgroup (ty, cx, b): 128 tokens of row
 // b from token 128 ty; lane k of channel tile cx takes channels 8(256 cx + k)
 // .. +7 for all 128 tokens, keeping the last W-1 inputs in registers and
 // loading the next 4 rows while the current 4 are computed.  The last channel
@@ -72,10 +72,10 @@ constexpr int kTok = 128;
 template <int W>
 __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
     const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * kTok;
+    const int64_t t0 = (int64_t)blockIdx.x * kTok;
     const int nt = (int)(a.L - t0 < kTok ? a.L - t0 : kTok);
     const __bf16 *rows = a.zx + (b * a.L) * a.row;
-    if ((int)blockIdx.x == a.ctiles) {
+    if ((int)blockIdx.y == a.ctiles) {
         const int H = (int)a.H;
         const int64_t off = 2 * a.HP + 2 * a.GN;
         for (int i = threadIdx.x; i < nt * H; i += 256) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(ProArgs a) {
         return;
     }
     const int64_t C = a.HP + 2 * a.GN;
-    const int64_t c = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    const int64_t c = 8 * ((int64_t)blockIdx.y * 256 + threadIdx.x);
     if (c >= C) return;
     float wk[W][8], bias[8];
 #pragma unroll
@@ -296,7 +296,11 @@ hipError_t launch_block_prologue(const void *zx, const float *conv_w, const floa
     const int ctiles = (int)((C / 8 + 255) / 256);
     ProArgs a{(const __bf16 *)zx, conv_w, conv_b, dt_bias, (__bf16 *)x, (__bf16 *)Bm, (__bf16 *)Cm, dt,
               L, HP, GN, H, 2 * HP + 2 * GN + H, ctiles};
-    const dim3 grid((unsigned)(ctiles + 1), (unsigned)((L + kTok - 1) / kTok), (unsigned)B);
+    // token tiles run fastest: the hardware deals workgroup i to XCD i mod 8,
+    // and with the channel tiles fastest each XCD got one kind of tile only
+    // (at the 2.7B shape, 4 kinds: half the XCDs carried the full channel
+    // tiles, the others the partial one or the light dt tiles)
+    const dim3 grid((unsigned)((L + kTok - 1) / kTok), (unsigned)(ctiles + 1), (unsigned)B);
     switch (W) {
         case 1: prologue_kernel<1><<<grid, 256, 0, stream>>>(a); break;
         case 2: prologue_kernel<2><<<grid, 256, 0, stream>>>(a); break;
